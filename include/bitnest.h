@@ -1,0 +1,138 @@
+/*
+ * bitnest.h - C ABI of the bit-nested W4/W8 quantized linear on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (BitNest-Llama-3-8B model card, section "Files", entry
+ * planes.safetensors; recipe table rows "Weights" and "Activations"):
+ *
+ *   One 8-bit weight is kept as two planes of unsigned nibbles, `hi` and `lo`,
+ *   each uint8 [N, K/2], nibble u = q + 8. Byte j of a row holds column 2j in
+ *   its low nibble and column 2j+1 in its high nibble. `scale` is fp16
+ *   [N, K/128], one scale per row and per 128 input columns.
+ *     draft  weight W4 = (hi - 8) * scale                        (reads hi only)
+ *     target weight W8 = (16 * (hi - 8) + (lo - 8)) * scale / 16 (reads hi and lo)
+ *   Activations are symmetric int8, one scale per token, or one per token and
+ *   128-column group (the o_proj recipe).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *     allocates nothing, frees nothing, keeps no pointer after returning, holds
+ *     no per-call state and never synchronises. Work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL is the default stream); results are
+ *     ready when that stream reaches the point of the call.
+ *   - Tensors are row-major and contiguous. Every tensor pointer must be
+ *     16-byte aligned.
+ *   - Sizes: 0 <= M <= BITNEST_MAX_M, 0 <= N, 128 <= K <= BITNEST_MAX_K, K a
+ *     multiple of 128. M == 0 or N == 0 is a valid call that does nothing.
+ *   - Arguments are checked on the host before anything is launched:
+ *       BITNEST_EINVAL       a required pointer is NULL, a size is negative,
+ *                            K is not a positive multiple of 128, or
+ *                            act_group is neither 0 nor 128;
+ *       BITNEST_EALIGN       a tensor pointer is not 16-byte aligned;
+ *       BITNEST_EUNSUPPORTED M > BITNEST_MAX_M or K > BITNEST_MAX_K;
+ *       BITNEST_EHIP         the HIP runtime reported an error while
+ *                            launching (an error left pending on the calling
+ *                            thread by an earlier HIP call is reported too).
+ *     A fault inside a kernel surfaces at the caller's next synchronisation
+ *     of the stream, as for any HIP kernel.
+ *   - Outputs must not overlap inputs.
+ *   - Calls are reentrant; calls on different streams may run concurrently.
+ *   - Nothing throws across this boundary.
+ */
+#ifndef BITNEST_H
+#define BITNEST_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITNEST_ABI_VERSION 1
+#define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
+#define BITNEST_MAX_M 32       /* most tokens per call */
+#define BITNEST_MAX_K 16384    /* largest input width */
+
+typedef enum bitnest_status {
+    BITNEST_OK = 0,
+    BITNEST_EINVAL = 1,
+    BITNEST_EALIGN = 2,
+    BITNEST_EUNSUPPORTED = 3,
+    BITNEST_EHIP = 4
+} bitnest_status;
+
+/* Version of this interface; equals BITNEST_ABI_VERSION of the built library. */
+int bitnest_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *bitnest_status_string(int status);
+
+/*
+ * Activation quantisation (model card, recipe table, row "Activations":
+ * symmetric int8, per token; o_proj per 128-column group).
+ *
+ * The pages do not fix the scale formula or the rounding. This library uses,
+ * for each token m and each column set R (the whole row when act_group == 0,
+ * each run of 128 columns when act_group == 128):
+ *     amax = max_{k in R} |x[m,k]|
+ *     s    = amax / 127                  IEEE fp32 division, round to nearest even
+ *     q    = 0                           if s == 0
+ *            clamp(rne(x / s), -127, 127) otherwise, x / s an IEEE fp32 division
+ *   (rne = round half to even; -128 is never produced.)
+ *
+ *   x   fp32 [M, K], finite values (NaN/Inf are outside the contract).
+ *   xq  int8 [M, K] codes, written.
+ *   xs  fp32 [M] (act_group 0) or [M, K/128] (act_group 128), written.
+ */
+bitnest_status bitnest_quant_act(const float *x, int M, int K, int act_group,
+                                 int8_t *xq, float *xs, void *stream);
+
+/*
+ * Draft linear, W4A8 (model card: the draft reads only the high nibble plane).
+ *   y[m, n] = sum_g float(P_hi[m,n,g]) * scale[n,g] * s_a
+ *   P_hi[m,n,g] = sum_{k in group g} xq[m,k] * (hi_nibble[n,k] - 8)   (exact int32)
+ *   s_a = xs[m] (act_group 0) or xs[m, g] (act_group 128).
+ * This equals sum_k (xq[m,k] * s_a) * W4[n,k] up to fp32 rounding.
+ *
+ *   xq     int8 [M, K] codes;  xs  fp32 [M] or [M, K/128]
+ *   hi     uint8 [N, K/2]      scale  fp16 bit patterns [N, K/128]
+ *   y      fp32 [M, N], every element overwritten.
+ * Only `hi` and `scale` are read from the weights.
+ */
+bitnest_status bitnest_linear_draft(const int8_t *xq, const float *xs, int act_group,
+                                    const uint8_t *hi, const uint16_t *scale,
+                                    float *y, int M, int N, int K, void *stream);
+
+/*
+ * Target linear, W8A8 (model card: the target reads all 8 bits).
+ *   P8[m,n,g] = 16 * P_hi[m,n,g] + P_lo[m,n,g]         (exact int32; the 8-bit
+ *               code 16*(hi-8) + (lo-8) spans [-136, 119] and is never formed
+ *               as an int8)
+ *   y[m, n]   = sum_g float(P8[m,n,g]) * (scale[n,g] / 16) * s_a
+ * Arguments as for the draft, plus `lo` uint8 [N, K/2]. M <= 7 runs the
+ * plane-streaming GEMV, M >= 8 the batched-verify int8 matrix-core kernel; the
+ * results obey the same definition.
+ */
+bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_group,
+                                     const uint8_t *hi, const uint8_t *lo,
+                                     const uint16_t *scale,
+                                     float *y, int M, int N, int K, void *stream);
+
+/*
+ * The integer partials of the two calls above, from the same kernels' integer
+ * loop (for checking; not a fast path).
+ *   p_hi  int32 [M, N, K/128] <- P_hi (always written)
+ *   p_lo  int32 [M, N, K/128] <- P_lo              (only if lo != NULL)
+ *   p8    int32 [M, N, K/128] <- 16 * P_hi + P_lo  (only if lo != NULL)
+ * lo == NULL selects the draft kernels (p_lo and p8 are then ignored and may
+ * be NULL); otherwise p_lo and p8 are required.
+ */
+bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo,
+                                       int32_t *p_hi, int32_t *p_lo, int32_t *p8,
+                                       int M, int N, int K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNEST_H */

@@ -1,0 +1,238 @@
+/*
+ * CPU oracle for the bit-nested W4/W8 quantized linear.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only tests/, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or helper with the HIP library it checks.
+ *
+ * What it computes, and where each step is defined:
+ *
+ *  - Weight planes: model card "BitNest-Llama-3-8B", section "Files", entry
+ *    planes.safetensors. Each decoder Linear stores two uint8 [N, K/2] planes
+ *    `.hi` and `.lo` of unsigned nibbles (u = q + 8). Byte j of a row carries
+ *    column 2j in its low nibble and column 2j+1 in its high nibble. One fp16
+ *    scale per row and per 128 input columns: `.scale` is fp16 [N, K/128].
+ *  - Dequantisation (same entry): the draft weight is (hi - 8) * scale, the
+ *    target weight is (16 * (hi - 8) + (lo - 8)) * scale / 16.
+ *  - Group size 128: same model card, recipe table, row "Weights".
+ *  - Activations: same recipe table, row "Activations": symmetric int8 per
+ *    token, and per 128-column group for o_proj. The pages fix neither the
+ *    scale formula nor the rounding; the reading used here is
+ *        amax = max |x| over the token (or its 128-column group),
+ *        s    = amax / 127            (IEEE fp32 division),
+ *        q    = 0 if s == 0, else clamp(round_half_even(x / s), -127, 127)
+ *    with x / s an IEEE fp32 division. Both sides take this integer decision
+ *    in fp32.
+ *  - The linear itself is the plain definition "dequantise, then multiply":
+ *        y[m, n] = sum_k (q[m, k] * s_a) * W[n, k]
+ *    in fp64, k ascending, with s_a the token's (or the token-group's) scale
+ *    and W the draft or target weight above.
+ *  - The per-group integer partials are the plain definition
+ *        P[m, n, g] = sum_{k in group g} q[m, k] * (u[n, k] - 8)
+ *    accumulated in int64, with the target's combined partial
+ *        P8 = 16 * P_hi + P_lo
+ *    (the integer part of the target formula before the scale / 16).
+ *
+ * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 and fp64
+ * operation is the IEEE operation written.
+ */
+#include <stddef.h>
+#include <stdint.h>
+#include <math.h>
+#include <fenv.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_GROUP 128
+
+enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ERANGE = 2 };
+
+/* IEEE 754 binary16 -> binary64, from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 * 2^-10 */
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* Nibble of column k in a plane row (model card, "Files", planes.safetensors):
+ * byte k/2, low nibble for even k, high nibble for odd k. */
+static int nibble_at(const uint8_t *plane_row, int k)
+{
+    uint8_t b = plane_row[k / 2];
+    return (k % 2 == 0) ? (b & 0x0F) : (b >> 4);
+}
+
+/* Unpack a whole plane [N, K/2] into unsigned nibbles u [N, K]. */
+int oracle_unpack_plane(const uint8_t *plane, int N, int K, uint8_t *u)
+{
+    if (!plane || !u || N < 0 || K < 0 || K % 2) return ORACLE_EINVAL;
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *row = plane + (size_t)n * (K / 2);
+        for (int k = 0; k < K; ++k) u[(size_t)n * K + k] = (uint8_t)nibble_at(row, k);
+    }
+    return ORACLE_OK;
+}
+
+/* Activation quantisation, one token (act_group 0) or one token-group
+ * (act_group 128) at a time, following the reading stated at the top. */
+int oracle_quant_act(const float *x, int M, int K, int act_group, int8_t *q, float *s)
+{
+    if (!x || !q || !s || M < 0 || K <= 0) return ORACLE_EINVAL;
+    if (act_group != 0 && act_group != ORACLE_GROUP) return ORACLE_EINVAL;
+    if (act_group == ORACLE_GROUP && K % ORACLE_GROUP) return ORACLE_EINVAL;
+    if (fegetround() != FE_TONEAREST) return ORACLE_EINVAL;
+    const int R = act_group ? act_group : K;        /* columns sharing one scale */
+    const int S = K / R;                            /* scales per token */
+    for (int m = 0; m < M; ++m) {
+        for (int r = 0; r < S; ++r) {
+            const float *xr = x + (size_t)m * K + (size_t)r * R;
+            int8_t *qr = q + (size_t)m * K + (size_t)r * R;
+            float amax = 0.0f;
+            for (int k = 0; k < R; ++k) {
+                float a = fabsf(xr[k]);
+                if (a > amax) amax = a;
+            }
+            float sc = amax / 127.0f;
+            s[(size_t)m * S + r] = sc;
+            for (int k = 0; k < R; ++k) {
+                int code = 0;
+                if (sc != 0.0f) {
+                    float t = xr[k] / sc;               /* fp32 division */
+                    float rt = nearbyintf(t);           /* ties to even */
+                    if (rt > 127.0f) rt = 127.0f;
+                    if (rt < -127.0f) rt = -127.0f;
+                    code = (int)rt;
+                }
+                qr[k] = (int8_t)code;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Per-group integer partials of one plane: P[m, n, g] = sum_{k in g} q[m,k] * (u[n,k] - 8). */
+static int partials_one_plane(const int8_t *q, const uint8_t *plane, int M, int N, int K,
+                              int32_t *P, int nthreads)
+{
+    const int G = K / ORACLE_GROUP;
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(|:bad)
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *row = plane + (size_t)n * (K / 2);
+        for (int m = 0; m < M; ++m) {
+            for (int g = 0; g < G; ++g) {
+                int64_t acc = 0;
+                for (int k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k)
+                    acc += (int64_t)q[(size_t)m * K + k] * (int64_t)(nibble_at(row, k) - 8);
+                if (acc > INT32_MAX || acc < INT32_MIN) bad = 1;
+                P[((size_t)m * N + n) * G + g] = (int32_t)acc;
+            }
+        }
+    }
+    return bad ? ORACLE_ERANGE : ORACLE_OK;
+}
+
+/* Integer partials, layout int32 [M, N, K/128]. lo, p_lo and p8 may be NULL
+ * (draft); if lo is given, p_lo and p8 receive P_lo and 16 * P_hi + P_lo. */
+int oracle_partials(const int8_t *q, const uint8_t *hi, const uint8_t *lo,
+                    int M, int N, int K, int32_t *p_hi, int32_t *p_lo, int32_t *p8,
+                    int nthreads)
+{
+    if (!q || !hi || !p_hi || M < 0 || N < 0 || K <= 0 || K % ORACLE_GROUP) return ORACLE_EINVAL;
+    if (lo && (!p_lo || !p8)) return ORACLE_EINVAL;
+    if (nthreads <= 0) nthreads = 1;
+    int rc = partials_one_plane(q, hi, M, N, K, p_hi, nthreads);
+    if (rc || !lo) return rc;
+    rc = partials_one_plane(q, lo, M, N, K, p_lo, nthreads);
+    if (rc) return rc;
+    const size_t total = (size_t)M * N * (K / ORACLE_GROUP);
+    for (size_t i = 0; i < total; ++i) {
+        int64_t v = 16 * (int64_t)p_hi[i] + (int64_t)p_lo[i];
+        if (v > INT32_MAX || v < INT32_MIN) return ORACLE_ERANGE;
+        p8[i] = (int32_t)v;
+    }
+    return ORACLE_OK;
+}
+
+/* Dequantised weight of one element (model card, "Files", planes.safetensors):
+ * mode 0 (draft):  (hi - 8) * scale
+ * mode 1 (target): (16 * (hi - 8) + (lo - 8)) * scale / 16 */
+static double weight_at(int mode, const uint8_t *hi_row, const uint8_t *lo_row,
+                        const uint16_t *scale_row, int k)
+{
+    double sc = oracle_half_to_double(scale_row[k / ORACLE_GROUP]);
+    int h = nibble_at(hi_row, k) - 8;
+    if (mode == 0) return (double)h * sc;
+    int l = nibble_at(lo_row, k) - 8;
+    return (double)(16 * h + l) * sc / 16.0;
+}
+
+/* Dense dequantised weight matrix W [N, K] in fp64 (small shapes, tests). */
+int oracle_dequant(int mode, const uint8_t *hi, const uint8_t *lo, const uint16_t *scale,
+                   int N, int K, double *W)
+{
+    if (!hi || !scale || !W || N < 0 || K <= 0 || K % ORACLE_GROUP) return ORACLE_EINVAL;
+    if (mode != 0 && mode != 1) return ORACLE_EINVAL;
+    if (mode == 1 && !lo) return ORACLE_EINVAL;
+    const int G = K / ORACLE_GROUP;
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            W[(size_t)n * K + k] = weight_at(mode, hi + (size_t)n * (K / 2),
+                                             lo ? lo + (size_t)n * (K / 2) : NULL,
+                                             scale + (size_t)n * G, k);
+    return ORACLE_OK;
+}
+
+/* The linear, dequantise-then-multiply in fp64:
+ * y64[m, n] = sum_{k ascending} (q[m,k] * s_a[m(,g)]) * W[n,k].
+ * s_a is xs[m] (act_group 0) or xs[m * K/128 + k/128] (act_group 128). */
+int oracle_linear(int mode, const int8_t *q, const float *xs, int act_group,
+                  const uint8_t *hi, const uint8_t *lo, const uint16_t *scale,
+                  int M, int N, int K, double *y64, int nthreads)
+{
+    if (!q || !xs || !hi || !scale || !y64) return ORACLE_EINVAL;
+    if (M < 0 || N < 0 || K <= 0 || K % ORACLE_GROUP) return ORACLE_EINVAL;
+    if (mode != 0 && mode != 1) return ORACLE_EINVAL;
+    if (mode == 1 && !lo) return ORACLE_EINVAL;
+    if (act_group != 0 && act_group != ORACLE_GROUP) return ORACLE_EINVAL;
+    if (nthreads <= 0) nthreads = 1;
+    const int G = K / ORACLE_GROUP;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *hr = hi + (size_t)n * (K / 2);
+        const uint8_t *lr = lo ? lo + (size_t)n * (K / 2) : NULL;
+        const uint16_t *sr = scale + (size_t)n * G;
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double sa = act_group ? (double)xs[(size_t)m * G + k / ORACLE_GROUP]
+                                      : (double)xs[m];
+                double xhat = (double)q[(size_t)m * K + k] * sa;
+                acc += xhat * weight_at(mode, hr, lr, sr, k);
+            }
+            y64[(size_t)m * N + n] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

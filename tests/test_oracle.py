@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Sources (BitNest-Llama-3-8B model card): section "Files", entry
+planes.safetensors (plane layout, nibble order, fp16 [N, K/128] scales, draft
+and target dequantisation formulas); recipe table rows "Weights" (group size
+128) and "Activations" (symmetric int8 per token, o_proj per 128-group).
+
+Each pin is chosen so that a plausible slip in the oracle fails it: swapped
+nibble order, wrong byte index, wrong offset (8 vs 7 or 128), a dropped 16 or
+/16, a wrong group index, a transposed operand, round-half-away instead of
+round-half-even, a missing clamp or a wrong activation scale.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GROUP = 128
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- fp16
+
+def test_half_decoder_matches_ieee_binary16_everywhere():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(ref[fin], got[fin])
+    assert np.array_equal(ref[np.isinf(ref)], got[np.isinf(ref)])
+    assert np.all(np.isnan(got[np.isnan(ref)]))
+
+
+# --------------------------------------------------------------------------- packing
+
+def test_nibble_order_golden(golden_dir):
+    fx = _load(golden_dir, "packing.json")
+    rows = fx["rows"]
+    plane = np.array([[int(r[0], 16) for r in rows]], dtype=np.uint8)
+    u = oracle.unpack_plane(plane, 2 * len(rows))
+    for j, r in enumerate(rows):
+        assert u[0, 2 * j] == r[1], r
+        assert u[0, 2 * j + 1] == r[2], r
+        assert int(u[0, 2 * j]) - 8 == r[3]
+        assert int(u[0, 2 * j + 1]) - 8 == r[4]
+
+
+def test_unpack_every_byte_value_and_position():
+    # 256 rows, each row's byte j is (row + 37 j) mod 256: every byte value at
+    # many positions. Expected nibbles come from the hex spelling of the byte
+    # (second hex digit = low nibble = even column), a route independent of
+    # the oracle's shifts and masks.
+    N, K = 256, 256
+    plane = ((np.arange(N)[:, None] + 37 * np.arange(K // 2)[None, :]) % 256).astype(np.uint8)
+    u = oracle.unpack_plane(plane, K)
+    for n in range(0, N, 17):
+        for j in range(K // 2):
+            h = "%02x" % plane[n, j]
+            assert u[n, 2 * j] == int(h[1], 16)
+            assert u[n, 2 * j + 1] == int(h[0], 16)
+
+
+# --------------------------------------------------------------------------- dequantisation
+
+def _single_column_planes(pairs, K=GROUP):
+    """Row i holds (hi, lo) nibble pair i in column 0; every other nibble is 8 (code 0)."""
+    N = len(pairs)
+    hi = np.full((N, K // 2), 0x88, np.uint8)
+    lo = np.full((N, K // 2), 0x88, np.uint8)
+    for i, (h, l) in enumerate(pairs):
+        hi[i, 0] = 0x80 | h       # column 0 = low nibble of byte 0
+        lo[i, 0] = 0x80 | l
+    return hi, lo
+
+
+def test_dequant_golden(golden_dir):
+    fx = _load(golden_dir, "dequant.json")
+    pairs = [(r[0], r[1]) for r in fx["rows"]]
+    hi, lo = _single_column_planes(pairs)
+    for sc in fx["scales"]:
+        bits = int(sc["fp16_bits"], 16)
+        scale = np.full((len(pairs), 1), bits, np.uint16)
+        w4 = oracle.dequant(hi, scale)
+        w8 = oracle.dequant(hi, scale, lo)
+        for i, r in enumerate(fx["rows"]):
+            assert w4[i, 0] == r[2] * sc["value"], (r, sc)
+            assert w8[i, 0] == r[3] * sc["value"] / 16.0, (r, sc)
+            assert np.all(w4[i, 1:] == 0) and np.all(w8[i, 1:] == 0)
+
+
+def test_w8_codes_are_a_bijection_onto_minus136_119():
+    # 16 * (hi - 8) + (lo - 8) over all 256 (hi, lo) pairs is every integer of
+    # [-136, 119] exactly once; a zero point of 128 or a dropped factor fails.
+    pairs = [(h, l) for h in range(16) for l in range(16)]
+    hi, lo = _single_column_planes(pairs)
+    scale = np.full((256, 1), 0x4C00, np.uint16)        # 16.0: W8 = code exactly
+    w8 = oracle.dequant(hi, scale, lo)[:, 0]
+    assert sorted(w8.astype(int).tolist()) == list(range(-136, 120))
+    w4 = oracle.dequant(hi, np.full((256, 1), 0x3C00, np.uint16))[:, 0]
+    vals, counts = np.unique(w4, return_counts=True)
+    assert vals.tolist() == list(range(-8, 8)) and set(counts.tolist()) == {16}
+    # Nesting: the target code's top part is the draft code, refined by lo.
+    assert np.array_equal(np.floor((w8 + 136) / 16) - 8, w4)
+
+
+def test_scale_groups_follow_columns_of_128():
+    N, K = 2, 3 * GROUP
+    hi = np.full((N, K // 2), 0x99, np.uint8)            # every code = +1
+    scale = np.array([[0x3C00, 0x4000, 0x3400],         # 1, 2, 0.25
+                      [0x3800, 0x3C00, 0x4400]], np.uint16)  # 0.5, 1, 4
+    W = oracle.dequant(hi, scale)
+    expect = np.repeat(np.array([[1.0, 2.0, 0.25], [0.5, 1.0, 4.0]]), GROUP, axis=1)
+    assert np.array_equal(W, expect)
+
+
+# --------------------------------------------------------------------------- activation quant
+
+def test_act_quant_golden_ties_to_even(golden_dir):
+    fx = _load(golden_dir, "act_quant.json")
+    for case in fx["per_token"]:
+        x = np.array([case["x"]], np.float32)   # act_group 0 takes any K
+        q, s = oracle.quant_act(x)
+        assert s[0] == np.float32(case["s"])
+        assert q[0].tolist() == case["q"], case
+
+
+def test_act_quant_grouped_golden(golden_dir):
+    g = _load(golden_dir, "act_quant.json")["grouped"]
+    K = g["K"]
+    x = np.zeros((1, K), np.float32)
+    x[0, 0] = g["group0"]["amax_value"]
+    x[0, GROUP] = g["group1"]["amax_value"]
+    for grp in ("group0", "group1"):
+        for col, val, _ in g[grp]["probe"]:
+            x[0, col] = val
+    q, s = oracle.quant_act(x, act_group=GROUP)
+    assert s.shape == (1, 2)
+    assert s[0, 0] == g["group0"]["s"] and s[0, 1] == g["group1"]["s"]
+    assert q[0, 0] == 127 and q[0, GROUP] == 127
+    for grp in ("group0", "group1"):
+        for col, _, code in g[grp]["probe"]:
+            assert q[0, col] == code
+
+
+def _rand_x(rng, M, K, outliers=True):
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if outliers:
+        idx = rng.choice(K, size=max(1, K // 200), replace=False)
+        x[:, idx] *= 20
+    return x
+
+
+@pytest.mark.parametrize("act_group", [0, GROUP])
+def test_act_quant_equals_library_rounding(act_group):
+    # numpy's fp32 division and np.rint (IEEE round half to even) give the
+    # textbook form of the rule; the oracle must agree code for code.
+    rng = np.random.default_rng(1)
+    M, K = 5, 1024
+    x = _rand_x(rng, M, K)
+    x[2] = 0.0
+    q, s = oracle.quant_act(x, act_group)
+    R = K if act_group == 0 else GROUP
+    xr = x.reshape(M, K // R, R)
+    amax = np.abs(xr).max(axis=2)
+    s_ref = (amax / np.float32(127)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = (xr / s_ref[:, :, None]).astype(np.float32)
+    q_ref = np.where(s_ref[:, :, None] == 0, 0, np.clip(np.rint(t), -127, 127)).astype(np.int8)
+    assert np.array_equal(q, q_ref.reshape(M, K))
+    assert np.array_equal(s.reshape(M, -1), s_ref)
+
+
+def test_act_quant_near_ties_divide_not_reciprocal():
+    # Elements within a few ulps of (k + 1/2) * s, kept only where the IEEE
+    # quotient x / s and the product x * fl(1/s) round to different codes.
+    # numpy's fp32 division and np.rint (the library form of the rule) decide
+    # the expected code; an oracle that multiplies by a reciprocal fails here.
+    rows, expect = [], []
+    for amax in (139.7, 3.3, 5.7, 0.91, 77.77, 1234.5, 17.0, 101.3):
+        a = np.float32(amax)
+        s = a / np.float32(127)
+        r = np.float32(1) / s
+        row, codes = [a], [127]
+        for k in range(0, 126):
+            x = np.float32((k + 0.5) * np.float64(s))
+            for _ in range(4):
+                x = np.nextafter(x, np.float32(-np.inf))
+            for _ in range(9):
+                if np.rint(x / s) != np.rint(x * r):
+                    row.append(x)
+                    codes.append(int(np.rint(x / s)))
+                x = np.nextafter(x, np.float32(np.inf))
+        rows.append(np.array(row, np.float32))
+        expect.append(codes)
+    assert sum(len(c) - 1 for c in expect) >= 10
+    for row, codes in zip(rows, expect):
+        q, s = oracle.quant_act(row[None, :])
+        assert s[0] == row[0] / np.float32(127)
+        assert q[0].tolist() == codes
+
+
+@pytest.mark.parametrize("act_group", [0, GROUP])
+def test_act_quant_properties(act_group):
+    rng = np.random.default_rng(2)
+    M, K = 4, 2048
+    x = _rand_x(rng, M, K)
+    q, s = oracle.quant_act(x, act_group)
+    R = K if act_group == 0 else GROUP
+    s2 = s.reshape(M, -1)
+    qr = q.reshape(M, K // R, R).astype(np.float64)
+    xr = x.reshape(M, K // R, R).astype(np.float64)
+    assert q.min() >= -127 and q.max() <= 127
+    # the largest-magnitude element of each set maps to +-127
+    i = np.abs(xr).argmax(axis=2)
+    top = np.take_along_axis(qr, i[:, :, None], axis=2)[:, :, 0]
+    assert np.all(np.abs(top) == 127)
+    # reconstruction error within half a step (plus fp32 division rounding)
+    err = np.abs(qr * s2[:, :, None] - xr)
+    assert np.all(err <= s2[:, :, None] * (0.5 + 1e-5))
+    # symmetric: negating x negates the codes and keeps the scales
+    qn, sn = oracle.quant_act(-x, act_group)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # power-of-two scaling of x leaves the codes unchanged and scales s exactly
+    q4, s4 = oracle.quant_act(x * np.float32(4.0), act_group)
+    assert np.array_equal(q4, q) and np.array_equal(s4, s * np.float32(4.0))
+
+
+# --------------------------------------------------------------------------- partials and linear
+
+def _onehot_problem(golden_dir):
+    fx = _load(golden_dir, "onehot_linear.json")
+    N, K = fx["N"], fx["K"]
+    fill = int(fx["fill_byte"], 16)
+    hi = np.full((N, K // 2), fill, np.uint8)
+    lo = np.full((N, K // 2), fill, np.uint8)
+    for e in fx["hi_bytes"]:
+        hi[e["row"], e["byte"]] = int(e["value"], 16)
+    for e in fx["lo_bytes"]:
+        lo[e["row"], e["byte"]] = int(e["value"], 16)
+    scale = np.array([[int(b, 16) for b in r] for r in fx["scale_bits"]], np.uint16)
+    x = np.zeros((1, K), np.float32)
+    x[0, fx["x_nonzero"]["column"]] = fx["x_nonzero"]["value"]
+    return fx, x, hi, lo, scale
+
+
+def test_onehot_linear_golden(golden_dir):
+    fx, x, hi, lo, scale = _onehot_problem(golden_dir)
+    q, s = oracle.quant_act(x)
+    assert s[0] == fx["act_scale"]
+    assert q[0, fx["x_nonzero"]["column"]] == fx["act_code"]
+    assert np.count_nonzero(q) == 1
+    p_hi, p_lo, p8 = oracle.partials(q, hi, lo)
+    assert p_hi.tolist() == fx["p_hi"]
+    assert p_lo.tolist() == fx["p_lo"]
+    assert p8.tolist() == fx["p8"]
+    assert oracle.partials(q, hi).tolist() == fx["p_hi"]
+    assert oracle.linear(q, s, hi, scale).tolist() == fx["y_draft"]
+    assert oracle.linear(q, s, hi, scale, lo).tolist() == fx["y_target"]
+
+
+def _random_problem(seed, M, N, K, lo_const=None):
+    rng = np.random.default_rng(seed)
+    hi = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    lo = rng.integers(0, 256, (N, K // 2), dtype=np.uint8) if lo_const is None else \
+        np.full((N, K // 2), lo_const, np.uint8)
+    scale = np.exp(np.log(0.01) + 0.3 * rng.standard_normal((N, K // GROUP))) \
+        .astype(np.float16).view(np.uint16)
+    x = _rand_x(rng, M, K)
+    return x, hi, lo, scale
+
+
+def test_brute_force_exact_rationals_tiny():
+    # An independent route: nibbles from the hex spelling of each byte, fp16
+    # from numpy, and exact rational arithmetic for the whole sum. The oracle's
+    # fp64 result must be the exact value to within a few fp64 roundings.
+    M, N, K = 2, 3, 2 * GROUP
+    x, hi, lo, scale = _random_problem(11, M, N, K)
+    for act_group in (0, GROUP):
+        q, s = oracle.quant_act(x, act_group)
+        for target in (False, True):
+            y = oracle.linear(q, s, hi, scale, lo if target else None, act_group)
+            for m in range(M):
+                for n in range(N):
+                    tot = Fraction(0)
+                    absum = Fraction(0)
+                    for k in range(K):
+                        hx = "%02x" % hi[n, k // 2]
+                        lx = "%02x" % lo[n, k // 2]
+                        pos = 1 if k % 2 == 0 else 0
+                        ch = int(hx[pos], 16) - 8
+                        cl = int(lx[pos], 16) - 8
+                        sw = Fraction(float(scale[n, k // GROUP:k // GROUP + 1].view(np.float16)[0]))
+                        w = sw * (Fraction(16 * ch + cl, 16) if target else ch)
+                        sa = Fraction(float(s[m] if act_group == 0 else s[m, k // GROUP]))
+                        term = int(q[m, k]) * sa * w
+                        tot += term
+                        absum += abs(term)
+                    # K fp64 additions and two products per term: |err| <= (K + 3) u sum|terms|
+                    bound = (K + 3) * 2.0 ** -53 * float(absum)
+                    assert abs(float(tot) - y[m, n]) <= bound, (m, n, target, act_group)
+
+
+@pytest.mark.parametrize("act_group", [0, GROUP])
+def test_target_equals_draft_when_lo_is_8(act_group):
+    # lo == 8 everywhere means every lo code is 0: W8 = 16 (hi - 8) scale / 16
+    # = W4 exactly, so the two linears must agree bit for bit.
+    M, N, K = 3, 40, 4 * GROUP
+    x, hi, lo, scale = _random_problem(3, M, N, K, lo_const=0x88)
+    q, s = oracle.quant_act(x, act_group)
+    assert np.array_equal(oracle.linear(q, s, hi, scale, lo, act_group),
+                          oracle.linear(q, s, hi, scale, None, act_group))
+    p_hi, p_lo, p8 = oracle.partials(q, hi, lo)
+    assert not p_lo.any()
+    assert np.array_equal(p8, 16 * p_hi)
+
+
+def test_combined_partial_identity_and_bounds():
+    M, N, K = 4, 33, 5 * GROUP
+    x, hi, lo, scale = _random_problem(4, M, N, K)
+    q, _ = oracle.quant_act(x)
+    p_hi, p_lo, p8 = oracle.partials(q, hi, lo)
+    assert np.array_equal(p8.astype(np.int64), 16 * p_hi.astype(np.int64) + p_lo)
+    assert np.abs(p_hi).max() <= 127 * 8 * GROUP
+    assert np.abs(p8).max() <= 127 * 136 * GROUP
+    # extreme inputs reach the bounds exactly
+    qx = np.full((1, GROUP), -127, np.int8)
+    h0 = np.zeros((1, GROUP // 2), np.uint8)              # every code -8
+    ph, pl, pe = oracle.partials(qx, h0, h0)
+    assert ph[0, 0, 0] == 127 * 8 * GROUP and pe[0, 0, 0] == 127 * 136 * GROUP
+
+
+@pytest.mark.parametrize("act_group", [0, GROUP])
+def test_verify_batch_rows_equal_single_token_calls(act_group):
+    # Per-token quantisation makes rows independent: an M = 4 call is four
+    # M = 1 calls stacked, bit for bit.
+    M, N, K = 4, 24, 3 * GROUP
+    x, hi, lo, scale = _random_problem(5, M, N, K)
+    q, s = oracle.quant_act(x, act_group)
+    y4 = oracle.linear(q, s, hi, scale, lo, act_group)
+    p4 = oracle.partials(q, hi, lo)
+    for m in range(M):
+        q1, s1 = oracle.quant_act(x[m:m + 1], act_group)
+        assert np.array_equal(q1, q[m:m + 1])
+        assert np.array_equal(oracle.linear(q1, s1, hi, scale, lo, act_group), y4[m:m + 1])
+        p1 = oracle.partials(q1, hi, lo)
+        for a, b in zip(p1, p4):
+            assert np.array_equal(a[0], b[m])
+
+
+@pytest.mark.parametrize("act_group", [0, GROUP])
+def test_factorised_form_equals_dequantise_then_multiply(act_group):
+    # sum_g P[m,n,g] * scale[n,g] * f * s_a equals the plain definition.
+    M, N, K = 3, 20, 4 * GROUP
+    x, hi, lo, scale = _random_problem(6, M, N, K)
+    q, s = oracle.quant_act(x, act_group)
+    p_hi, p_lo, p8 = oracle.partials(q, hi, lo)
+    sw = scale.view(np.float16).astype(np.float64)
+    sa = s.astype(np.float64)[:, None, None] if act_group == 0 else s.astype(np.float64)[:, None, :]
+    yd = (p_hi * sw[None] * sa).sum(axis=2)
+    yt = (p8 * (sw[None] / 16.0) * sa).sum(axis=2)
+    np.testing.assert_allclose(oracle.linear(q, s, hi, scale, None, act_group), yd, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.linear(q, s, hi, scale, lo, act_group), yt, rtol=1e-12, atol=1e-12)
+    # and the dense dequantised matrices under a library matmul
+    xhat = q.astype(np.float64) * (np.repeat(s.astype(np.float64), GROUP, axis=1) if act_group else
+                                   s.astype(np.float64)[:, None])
+    np.testing.assert_allclose(xhat @ oracle.dequant(hi, scale).T, yd, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(xhat @ oracle.dequant(hi, scale, lo).T, yt, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_is_transposed_correctly_on_non_square_shapes():
+    # A one-hot token at column k must return column k of W [N, K] (length N).
+    M, N, K = 1, 7, 3 * GROUP
+    _, hi, lo, scale = _random_problem(8, M, N, K)
+    W = oracle.dequant(hi, scale, lo)
+    for k in (0, 1, 200, K - 1):
+        q = np.zeros((1, K), np.int8)
+        q[0, k] = 1
+        y = oracle.linear(q, np.ones(1, np.float32), hi, scale, lo)
+        assert y.shape == (1, N)
+        assert np.array_equal(y[0], W[:, k])
+
+
+def test_oracle_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.unpack_plane(np.zeros((2, 3), np.uint8), 4)
+    with pytest.raises(oracle.OracleError):
+        oracle.quant_act(np.zeros((1, 100), np.float32), act_group=GROUP)

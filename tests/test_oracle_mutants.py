@@ -1,0 +1,94 @@
+"""The oracle's pins must catch plausible slips.
+
+Each case below compiles a copy of the C oracle with one planted mistake (on
+the CPU, in a temporary directory) and checks that at least one pin of
+test_oracle.py fails against it. A mutant that every pin accepts would mean a
+part of the oracle is not actually pinned.
+"""
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "bitnest_oracle.c")
+
+MUTANTS = {
+    "nibble order swapped": ("(k % 2 == 0) ? (b & 0x0F) : (b >> 4)", "(k % 2 == 0) ? (b >> 4) : (b & 0x0F)"),
+    "byte index k instead of k/2": ("uint8_t b = plane_row[k / 2];", "uint8_t b = plane_row[k / 2 + (k & 1) * 0];\n    b = plane_row[(k / 2) ^ 1];"),
+    "draft offset 7": ("int h = nibble_at(hi_row, k) - 8;", "int h = nibble_at(hi_row, k) - 7;"),
+    "target /16 dropped": ("return (double)(16 * h + l) * sc / 16.0;", "return (double)(16 * h + l) * sc;"),
+    "target factor 16 dropped": ("return (double)(16 * h + l) * sc / 16.0;", "return (double)(h + l) * sc / 16.0;"),
+    "zero point 128": ("return (double)(16 * h + l) * sc / 16.0;", "return (double)(16 * h + l + 8) * sc / 16.0;"),
+    "scale group index": ("double sc = oracle_half_to_double(scale_row[k / ORACLE_GROUP]);",
+                          "double sc = oracle_half_to_double(scale_row[(k / ORACLE_GROUP) / 2]);"),
+    "scale row stride": ("const uint16_t *sr = scale + (size_t)n * G;", "const uint16_t *sr = scale + (size_t)n;"),
+    "round half away from zero": ("float rt = nearbyintf(t);", "float rt = roundf(t);"),
+    "act scale /128": ("float sc = amax / 127.0f;", "float sc = amax / 128.0f;"),
+    "act scale by reciprocal": ("float t = xr[k] / sc;", "float t = xr[k] * (1.0f / sc);"),
+    "partials offset dropped": ("acc += (int64_t)q[(size_t)m * K + k] * (int64_t)(nibble_at(row, k) - 8);",
+                                "acc += (int64_t)q[(size_t)m * K + k] * (int64_t)(nibble_at(row, k));"),
+    "p8 factor 8": ("int64_t v = 16 * (int64_t)p_hi[i] + (int64_t)p_lo[i];",
+                    "int64_t v = 8 * (int64_t)p_hi[i] + (int64_t)p_lo[i];"),
+    "group act scale index": ("double sa = act_group ? (double)xs[(size_t)m * G + k / ORACLE_GROUP]",
+                              "double sa = act_group ? (double)xs[(size_t)m * G]"),
+    "half exponent bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    "plane row stride": ("const uint8_t *hr = hi + (size_t)n * (K / 2);", "const uint8_t *hr = hi + (size_t)n * (K / 4);"),
+}
+
+
+def _all_pins():
+    out = []
+    for name, fn in sorted(vars(pins).items()):
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        params = getattr(fn, "pytestmark", [])
+        grid = [{}]
+        for mark in params:
+            if mark.name == "parametrize":
+                argname, values = mark.args[0], mark.args[1]
+                grid = [dict(g, **{argname: v}) for g in grid for v in values]
+        out.append((name, fn, grid))
+    return out
+
+
+def _fails(golden_dir):
+    failed = []
+    for name, fn, grid in _all_pins():
+        for kw in grid:
+            args = dict(kw)
+            if "golden_dir" in inspect.signature(fn).parameters:
+                args["golden_dir"] = golden_dir
+            try:
+                fn(**args)
+            except Exception:
+                failed.append(name)
+                break
+    return failed
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(mutant, tmp_path, monkeypatch, golden_dir):
+    old, new = MUTANTS[mutant]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation site not found: %s" % mutant
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-std=c99", "-D_GNU_SOURCE",
+                    "-fPIC", "-shared", str(msrc), "-o", str(lib), "-lm"], check=True)
+    monkeypatch.setattr(oracle, "_lib", None)
+    monkeypatch.setattr(oracle, "_LIB", str(lib))
+    monkeypatch.setattr(oracle, "_SRC", str(msrc))
+    try:
+        failed = _fails(golden_dir)
+    finally:
+        monkeypatch.setattr(oracle, "_lib", None)
+    assert failed, "no pin caught the mutant '%s'" % mutant
+
+
+def test_unmutated_oracle_passes_every_pin(golden_dir):
+    assert _fails(golden_dir) == []
