@@ -23,7 +23,8 @@
  *   - Tensors are row-major and contiguous. Every tensor pointer must be
  *     16-byte aligned.
  *   - Sizes: 0 <= M <= BITNEST_MAX_M, 0 <= N, 128 <= K <= BITNEST_MAX_K, K a
- *     multiple of 128. M == 0 or N == 0 is a valid call that does nothing.
+ *     multiple of 128. M == 0 or N == 0 is a valid call that does nothing;
+ *     its tensor pointers are not checked and may be NULL.
  *   - Arguments are checked on the host before anything is launched:
  *       BITNEST_EINVAL       a required pointer is NULL, a size is negative,
  *                            K is not a positive multiple of 128, or

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point that include/bitnest.h declares, and rejects bad arguments on the
+host, before anything reaches the HIP runtime."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import w8_quantized_linear_amd as bn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnest.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnest_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
+              "bitnest_linear_partials", "bitnest_status_string", "bitnest_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bn.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", bn.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(L, name)
+    # C linkage: no mangled bitnest_ symbols leak out
+    assert not [s for s in exported if s.startswith("_Z") and "bitnest_" in s and "bitnest7" not in s]
+
+
+def test_version_and_status_strings():
+    assert bn.bitnest_abi_version() == 1
+    seen = set()
+    for s in range(5):
+        txt = bn.bitnest_status_string(s)
+        assert txt and txt not in seen
+        seen.add(txt)
+    assert bn.bitnest_status_string(99) == "unknown status"
+    assert bn.bitnest_status_string(0) == "ok"
+
+
+# Fake, 16-byte-aligned, non-null addresses: validation must reject every call
+# below before dereferencing anything or calling HIP.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+D = ctypes.c_void_p(0x40000)
+E = ctypes.c_void_p(0x50000)
+F = ctypes.c_void_p(0x60000)
+MIS = ctypes.c_void_p(0x10004)
+NUL = None
+
+
+def _q(x, M, K, g, xq, xs):
+    return bn.lib().bitnest_quant_act(x, M, K, g, xq, xs, None)
+
+
+def _d(xq, xs, g, hi, sc, y, M, N, K):
+    return bn.lib().bitnest_linear_draft(xq, xs, g, hi, sc, y, M, N, K, None)
+
+
+def _t(xq, xs, g, hi, lo, sc, y, M, N, K):
+    return bn.lib().bitnest_linear_target(xq, xs, g, hi, lo, sc, y, M, N, K, None)
+
+
+def _p(xq, hi, lo, ph, pl, p8, M, N, K):
+    return bn.lib().bitnest_linear_partials(xq, hi, lo, ph, pl, p8, M, N, K, None)
+
+
+@pytest.mark.parametrize("call,status", [
+    # quant_act
+    (lambda: _q(NUL, 1, 128, 0, B, C), bn.EINVAL),
+    (lambda: _q(A, 1, 128, 0, NUL, C), bn.EINVAL),
+    (lambda: _q(A, 1, 128, 0, B, NUL), bn.EINVAL),
+    (lambda: _q(A, 1, 128, 64, B, C), bn.EINVAL),
+    (lambda: _q(A, -1, 128, 0, B, C), bn.EINVAL),
+    (lambda: _q(A, 1, 0, 0, B, C), bn.EINVAL),
+    (lambda: _q(A, 1, 100, 0, B, C), bn.EINVAL),
+    (lambda: _q(A, 1, 16384 + 128, 0, B, C), bn.EUNSUPPORTED),
+    (lambda: _q(MIS, 1, 128, 0, B, C), bn.EALIGN),
+    (lambda: _q(A, 1, 128, 0, MIS, C), bn.EALIGN),
+    (lambda: _q(A, 1, 128, 128, B, MIS), bn.EALIGN),
+    (lambda: _q(A, 0, 128, 0, B, C), bn.OK),                # empty: nothing launched
+    # draft
+    (lambda: _d(NUL, B, 0, C, D, E, 1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, NUL, 0, C, D, E, 1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 0, NUL, D, E, 1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, NUL, E, 1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, D, NUL, 1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 7, C, D, E, 1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, D, E, -1, 8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, D, E, 1, -8, 128), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, D, E, 1, 8, 0), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, D, E, 1, 8, 192), bn.EINVAL),
+    (lambda: _d(A, B, 0, C, D, E, 33, 8, 128), bn.EUNSUPPORTED),
+    (lambda: _d(A, B, 0, C, D, E, 1, 8, 16512), bn.EUNSUPPORTED),
+    (lambda: _d(MIS, B, 0, C, D, E, 1, 8, 128), bn.EALIGN),
+    (lambda: _d(A, B, 0, MIS, D, E, 1, 8, 128), bn.EALIGN),
+    (lambda: _d(A, B, 0, C, MIS, E, 1, 8, 128), bn.EALIGN),
+    (lambda: _d(A, B, 0, C, D, MIS, 1, 8, 128), bn.EALIGN),
+    (lambda: _d(A, B, 0, C, D, E, 0, 8, 128), bn.OK),
+    (lambda: _d(A, B, 0, C, D, E, 4, 0, 128), bn.OK),
+    # target
+    (lambda: _t(A, B, 0, C, NUL, D, E, 1, 8, 128), bn.EINVAL),
+    (lambda: _t(A, B, 0, C, MIS, D, E, 1, 8, 128), bn.EALIGN),
+    (lambda: _t(A, B, 128, C, F, D, E, 1, 8, 100), bn.EINVAL),
+    (lambda: _t(A, B, 0, C, F, D, E, 40, 8, 128), bn.EUNSUPPORTED),
+    (lambda: _t(A, B, 0, C, F, D, E, 0, 8, 128), bn.OK),
+    # partials
+    (lambda: _p(NUL, B, C, D, E, F, 1, 8, 128), bn.EINVAL),
+    (lambda: _p(A, NUL, C, D, E, F, 1, 8, 128), bn.EINVAL),
+    (lambda: _p(A, B, C, NUL, E, F, 1, 8, 128), bn.EINVAL),
+    (lambda: _p(A, B, C, D, NUL, F, 1, 8, 128), bn.EINVAL),
+    (lambda: _p(A, B, C, D, E, NUL, 1, 8, 128), bn.EINVAL),
+    (lambda: _p(A, B, NUL, D, NUL, NUL, 1, 8, 130), bn.EINVAL),
+    (lambda: _p(A, B, C, D, E, MIS, 1, 8, 128), bn.EALIGN),
+    (lambda: _p(A, B, NUL, D, NUL, NUL, 0, 8, 128), bn.OK),
+    # empty calls accept NULL pointers (torch's empty tensors have none)
+    (lambda: _q(NUL, 0, 128, 0, NUL, NUL), bn.OK),
+    (lambda: _d(NUL, NUL, 0, NUL, NUL, NUL, 0, 8, 128), bn.OK),
+    (lambda: _t(NUL, NUL, 0, NUL, NUL, NUL, NUL, 3, 0, 128), bn.OK),
+    (lambda: _p(NUL, NUL, NUL, NUL, NUL, NUL, 0, 0, 128), bn.OK),
+    (lambda: _d(NUL, NUL, 0, NUL, NUL, NUL, 0, 8, 100), bn.EINVAL),
+])
+def test_host_validation(call, status):
+    assert call() == status
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 128), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        bn.bitnest_quant_act(x)

@@ -1,0 +1,292 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: int8 activation codes, fp32 activation scales and int32 per-group
+partials bit-exact; fp32 outputs within max|y - y_oracle| <= 1e-5 * max|y_oracle|
+(y_oracle is the oracle's fp64 dequantise-then-multiply result). Invariants of
+the format are checked on the GPU bit for bit: lo == 8 makes the target equal
+the draft, an M-token call equals single-token calls row by row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w8_quantized_linear_amd as bn
+from w8_quantized_linear_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+GROUP = 128
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bn.lib()
+
+
+def _dev(t):
+    return t.to("cuda")
+
+
+def _problem(M, N, K, seed=0, outliers=True, lo=True):
+    w = synth.make_weights(N, K, seed=seed, layer=M, linear=N % 97, with_lo=lo)
+    x = synth.make_activations(M, K, seed=seed, layer=M, linear=N % 97, outliers=outliers)
+    return w, x
+
+
+def _check_y(y_gpu, y64, what=""):
+    y = y_gpu.double().cpu().numpy()
+    ref = np.abs(y64).max()
+    err = np.abs(y - y64).max() if y.size else 0.0
+    assert err <= TOL * ref + 1e-30, "%s: max err %.3e vs bound %.3e" % (what, err, TOL * ref)
+
+
+def _run(w, x, act_group, target, M=None):
+    xd = _dev(x)
+    xq, xs = bn.bitnest_quant_act(xd, act_group)
+    hi, lo, sc = _dev(w.hi), (_dev(w.lo) if target else None), _dev(w.scale)
+    if target:
+        y = bn.bitnest_linear_target(xq, xs, hi, lo, sc, act_group)
+    else:
+        y = bn.bitnest_linear_draft(xq, xs, hi, sc, act_group)
+    torch.cuda.synchronize()
+    return xq, xs, y
+
+
+# --------------------------------------------------------------------------- activation quant
+
+@pytest.mark.parametrize("M,K,act_group", [
+    (1, 512, 0), (1, 4096, 0), (4, 4096, 0), (3, 14336, 0), (32, 4096, 0), (7, 16384, 0),
+    (1, 128, 0), (1, 4096, 128), (4, 4096, 128), (13, 640, 128), (32, 14336, 128), (5, 128, 128),
+])
+def test_quant_act_bit_exact(M, K, act_group):
+    x = synth.make_activations(M, K, seed=1, layer=K, linear=M)
+    if M > 2:
+        x[1] = 0.0                                   # a zero token: s = 0, q = 0
+    xq, xs = bn.bitnest_quant_act(_dev(x), act_group)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quant_act_ties_golden_on_gpu(golden_dir):
+    import json, os
+    fx = json.load(open(os.path.join(golden_dir, "act_quant.json")))
+    rows = []
+    for case in fx["per_token"]:
+        r = np.zeros(GROUP, np.float32)
+        r[:len(case["x"])] = case["x"]
+        rows.append(r)
+    x = torch.from_numpy(np.stack(rows))
+    xq, xs = bn.bitnest_quant_act(_dev(x))
+    torch.cuda.synchronize()
+    for i, case in enumerate(fx["per_token"]):
+        assert xs[i].item() == case["s"]
+        assert xq[i, :len(case["q"])].cpu().tolist() == case["q"]
+
+
+# --------------------------------------------------------------------------- partials
+
+SHAPES = [(256, 512), (37, 640), (70, 2176), (33, 14336), (5, 128), (129, 4096), (17, 16384)]
+MS = [1, 2, 3, 4, 5, 7, 8, 13, 16, 17, 32]
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("M", MS)
+def test_partials_bit_exact(M, N, K):
+    w, x = _problem(M, N, K)
+    q, _ = oracle.quant_act(x.numpy())
+    xq = _dev(torch.from_numpy(q))
+    hi, lo, _ = w.numpy()
+    g_hi, g_lo, g_8 = bn.bitnest_linear_partials(xq, _dev(w.hi), _dev(w.lo))
+    d_hi = bn.bitnest_linear_partials(xq, _dev(w.hi))
+    torch.cuda.synchronize()
+    r_hi, r_lo, r_8 = oracle.partials(q, hi, lo)
+    assert np.array_equal(g_hi.cpu().numpy(), r_hi)
+    assert np.array_equal(g_lo.cpu().numpy(), r_lo)
+    assert np.array_equal(g_8.cpu().numpy(), r_8)
+    assert np.array_equal(d_hi.cpu().numpy(), r_hi)
+
+
+def test_partials_reach_their_bounds():
+    # every code -8 (nibble 0) against codes -127: |P_hi| = 127*8*128 and
+    # |P8| = 127*136*128 exactly, on both kernels
+    for M in (1, 4, 8, 32):
+        xq = torch.full((M, 256), -127, dtype=torch.int8, device="cuda")
+        z = torch.zeros((3, 128), dtype=torch.uint8, device="cuda")
+        p_hi, p_lo, p8 = bn.bitnest_linear_partials(xq, z, z)
+        torch.cuda.synchronize()
+        assert int(p_hi.min()) == int(p_hi.max()) == 127 * 8 * 128
+        assert int(p8.min()) == int(p8.max()) == 127 * 136 * 128
+        assert int(p_lo.max()) == 127 * 8 * 128
+
+
+# --------------------------------------------------------------------------- fp32 outputs
+
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("M", [1, 3, 4, 7, 8, 16, 32])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_linear_matches_oracle(M, N, K, act_group, target):
+    w, x = _problem(M, N, K, seed=2)
+    xq, xs, y = _run(w, x, act_group, target)
+    hi, lo, sc = w.numpy()
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    y64 = oracle.linear(q, s, hi, sc, lo if target else None, act_group)
+    _check_y(y, y64, "M=%d N=%d K=%d g=%d t=%s" % (M, N, K, act_group, target))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 32])
+@pytest.mark.parametrize("act_group", [0, 128])
+def test_target_equals_draft_when_lo_is_8(M, act_group):
+    N, K = 96, 2176
+    w, x = _problem(M, N, K, seed=3)
+    xd = _dev(x)
+    xq, xs = bn.bitnest_quant_act(xd, act_group)
+    hi, sc = _dev(w.hi), _dev(w.scale)
+    lo8 = torch.full_like(hi, 0x88)
+    yd = bn.bitnest_linear_draft(xq, xs, hi, sc, act_group)
+    yt = bn.bitnest_linear_target(xq, xs, hi, lo8, sc, act_group)
+    torch.cuda.synchronize()
+    assert torch.equal(yd.view(torch.int32), yt.view(torch.int32))
+
+
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_verify_batch_rows_equal_single_token_calls(act_group, target):
+    # GEMV: one M = 4 call == four M = 1 calls, bit for bit (y and partials).
+    N, K = 200, 4096
+    w, x = _problem(4, N, K, seed=4)
+    _, _, y4 = _run(w, x, act_group, target)
+    for m in range(4):
+        _, _, y1 = _run(w, x[m:m + 1], act_group, target)
+        assert torch.equal(y1[0].view(torch.int32), y4[m].view(torch.int32)), m
+    xq, _ = bn.bitnest_quant_act(_dev(x))
+    p4 = bn.bitnest_linear_partials(xq, _dev(w.hi), _dev(w.lo))
+    for m in range(4):
+        p1 = bn.bitnest_linear_partials(xq[m:m + 1].contiguous(), _dev(w.hi), _dev(w.lo))
+        for a, b in zip(p1, p4):
+            assert torch.equal(a[0], b[m])
+
+
+@pytest.mark.parametrize("target", [False, True])
+def test_batched_verify_rows_do_not_depend_on_batch(target):
+    # The matrix-core kernel: rows of an M = 32 call equal an M = 8 and an
+    # M = 16 call on the same tokens, bit for bit.
+    N, K = 160, 4096
+    w, x = _problem(32, N, K, seed=5)
+    _, _, y32 = _run(w, x, 0, target)
+    _, _, y8 = _run(w, x[:8], 0, target)
+    _, _, y16 = _run(w, x[8:24], 0, target)
+    assert torch.equal(y8.view(torch.int32), y32[:8].view(torch.int32))
+    assert torch.equal(y16.view(torch.int32), y32[8:24].view(torch.int32))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_repeated_calls_are_bit_identical(M):
+    N, K = 1000, 4096
+    w, x = _problem(M, N, K, seed=6)
+    xq, xs = bn.bitnest_quant_act(_dev(x))
+    hi, lo, sc = _dev(w.hi), _dev(w.lo), _dev(w.scale)
+    ref = bn.bitnest_linear_target(xq, xs, hi, lo, sc)
+    for _ in range(10):
+        y = bn.bitnest_linear_target(xq, xs, hi, lo, sc)
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+
+
+def test_zero_activations_give_zero_outputs():
+    for M in (1, 8):
+        x = torch.zeros((M, 512), device="cuda")
+        xq, xs = bn.bitnest_quant_act(x)
+        w = synth.make_weights(64, 512)
+        y = bn.bitnest_linear_target(xq, xs, _dev(w.hi), _dev(w.lo), _dev(w.scale))
+        torch.cuda.synchronize()
+        assert float(xs.abs().max()) == 0.0 and int(xq.abs().max()) == 0
+        assert float(y.abs().max()) == 0.0
+
+
+def test_empty_calls_are_noops():
+    xq = torch.zeros((0, 256), dtype=torch.int8, device="cuda")
+    xs = torch.zeros((0,), dtype=torch.float32, device="cuda")
+    w = synth.make_weights(8, 256)
+    y = bn.bitnest_linear_draft(xq, xs, _dev(w.hi), _dev(w.scale))
+    assert y.shape == (0, 8)
+    xq1 = torch.zeros((2, 256), dtype=torch.int8, device="cuda")
+    xs1 = torch.ones((2,), dtype=torch.float32, device="cuda")
+    hi0 = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
+    sc0 = torch.zeros((0, 2), dtype=torch.int16, device="cuda")
+    y0 = bn.bitnest_linear_target(xq1, xs1, hi0, hi0, sc0)
+    assert y0.shape == (2, 0)
+
+
+def test_misaligned_pointer_is_rejected_on_gpu():
+    buf = torch.zeros(4096 + 16, dtype=torch.uint8, device="cuda")
+    hi = buf[4:4 + 8 * 64].view(8, 64)              # offset 4 bytes: misaligned
+    xq = torch.zeros((1, 128), dtype=torch.int8, device="cuda")
+    xs = torch.ones((1,), dtype=torch.float32, device="cuda")
+    sc = torch.zeros((8, 1), dtype=torch.int16, device="cuda")
+    with pytest.raises(bn.BitnestError) as e:
+        bn.bitnest_linear_draft(xq, xs, hi, sc)
+    assert e.value.status == bn.EALIGN
+
+
+def test_runs_on_a_side_stream():
+    N, K, M = 300, 4096, 4
+    w, x = _problem(M, N, K, seed=7)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd = _dev(x)
+        xq, xs = bn.bitnest_quant_act(xd)
+        y = bn.bitnest_linear_target(xq, xs, _dev(w.hi), _dev(w.lo), _dev(w.scale))
+    s.synchronize()
+    hi, lo, sc = w.numpy()
+    q, sa = oracle.quant_act(x.numpy())
+    assert np.array_equal(xq.cpu().numpy(), q)
+    _check_y(y, oracle.linear(q, sa, hi, sc, lo), "side stream")
+
+
+# --------------------------------------------------------------------------- full-size layers
+
+@pytest.fixture(scope="module")
+def llama_layer():
+    """One Llama-3-8B decoder layer's four linears (seed 0, layer 0), both planes."""
+    out = []
+    for li, (name, N, K, g) in enumerate(synth.LLAMA3_8B_LINEARS):
+        w = synth.make_weights(N, K, seed=0, layer=0, linear=li)
+        out.append((name, N, K, g, w, w.to("cuda")))
+    return out
+
+
+def _rows_sample(N, n=384):
+    idx = np.unique(np.concatenate([np.linspace(0, N - 1, n).astype(int), np.arange(N - 16, N)]))
+    return idx
+
+
+@pytest.mark.parametrize("M,target", [(1, False), (1, True), (4, True), (8, True), (16, True), (32, True)])
+def test_llama_layer_full_size(llama_layer, M, target):
+    for li, (name, N, K, g, w, wd) in enumerate(llama_layer):
+        x = synth.make_activations(M, K, seed=0, layer=0, linear=li)
+        xq, xs = bn.bitnest_quant_act(_dev(x), g)
+        if target:
+            y = bn.bitnest_linear_target(xq, xs, wd.hi, wd.lo, wd.scale, g)
+        else:
+            y = bn.bitnest_linear_draft(xq, xs, wd.hi, wd.scale, g)
+        torch.cuda.synchronize()
+        q_ref, s_ref = oracle.quant_act(x.numpy(), g)
+        assert np.array_equal(xq.cpu().numpy(), q_ref), name
+        assert np.array_equal(xs.cpu().numpy(), s_ref), name
+        hi, lo, sc = w.numpy()
+        rows = _rows_sample(N) if M > 1 else np.arange(N)
+        y64 = oracle.linear(q_ref, s_ref, np.ascontiguousarray(hi[rows]), np.ascontiguousarray(sc[rows]),
+                            np.ascontiguousarray(lo[rows]) if target else None, g)
+        _check_y(y[:, torch.from_numpy(rows).cuda()], y64, "%s M=%d target=%s" % (name, M, target))
+        if M in (1, 8):
+            p = bn.bitnest_linear_partials(xq, wd.hi[:64].contiguous(), wd.lo[:64].contiguous())
+            r = oracle.partials(q_ref, hi[:64], lo[:64])
+            for a, b in zip(p, r):
+                assert np.array_equal(a.cpu().numpy(), b), name

@@ -1,0 +1,191 @@
+"""Bit-nested W4/W8 quantized linear on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/bitnest.h`` (library
+``libbitnest.so`` in this directory, built by ``build.py``). The functions
+keep the C names and only marshal arguments: they check dtypes, shapes and
+devices of torch tensors, pass their device pointers and torch's current
+stream, and raise ``BitnestError`` on a non-zero status. Every step of the
+computation runs in the HIP kernels; there is no CPU or PyTorch fallback, and
+calling any of them without the built library raises at once.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BitnestError", "GROUP", "MAX_M", "MAX_K", "library_path", "lib",
+    "bitnest_abi_version", "bitnest_status_string", "bitnest_quant_act",
+    "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
+]
+
+GROUP = 128
+MAX_M = 32
+MAX_K = 16384
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libbitnest.so")
+
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+
+_lib = None
+
+
+class BitnestError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: status %d (%s)" % (what, status, bitnest_status_string(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library, with argument types declared. Raises if not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                "libbitnest.so is not built (%s); run `python -m w8_quantized_linear_amd.build` "
+                "or __graft_entry__.build() first" % library_path)
+        L = ctypes.CDLL(library_path)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.bitnest_abi_version.argtypes = []
+        L.bitnest_abi_version.restype = I
+        L.bitnest_status_string.argtypes = [I]
+        L.bitnest_status_string.restype = ctypes.c_char_p
+        L.bitnest_quant_act.argtypes = [P, I, I, I, P, P, P]
+        L.bitnest_linear_draft.argtypes = [P, P, I, P, P, P, I, I, I, P]
+        L.bitnest_linear_target.argtypes = [P, P, I, P, P, P, P, I, I, I, P]
+        L.bitnest_linear_partials.argtypes = [P, P, P, P, P, P, I, I, I, P]
+        for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
+                  "bitnest_linear_partials"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def bitnest_abi_version() -> int:
+    return lib().bitnest_abi_version()
+
+
+def bitnest_status_string(status: int) -> str:
+    return lib().bitnest_status_string(int(status)).decode()
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _call(status: int, what: str):
+    if status != OK:
+        raise BitnestError(status, what)
+
+
+def _scale_tensor(scale: torch.Tensor) -> torch.Tensor:
+    # fp16 scales may come as float16 or as their int16 bit patterns
+    if scale.dtype == torch.float16:
+        return scale.view(torch.int16)
+    return scale
+
+
+def bitnest_quant_act(x: torch.Tensor, act_group: int = 0, xq: torch.Tensor | None = None,
+                      xs: torch.Tensor | None = None):
+    """x fp32 [M, K] -> (xq int8 [M, K], xs fp32 [M] or [M, K/128])."""
+    _need(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,) if act_group == 0 else (M, K // GROUP), dtype=torch.float32, device=x.device)
+    _need(xq, "xq", torch.int8, (M, K))
+    _need(xs, "xs", torch.float32, (M,) if act_group == 0 else (M, K // GROUP))
+    _call(lib().bitnest_quant_act(_p(x), M, K, act_group, _p(xq), _p(xs), _stream(x)), "bitnest_quant_act")
+    return xq, xs
+
+
+def _linear_shapes(xq, xs, hi, scale, act_group):
+    _need(xq, "xq", torch.int8)
+    if xq.dim() != 2:
+        raise ValueError("xq must be [M, K]")
+    M, K = xq.shape
+    _need(hi, "hi", torch.uint8)
+    if hi.dim() != 2 or hi.shape[1] * 2 != K:
+        raise ValueError("hi must be [N, K/2] with K=%d, got %s" % (K, tuple(hi.shape)))
+    N = hi.shape[0]
+    _need(scale, "scale", torch.int16, (N, K // GROUP))
+    _need(xs, "xs", torch.float32, (M,) if act_group == 0 else (M, K // GROUP))
+    return M, N, K
+
+
+def bitnest_linear_draft(xq: torch.Tensor, xs: torch.Tensor, hi: torch.Tensor, scale: torch.Tensor,
+                         act_group: int = 0, y: torch.Tensor | None = None) -> torch.Tensor:
+    """Draft W4A8 linear: y fp32 [M, N] from the hi plane only."""
+    scale = _scale_tensor(scale)
+    M, N, K = _linear_shapes(xq, xs, hi, scale, act_group)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _need(y, "y", torch.float32, (M, N))
+    _call(lib().bitnest_linear_draft(_p(xq), _p(xs), act_group, _p(hi), _p(scale), _p(y), M, N, K,
+                                     _stream(xq)), "bitnest_linear_draft")
+    return y
+
+
+def bitnest_linear_target(xq: torch.Tensor, xs: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor,
+                          scale: torch.Tensor, act_group: int = 0,
+                          y: torch.Tensor | None = None) -> torch.Tensor:
+    """Target W8A8 linear: y fp32 [M, N] from the hi and lo planes."""
+    scale = _scale_tensor(scale)
+    M, N, K = _linear_shapes(xq, xs, hi, scale, act_group)
+    _need(lo, "lo", torch.uint8, tuple(hi.shape))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _need(y, "y", torch.float32, (M, N))
+    _call(lib().bitnest_linear_target(_p(xq), _p(xs), act_group, _p(hi), _p(lo), _p(scale), _p(y),
+                                      M, N, K, _stream(xq)), "bitnest_linear_target")
+    return y
+
+
+def bitnest_linear_partials(xq: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor | None = None):
+    """Integer partials int32 [M, N, K/128]: P_hi, or (P_hi, P_lo, P8) with ``lo``."""
+    _need(xq, "xq", torch.int8)
+    M, K = xq.shape
+    _need(hi, "hi", torch.uint8)
+    if hi.dim() != 2 or hi.shape[1] * 2 != K:
+        raise ValueError("hi must be [N, K/2]")
+    N = hi.shape[0]
+    G = K // GROUP
+    p_hi = torch.empty((M, N, G), dtype=torch.int32, device=xq.device)
+    p_lo = p8 = None
+    if lo is not None:
+        _need(lo, "lo", torch.uint8, tuple(hi.shape))
+        p_lo = torch.empty_like(p_hi)
+        p8 = torch.empty_like(p_hi)
+    _call(lib().bitnest_linear_partials(_p(xq), _p(hi), _p(lo), _p(p_hi), _p(p_lo), _p(p8), M, N, K,
+                                        _stream(xq)), "bitnest_linear_partials")
+    return p_hi if lo is None else (p_hi, p_lo, p8)
+
+
+# Short aliases
+quant_act = bitnest_quant_act
+linear_draft = bitnest_linear_draft
+linear_target = bitnest_linear_target
+linear_partials = bitnest_linear_partials

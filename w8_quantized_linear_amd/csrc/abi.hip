@@ -1,0 +1,132 @@
+// C ABI of the nested W4/W8 linear (declared and documented in bitnest.h).
+// Arguments are validated on the host before any HIP call; then the call is
+// dispatched by M: the plane-streaming GEMV for M <= 7, the int8 matrix-core
+// kernel for 8 <= M <= 32.
+#include "bitnest.h"
+#include "bitnest_internal.h"
+
+#include <atomic>
+
+namespace bitnest {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_lds[kMaxDevices];
+}  // namespace
+
+hipError_t device_info(DeviceInfo *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int cus = g_cus[dev].load(std::memory_order_acquire);
+    int lds = g_lds[dev].load(std::memory_order_acquire);
+    if (cus <= 0 || lds <= 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) return e;
+        g_cus[dev].store(cus, std::memory_order_release);
+        g_lds[dev].store(lds, std::memory_order_release);
+    }
+    out->cus = cus;
+    out->max_lds = lds;
+    return hipSuccess;
+}
+
+}  // namespace bitnest
+
+namespace {
+
+using bitnest::kGroup;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared size checks for the linear calls. Returns BITNEST_OK or an error.
+bitnest_status check_sizes(int M, int N, int K) {
+    if (M < 0 || N < 0 || K <= 0 || K % kGroup != 0) return BITNEST_EINVAL;
+    if (M > BITNEST_MAX_M || K > BITNEST_MAX_K) return BITNEST_EUNSUPPORTED;
+    return BITNEST_OK;
+}
+
+bitnest_status to_status(hipError_t e) { return e == hipSuccess ? BITNEST_OK : BITNEST_EHIP; }
+
+bitnest_status run_linear(const bitnest::LinearArgs &a, bool exporting, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.M <= bitnest::kGemvMaxM) return to_status(bitnest::launch_gemv(a, exporting, s));
+    return to_status(bitnest::launch_verify_mfma(a, exporting, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitnest_abi_version(void) { return BITNEST_ABI_VERSION; }
+
+const char *bitnest_status_string(int status) {
+    switch (status) {
+        case BITNEST_OK: return "ok";
+        case BITNEST_EINVAL: return "invalid argument (null pointer, negative size, K not a positive multiple of 128, or act_group not 0/128)";
+        case BITNEST_EALIGN: return "tensor pointer not 16-byte aligned";
+        case BITNEST_EUNSUPPORTED: return "size beyond the library limits (M > BITNEST_MAX_M or K > BITNEST_MAX_K)";
+        case BITNEST_EHIP: return "HIP runtime error while launching";
+        default: return "unknown status";
+    }
+}
+
+bitnest_status bitnest_quant_act(const float *x, int M, int K, int act_group, int8_t *xq, float *xs,
+                                 void *stream) {
+    if (act_group != 0 && act_group != kGroup) return BITNEST_EINVAL;
+    // quantisation takes any number of tokens; only K is bounded
+    if (M < 0 || K <= 0 || K % kGroup != 0) return BITNEST_EINVAL;
+    if (K > BITNEST_MAX_K) return BITNEST_EUNSUPPORTED;
+    if (M == 0) return BITNEST_OK;                  // empty: pointers may be NULL
+    if (!x || !xq || !xs) return BITNEST_EINVAL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return BITNEST_EALIGN;
+    return to_status(bitnest::launch_quant_act(x, M, K, act_group, xq, xs, static_cast<hipStream_t>(stream)));
+}
+
+bitnest_status bitnest_linear_draft(const int8_t *xq, const float *xs, int act_group, const uint8_t *hi,
+                                    const uint16_t *scale, float *y, int M, int N, int K, void *stream) {
+    if (act_group != 0 && act_group != kGroup) return BITNEST_EINVAL;
+    bitnest_status st = check_sizes(M, N, K);
+    if (st != BITNEST_OK) return st;
+    if (M == 0 || N == 0) return BITNEST_OK;        // empty: pointers may be NULL
+    if (!xq || !xs || !hi || !scale || !y) return BITNEST_EINVAL;
+    if (!aligned16(xq) || !aligned16(xs) || !aligned16(hi) || !aligned16(scale) || !aligned16(y))
+        return BITNEST_EALIGN;
+    bitnest::LinearArgs a{xq, xs, hi, nullptr, scale, y, nullptr, nullptr, nullptr, M, N, K, act_group};
+    return run_linear(a, false, stream);
+}
+
+bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_group, const uint8_t *hi,
+                                     const uint8_t *lo, const uint16_t *scale, float *y, int M, int N, int K,
+                                     void *stream) {
+    if (act_group != 0 && act_group != kGroup) return BITNEST_EINVAL;
+    bitnest_status st = check_sizes(M, N, K);
+    if (st != BITNEST_OK) return st;
+    if (M == 0 || N == 0) return BITNEST_OK;        // empty: pointers may be NULL
+    if (!xq || !xs || !hi || !lo || !scale || !y) return BITNEST_EINVAL;
+    if (!aligned16(xq) || !aligned16(xs) || !aligned16(hi) || !aligned16(lo) || !aligned16(scale) ||
+        !aligned16(y))
+        return BITNEST_EALIGN;
+    bitnest::LinearArgs a{xq, xs, hi, lo, scale, y, nullptr, nullptr, nullptr, M, N, K, act_group};
+    return run_linear(a, false, stream);
+}
+
+bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo, int32_t *p_hi,
+                                       int32_t *p_lo, int32_t *p8, int M, int N, int K, void *stream) {
+    bitnest_status st = check_sizes(M, N, K);
+    if (st != BITNEST_OK) return st;
+    if (M == 0 || N == 0) return BITNEST_OK;        // empty: pointers may be NULL
+    if (!xq || !hi || !p_hi) return BITNEST_EINVAL;
+    if (lo && (!p_lo || !p8)) return BITNEST_EINVAL;
+    if (!aligned16(xq) || !aligned16(hi) || !aligned16(p_hi)) return BITNEST_EALIGN;
+    if (lo && (!aligned16(lo) || !aligned16(p_lo) || !aligned16(p8))) return BITNEST_EALIGN;
+    bitnest::LinearArgs a{xq, nullptr, hi, lo, nullptr, nullptr, p_hi, lo ? p_lo : nullptr, lo ? p8 : nullptr,
+                          M, N, K, 0};
+    return run_linear(a, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (abi.hip) and the gfx950 kernels.
+// Not installed; the public interface is include/bitnest.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnest {
+
+constexpr int kGroup = 128;     // columns per weight scale and per grouped act scale
+constexpr int kGemvMaxM = 7;    // tokens handled by the plane-streaming GEMV
+constexpr int kMaxM = 32;       // tokens handled by the batched-verify matrix-core kernel
+constexpr int kMaxK = 16384;
+
+// Per-device facts the launchers need, read once per device.
+struct DeviceInfo {
+    int cus = 0;                // compute units
+    int max_lds = 0;            // bytes of LDS one workgroup may use
+};
+hipError_t device_info(DeviceInfo *out);
+
+// Everything a linear launch needs. Pointers are device pointers.
+struct LinearArgs {
+    const int8_t *xq;
+    const float *xs;
+    const uint8_t *hi;
+    const uint8_t *lo;          // nullptr: draft
+    const uint16_t *scale;
+    float *y;
+    int32_t *p_hi;              // partials export (nullptr unless exporting)
+    int32_t *p_lo;
+    int32_t *p8;
+    int M, N, K;
+    int act_group;              // 0 or 128
+};
+
+hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t *xq, float *xs,
+                            hipStream_t stream);
+
+// M <= kGemvMaxM. export_partials selects the integer export instead of y.
+hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream);
+
+// 8 <= M <= kMaxM.
+hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStream_t stream);
+
+}  // namespace bitnest

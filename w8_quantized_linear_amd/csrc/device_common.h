@@ -1,0 +1,70 @@
+// Small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnest {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// fp16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// 16 bytes that are read exactly once per call: non-temporal, so the plane
+// stream does not evict the activations and scales from the caches.
+__device__ __forceinline__ u32x4 load_stream16(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// DPP lane moves (gfx9 encodings of the dpp_ctrl field).
+enum : int {
+    kDppQuadSwap1 = 0xB1,   // quad_perm [1,0,3,2]
+    kDppQuadSwap2 = 0x4E,   // quad_perm [2,3,0,1]
+    kDppRowRor4 = 0x124,    // rotate right by 4 within each row of 16 lanes
+    kDppRowRor8 = 0x128,    // rotate right by 8 within each row of 16 lanes
+};
+
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                  kCtrl, 0xF, 0xF, false));
+}
+
+// Exact integer sum over the 4 lanes of a quad; every lane of the quad gets it.
+__device__ __forceinline__ int quad_sum_i32(int v) {
+    v += dpp_i32<kDppQuadSwap1>(v);
+    v += dpp_i32<kDppQuadSwap2>(v);
+    return v;
+}
+
+// Sum over the 16 quads of a wave of a value that is uniform within each quad.
+// The association order is fixed, so the result is deterministic. Lane 0
+// holds the sum (all lanes do, with lane-dependent association).
+__device__ __forceinline__ float sum_over_quads_f32(float v) {
+    v += dpp_f32<kDppRowRor4>(v);
+    v += dpp_f32<kDppRowRor8>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int sdot4(unsigned a, unsigned b, int acc) {
+    return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), acc, false);
+}
+
+}  // namespace bitnest

@@ -1,0 +1,117 @@
+// Activation quantisation to symmetric int8 (BitNest-Llama-3-8B model card,
+// recipe table row "Activations": per token, and per 128-column group for
+// o_proj). The rule, which the pages leave open and the public header states:
+//   s = amax / 127 (IEEE fp32 division), q = 0 if s == 0, otherwise
+//   q = clamp(round_half_even(x / s), -127, 127) with x / s an IEEE fp32
+//   division (hipcc's default division is correctly rounded; no fast-math).
+//
+// The work is a few KiB per token and latency-bound: one workgroup per token
+// holds its whole row in registers (one HBM round trip), reduces |x| with
+// wave shuffles and writes packed codes with 4-byte stores.
+#include "bitnest_internal.h"
+#include "device_common.h"
+
+namespace bitnest {
+namespace {
+
+constexpr int kQuantThreads = 256;
+
+__device__ __forceinline__ int code_of(float x, float s) {
+    if (s == 0.0f) return 0;
+    float r = rintf(x / s);                 // v_rndne_f32: ties to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return static_cast<int>(r);
+}
+
+__device__ __forceinline__ unsigned pack4(const float4 &v, float s) {
+    return (static_cast<unsigned>(code_of(v.x, s)) & 0xFFu) |
+           ((static_cast<unsigned>(code_of(v.y, s)) & 0xFFu) << 8) |
+           ((static_cast<unsigned>(code_of(v.z, s)) & 0xFFu) << 16) |
+           ((static_cast<unsigned>(code_of(v.w, s)) & 0xFFu) << 24);
+}
+
+__device__ __forceinline__ float absmax4(const float4 &v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// One token per workgroup; each thread keeps up to NV float4 of the row.
+template <int NV>
+__global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(
+    const float *__restrict__ x, int K, int8_t *__restrict__ q, float *__restrict__ s) {
+    __shared__ float part[kQuantThreads / 64];
+    const int m = blockIdx.x;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + static_cast<size_t>(m) * K);
+    const int n4 = K >> 2;
+    float4 v[NV];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = threadIdx.x + i * kQuantThreads;
+        if (idx < n4) {
+            v[i] = xr[idx];
+            amax = fmaxf(amax, absmax4(v[i]));
+        }
+    }
+    amax = wave_max_f32(amax);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    const float sc = amax / 127.0f;
+    if (threadIdx.x == 0) s[m] = sc;
+    unsigned *qr = reinterpret_cast<unsigned *>(q + static_cast<size_t>(m) * K);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = threadIdx.x + i * kQuantThreads;
+        if (idx < n4) qr[idx] = pack4(v[i], sc);
+    }
+}
+
+// One (token, 128-column group) per 32 lanes, eight per workgroup. Row-major
+// x [M, K] makes (m, g) -> m*K + 128 g = 128 (m*G + g), so the flat group
+// index addresses both x/q and the [M, K/128] scales.
+__global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
+    const float *__restrict__ x, int total_groups, int8_t *__restrict__ q, float *__restrict__ s) {
+    const int gid = blockIdx.x * (kQuantThreads / 32) + (threadIdx.x >> 5);
+    const int l = threadIdx.x & 31;
+    const bool active = gid < total_groups;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (active) v = reinterpret_cast<const float4 *>(x + static_cast<size_t>(gid) * kGroup)[l];
+    float amax = absmax4(v);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float sc = amax / 127.0f;
+    if (active) {
+        if (l == 0) s[gid] = sc;
+        reinterpret_cast<unsigned *>(q + static_cast<size_t>(gid) * kGroup)[l] = pack4(v, sc);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t *xq, float *xs,
+                            hipStream_t stream) {
+    if (act_group == kGroup) {
+        const int total = M * (K / kGroup);
+        const int per_block = kQuantThreads / 32;
+        const int blocks = (total + per_block - 1) / per_block;
+        hipLaunchKernelGGL(quant_group_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x,
+                           total, xq, xs);
+    } else {
+        const int nv = (K / 4 + kQuantThreads - 1) / kQuantThreads;   // float4 per thread
+        if (nv <= 1)
+            hipLaunchKernelGGL(quant_token_kernel<1>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+        else if (nv <= 2)
+            hipLaunchKernelGGL(quant_token_kernel<2>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+        else if (nv <= 4)
+            hipLaunchKernelGGL(quant_token_kernel<4>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+        else if (nv <= 8)
+            hipLaunchKernelGGL(quant_token_kernel<8>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+        else if (nv <= 16)
+            hipLaunchKernelGGL(quant_token_kernel<16>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+        else
+            return hipErrorInvalidValue;   // K > kMaxK: rejected by the ABI before this point
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bitnest
