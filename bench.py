@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the bit-nested W4/W8 linear on one MI355X.
+
+Workload (one "step"): one speculative decoding round over the linear stack of
+Llama-3-8B (32 decoder layers, linears qkv 6144x4096, o_proj 4096x4096 with
+per-128-group activation scales, gate_up 28672x4096, down 4096x14336; the
+base model and the default draft length gamma = 3 of the BitNest-Llama-3-8B
+model card): three draft passes at M = 1 (hi plane only) and one target
+(verify) pass at M = gamma + 1 = 4 (hi and lo planes). Every linear is an
+activation quantisation followed by the nested linear, so one round is
+4 passes x 32 layers x 4 linears x 2 kernels = 1024 launches, replayed from
+one HIP graph. Weights are seeded synthetic tensors in the layout and with
+the distributions of the weight package (generated on the GPU, 3.49 GB per
+plane, so the stream is far larger than the 256 MB Infinity Cache); they are
+resident in HBM before timing starts.
+
+Printed: one JSON line with the aggregate plane GB/s of the round (plane bytes
+read / time per round), the roofline of the dominant kernel (the
+plane-streaming GEMV, timed per launch with HIP events on the launch stream)
+and the CPU oracle's throughput on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+GAMMA = 3
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-baseline", dest="cpu_baseline", action="store_true", default=True)
+    p.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU work for the oracle baseline sample")
+    p.add_argument("--no-kernel-timing", dest="kernel_timing", action="store_false", default=True)
+    p.add_argument("--verbose", action="store_true")
+    return p.parse_args(argv)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Stack:
+    """Weights of every layer and the per-pass activation inputs, on the GPU."""
+
+    def __init__(self, layers, seed, device):
+        import torch
+        from w8_quantized_linear_amd import synth
+        self.linears = synth.LLAMA3_8B_LINEARS
+        self.layers = layers
+        self.w = []
+        for l in range(layers):
+            self.w.append([synth.make_weights(N, K, seed=seed, layer=l, linear=i, device=device)
+                           for i, (_, N, K, _) in enumerate(self.linears)])
+        # activation inputs: draft pass p (M = 1) and the verify pass (M = gamma + 1)
+        self.x_draft = [[[synth.make_activations(1, K, seed=seed, layer=l, linear=i, step=p, device=device)
+                          for i, (_, _, K, _) in enumerate(self.linears)] for l in range(layers)]
+                        for p in range(GAMMA)]
+        self.x_verify = [[synth.make_activations(GAMMA + 1, K, seed=seed, layer=l, linear=i, step=GAMMA,
+                                                 device=device)
+                          for i, (_, _, K, _) in enumerate(self.linears)] for l in range(layers)]
+        # per-shape work buffers (reused across layers, as a decoder would)
+        self.buf = {}
+        for M in (1, GAMMA + 1):
+            for i, (_, N, K, g) in enumerate(self.linears):
+                self.buf[(M, i)] = (
+                    torch.empty((M, K), dtype=torch.int8, device=device),
+                    torch.empty((M,) if g == 0 else (M, K // 128), dtype=torch.float32, device=device),
+                    torch.empty((M, N), dtype=torch.float32, device=device))
+        torch.cuda.synchronize()
+
+    def plane_bytes_per_round(self):
+        per_layer = sum(N * K // 2 for (_, N, K, _) in self.linears)
+        return self.layers * per_layer * (GAMMA * 1 + 2)
+
+    def gemv_algorithmic_bytes_per_round(self):
+        """Bytes every GEMV launch of a round must move at least (planes, scales,
+        codes, activation scales, outputs), summed over the round."""
+        tot = 0
+        for M, planes, passes in ((1, 1, GAMMA), (GAMMA + 1, 2, 1)):
+            for (_, N, K, g) in self.linears:
+                S = 1 if g == 0 else K // 128
+                tot += passes * self.layers * (planes * N * K // 2 + N * (K // 128) * 2 + M * K + M * S * 4 + M * N * 4)
+        return tot
+
+    def gemv_launches_per_round(self):
+        return (GAMMA + 1) * self.layers * len(self.linears)
+
+
+def run_round(stack, bn, quant=True):
+    """One speculative round: 3 draft passes at M = 1, one verify pass at M = 4.
+    quant=False launches only the GEMVs (on the codes already in the buffers),
+    which is how the GEMV launches are timed on their own."""
+    for p in range(GAMMA + 1):
+        verify = p == GAMMA
+        M = GAMMA + 1 if verify else 1
+        for l in range(stack.layers):
+            for i, (_, N, K, g) in enumerate(stack.linears):
+                xq, xs, y = stack.buf[(M, i)]
+                w = stack.w[l][i]
+                if quant:
+                    x = stack.x_verify[l][i] if verify else stack.x_draft[p][l][i]
+                    bn.bitnest_quant_act(x, g, xq=xq, xs=xs)
+                if verify:
+                    bn.bitnest_linear_target(xq, xs, w.hi, w.lo, w.scale, g, y=y)
+                else:
+                    bn.bitnest_linear_draft(xq, xs, w.hi, w.scale, g, y=y)
+
+
+def capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                      # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def gemv_kernel_timing(stack, bn, steps):
+    """Average GEMV launch duration: the round's 512 GEMV launches (same
+    shapes, weights and order, without the quantisation launches) replayed
+    back to back from a HIP graph, timed with HIP events on the stream they
+    run on, divided by the number of launches. The short gaps between
+    dispatches are included, so this slightly overstates the duration."""
+    import torch
+    n = stack.gemv_launches_per_round()
+    g = capture(lambda: run_round(stack, bn, quant=False))
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(max(3, steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / n)
+    per.sort()
+    return per[len(per) // 2] * 1e-3     # seconds per launch, median over replays
+
+
+def cpu_baseline(stack, budget_s):
+    """The oracle on the machine's host cores over a bounded sample of the round:
+    the first layer(s) of the stack, 3 draft passes + 1 verify pass each,
+    quantisation plus linear, until about `budget_s` seconds of CPU work."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    done_bytes = 0
+    t_total = 0.0
+    layers_done = 0
+    for l in range(stack.layers):
+        host = [w.numpy() for w in stack.w[l]]
+        t0 = time.perf_counter()
+        for p in range(GAMMA + 1):
+            verify = p == GAMMA
+            for i, (_, N, K, g) in enumerate(stack.linears):
+                x = (stack.x_verify[l][i] if verify else stack.x_draft[p][l][i]).cpu().numpy()
+                hi, lo, sc = host[i]
+                q, s = oracle.quant_act(x, g)
+                oracle.linear(q, s, hi, sc, lo if verify else None, g, threads=threads)
+                done_bytes += N * K // 2 * (2 if verify else 1)
+        t_total += time.perf_counter() - t0
+        layers_done += 1
+        if t_total >= budget_s:
+            break
+    gbs = done_bytes / t_total / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d layers of the round (3 draft passes at M=1 + 1 verify pass at M=4 per layer, "
+                      "activation quant + dequantise-then-multiply in fp64), %.1f s; plane bytes %d"
+                      % (layers_done, stack.layers, t_total, done_bytes)}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+    import torch
+    import w8_quantized_linear_amd as bn
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    bn.lib()                            # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    t0 = time.perf_counter()
+    stack = Stack(args.layers, args.seed, dev)
+    log("stack ready: %d layers, %.2f GB of planes per round, %.1f s"
+        % (args.layers, stack.plane_bytes_per_round() / 1e9, time.perf_counter() - t0))
+
+    graph = capture(lambda: run_round(stack, bn))
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    plane_bytes = stack.plane_bytes_per_round()
+    value = plane_bytes / (ms_per_step * 1e-3) / 1e9
+    log("timed %d rounds: %.3f ms/round wall, %.3f ms/round events" % (args.steps, ms_per_step, ev_ms))
+
+    roofline = None
+    if args.kernel_timing:
+        t_gemv = gemv_kernel_timing(stack, bn, min(args.steps, 10))
+        per_launch_bytes = stack.gemv_algorithmic_bytes_per_round() / stack.gemv_launches_per_round()
+        achieved = per_launch_bytes / t_gemv / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "gemv_planes_kernel (draft M=1 and target M=4 instantiations)",
+                    "avg_launch_us": round(t_gemv * 1e6, 3),
+                    "algorithmic_bytes_per_launch": int(per_launch_bytes)}
+        log("GEMV: %.3f us per launch (events), %.1f GB/s algorithmic" % (t_gemv * 1e6, achieved))
+
+    cpu = None
+    if args.cpu_baseline:
+        cpu = cpu_baseline(stack, args.cpu_seconds)
+        log("cpu oracle: %s GB/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    out = {
+        "metric": "nested W4/W8 linear: plane GB/s (% HBM peak), draft M=1 & verify M=4",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3-8B linear stack (%d layers x qkv/o_proj/gate_up/down), one speculative "
+                               "round: %d draft passes M=1 (hi plane) + 1 verify pass M=%d (hi+lo planes), "
+                               "act quant + nested linear per linear" % (args.layers, GAMMA, GAMMA + 1),
+                   "layers": args.layers, "gamma": GAMMA, "plane_bytes_per_round": plane_bytes,
+                   "launches_per_round": 2 * stack.gemv_launches_per_round(), "replay": "hip_graph"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -30,7 +30,8 @@
  *                            K is not a positive multiple of 128, or
  *                            act_group is neither 0 nor 128;
  *       BITNEST_EALIGN       a tensor pointer is not 16-byte aligned;
- *       BITNEST_EUNSUPPORTED M > BITNEST_MAX_M or K > BITNEST_MAX_K;
+ *       BITNEST_EUNSUPPORTED M > BITNEST_MAX_M, K > BITNEST_MAX_K, or one
+ *                            plane larger than BITNEST_MAX_PLANE_BYTES;
  *       BITNEST_EHIP         the HIP runtime reported an error while
  *                            launching (an error left pending on the calling
  *                            thread by an earlier HIP call is reported too).
@@ -53,6 +54,7 @@ extern "C" {
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
+#define BITNEST_MAX_PLANE_BYTES 2147483647LL  /* largest N * K / 2 (bytes of one plane) */
 
 typedef enum bitnest_status {
     BITNEST_OK = 0,

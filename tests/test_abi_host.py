@@ -117,6 +117,7 @@ def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     (lambda: _t(A, B, 128, C, F, D, E, 1, 8, 100), bn.EINVAL),
     (lambda: _t(A, B, 0, C, F, D, E, 40, 8, 128), bn.EUNSUPPORTED),
     (lambda: _t(A, B, 0, C, F, D, E, 0, 8, 128), bn.OK),
+    (lambda: _t(A, B, 0, C, F, D, E, 1, 300000, 16384), bn.EUNSUPPORTED),   # plane > 2 GiB
     # partials
     (lambda: _p(NUL, B, C, D, E, F, 1, 8, 128), bn.EINVAL),
     (lambda: _p(A, NUL, C, D, E, F, 1, 8, 128), bn.EINVAL),

@@ -47,6 +47,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bitnest_status check_sizes(int M, int N, int K) {
     if (M < 0 || N < 0 || K <= 0 || K % kGroup != 0) return BITNEST_EINVAL;
     if (M > BITNEST_MAX_M || K > BITNEST_MAX_K) return BITNEST_EUNSUPPORTED;
+    // plane offsets are 32-bit in the kernels
+    if (static_cast<long long>(N) * (K / 2) > static_cast<long long>(BITNEST_MAX_PLANE_BYTES))
+        return BITNEST_EUNSUPPORTED;
     return BITNEST_OK;
 }
 

@@ -26,6 +26,8 @@ enum : int {
     kDppQuadSwap2 = 0x4E,   // quad_perm [2,3,0,1]
     kDppRowRor4 = 0x124,    // rotate right by 4 within each row of 16 lanes
     kDppRowRor8 = 0x128,    // rotate right by 8 within each row of 16 lanes
+    kDppRowBcast15 = 0x142, // lane 15 of each row to the whole next row
+    kDppRowBcast31 = 0x143, // lane 31 to rows 2 and 3
 };
 
 template <int kCtrl>
@@ -37,6 +39,14 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                   kCtrl, 0xF, 0xF, false));
+}
+
+// DPP move with a row mask: rows outside the mask keep their old value and
+// receive 0 to add (the old operand is 0 and bound_ctrl is off).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f32_masked(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                                  kRowMask, 0xF, false));
 }
 
 // Exact integer sum over the 4 lanes of a quad; every lane of the quad gets it.

@@ -43,33 +43,35 @@
 namespace bitnest {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr unsigned kLowNibbles = 0x0F0F0F0Fu;
+constexpr unsigned kHighNibbles = 0xF0F0F0F0u;
 
 // v_perm_b32 selectors: bytes {0,2} of lo and {0,2} of hi (even columns),
 // and bytes {1,3}, {1,3} (odd columns).
 constexpr unsigned kSelEven = 0x06040200u;
 constexpr unsigned kSelOdd = 0x07050301u;
 
-// Unpacked nibbles of one 16-byte slot: e[d] / o[d] are the even / odd
-// columns of weight dword d, one unsigned nibble per byte.
-struct Nibbles {
+// Signed operands of one 16-byte plane slot (32 columns). A nibble u holds
+// the code u - 8; xor 0x8 turns it into the 4-bit two's complement of u - 8,
+// and placing that in the high half of a byte gives the int8 value
+// 16 * (u - 8). e[d] / o[d] hold the even / odd columns of weight dword d.
+struct Signed16 {
     unsigned e[4], o[4];
 };
 
-__device__ __forceinline__ Nibbles unpack(const u32x4 w) {
-    Nibbles n;
-    n.e[0] = w.x & kLowNibbles; n.o[0] = (w.x >> 4) & kLowNibbles;
-    n.e[1] = w.y & kLowNibbles; n.o[1] = (w.y >> 4) & kLowNibbles;
-    n.e[2] = w.z & kLowNibbles; n.o[2] = (w.z >> 4) & kLowNibbles;
-    n.e[3] = w.w & kLowNibbles; n.o[3] = (w.w >> 4) & kLowNibbles;
+__device__ __forceinline__ Signed16 to_signed16(const u32x4 w) {
+    Signed16 n;
+    const unsigned x0 = w.x ^ 0x88888888u, x1 = w.y ^ 0x88888888u;
+    const unsigned x2 = w.z ^ 0x88888888u, x3 = w.w ^ 0x88888888u;
+    n.e[0] = (x0 << 4) & kHighNibbles; n.o[0] = x0 & kHighNibbles;
+    n.e[1] = (x1 << 4) & kHighNibbles; n.o[1] = x1 & kHighNibbles;
+    n.e[2] = (x2 << 4) & kHighNibbles; n.o[2] = x2 & kHighNibbles;
+    n.e[3] = (x3 << 4) & kHighNibbles; n.o[3] = x3 & kHighNibbles;
     return n;
 }
 
-// Sum over the slot's 32 columns of q * u (u unsigned), with the activation
-// halves a0 = [e0 o0 e1 o1], a1 = [e2 o2 e3 o3] as staged in LDS.
-__device__ __forceinline__ int dot_slot(const Nibbles &n, const u32x4 a0, const u32x4 a1) {
+// 16 * sum over the slot's 32 columns of q * (u - 8), exact, with the
+// activation halves a0 = [e0 o0 e1 o1], a1 = [e2 o2 e3 o3] as staged in LDS.
+__device__ __forceinline__ int dot_slot16(const Signed16 &n, const u32x4 a0, const u32x4 a1) {
     int acc = 0;
     acc = sdot4(a0.x, n.e[0], acc);
     acc = sdot4(a0.y, n.o[0], acc);
@@ -84,174 +86,269 @@ __device__ __forceinline__ int dot_slot(const Nibbles &n, const u32x4 a0, const 
 
 template <int M>
 struct GemvLds {
-    static constexpr int kMP = (M + 3) & ~3;   // tokens padded to 4 in the per-group tables
+    static constexpr int kMP = (M + 3) & ~3;   // tokens padded to 4 in the grouped-scale table
     static size_t bytes(int K, bool grouped_act) {
         const size_t G = K / kGroup;
-        return static_cast<size_t>(M) * K + G * kMP * sizeof(int) +
-               (grouped_act ? G * kMP * sizeof(float) : 0);
+        return static_cast<size_t>(M) * K + (grouped_act ? G * kMP * sizeof(float) : 0);
     }
 };
 
+// Buffer descriptor over [p, p + bytes): loads beyond it return 0 (gfx9 raw
+// buffer, dword 3 = 0x00020000).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+constexpr int kAuxStream = 2;   // non-temporal: plane bytes are read once
+
+// Sum over the 16 quads of a wave of a value that is uniform within each
+// quad; the total lands in lane 63. Fixed association order.
+__device__ __forceinline__ float sum_quads_to_lane63(float v) {
+    v += dpp_f32<kDppRowRor4>(v);
+    v += dpp_f32<kDppRowRor8>(v);
+    v += dpp_f32_masked<kDppRowBcast15, 0xA>(v);
+    v += dpp_f32_masked<kDppRowBcast31, 0xC>(v);
+    return v;
+}
+
+// Permute one 16-column code block into its LDS place: columns 16 j .. 16 j + 15
+// of a token are half (j & 1) of slot (j >> 1), split into even and odd columns.
+__device__ __forceinline__ void stage_block(unsigned char *act_tok, int j, int row_bytes, const u32x4 v) {
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(v.y, v.x, kSelEven);
+    o.y = __builtin_amdgcn_perm(v.y, v.x, kSelOdd);
+    o.z = __builtin_amdgcn_perm(v.w, v.z, kSelEven);
+    o.w = __builtin_amdgcn_perm(v.w, v.z, kSelOdd);
+    *reinterpret_cast<u32x4 *>(act_tok + (j & 1) * row_bytes + (j >> 1) * 16) = o;
+}
+
+// One item = one 1 KiB chunk of one row, per plane: lane l holds 16 bytes,
+// plus the fp16 bits of its group's scale (converted when consumed, so that
+// no load result is needed before the next loads are issued).
+template <int PLANES>
+struct Item {
+    u32x4 h, l;
+    unsigned sbits;
+};
+
 // PLANES: 1 draft (hi), 2 target (hi + lo). GA: per-128-group activation
-// scales. EXPORT: write the integer partials instead of y. CB: chunk slots
-// unrolled per row (a row has C = ceil(K / 2048) chunks, C <= CB).
-template <int PLANES, int M, bool GA, bool EXPORT, int CB>
-__global__ __launch_bounds__(kThreads) void gemv_planes_kernel(const LinearArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
+// scales. EXPORT: write the integer partials instead of y. D: items in flight
+// per wave. WAVES: waves per workgroup.
+//
+// A row of K columns is C = ceil(K / 2048) chunks; the (row, chunk) items of
+// the whole call are split into contiguous runs, one per wave, and each wave
+// streams its run with D items in flight: the loads of item i + D are issued
+// as soon as item i has been consumed. Item addresses are wave-uniform
+// (scalar registers) plus a fixed lane offset, so address arithmetic stays
+// off the vector ALU; loads past the end of a plane return 0. The workgroup
+// stages the codes once into LDS while its first D items are in flight.
+template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArgs a) {
+    constexpr int kThreads = 64 * WAVES;
+    constexpr int kPB = (kMaxK / 16 + kThreads - 1) / kThreads;   // code blocks per thread and token
     constexpr int kMP = GemvLds<M>::kMP;
+    extern __shared__ __align__(16) unsigned char smem[];
     const int K = a.K;
     const int N = a.N;
     const int G = K >> 7;
     const int slots = K >> 5;       // 16-byte slots per plane row
     const int row_bytes = K >> 1;   // bytes per plane row
+    const int C = (slots + 63) >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // draft: (16 P_hi) * scale / 16; target: 16 (16 P_hi + P_lo) * scale / 256
+    const float fscale = PLANES == 2 ? 0.00390625f : 0.0625f;
 
-    unsigned char *act = smem;                                       // [M][2][slots][16]
-    int *sumq = reinterpret_cast<int *>(smem + static_cast<size_t>(M) * K);   // [G][kMP]
-    float *sact = reinterpret_cast<float *>(sumq + G * kMP);        // [G][kMP] (GA)
+    const unsigned plane_bytes = static_cast<unsigned>(N) * static_cast<unsigned>(row_bytes);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hi, plane_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(PLANES == 2 ? a.lo : a.hi, plane_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale, static_cast<unsigned>(N) * G * 2u);
+    const int voff_plane = lane * 16;          // lane's 16 bytes within a chunk
+    const int voff_scale = (lane >> 2) * 2;    // its group's scale within the chunk's 16 groups
 
-    // ---- stage the codes, permuted: 16-column block j of token m is half
-    // (j & 1) of slot (j >> 1).
-    const int nb16 = K >> 4;
-    for (int i = threadIdx.x; i < M * nb16; i += kThreads) {
-        const int m = i / nb16;
-        const int j = i - m * nb16;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.xq + static_cast<size_t>(m) * K + 16 * j);
-        u32x4 o;
-        o.x = __builtin_amdgcn_perm(v.y, v.x, kSelEven);
-        o.y = __builtin_amdgcn_perm(v.y, v.x, kSelOdd);
-        o.z = __builtin_amdgcn_perm(v.w, v.z, kSelEven);
-        o.w = __builtin_amdgcn_perm(v.w, v.z, kSelOdd);
-        *reinterpret_cast<u32x4 *>(act + static_cast<size_t>(m) * K + (j & 1) * row_bytes +
-                                   (j >> 1) * 16) = o;
-    }
-    // ---- per (group, token) code sums and grouped activation scales
-    for (int i = threadIdx.x; i < G * kMP; i += kThreads) {
-        const int g = i / kMP;
-        const int m = i - g * kMP;
-        int acc = 0;
-        float sv = 0.0f;
-        if (m < M) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(a.xq + static_cast<size_t>(m) * K + g * kGroup);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const u32x4 v = p[t];
-                acc = sdot4(v.x, 0x01010101u, acc);
-                acc = sdot4(v.y, 0x01010101u, acc);
-                acc = sdot4(v.z, 0x01010101u, acc);
-                acc = sdot4(v.w, 0x01010101u, acc);
-            }
-            if (GA) sv = a.xs[static_cast<size_t>(m) * G + g];
+    // this wave's rows [row_begin, row_end): whole rows, so that exactly one
+    // wave owns each output; its items are the C chunks of each row, in order
+    const long long gw = static_cast<long long>(blockIdx.x) * WAVES + wave;
+    const long long W = static_cast<long long>(gridDim.x) * WAVES;
+    const int row_begin = static_cast<int>(N * gw / W);
+    const int row_end = static_cast<int>(N * (gw + 1) / W);
+    const int n_items = (row_end - row_begin) * C;
+
+    // Issue the loads of the next item in order. Items past this wave's run
+    // are given an offset beyond the plane, which the buffer unit answers
+    // with zeros and no memory traffic; so every issue is unconditional and
+    // the number of loads in flight is the same on every path.
+    const int oob = static_cast<int>(plane_bytes);
+    int irow = row_begin, ichunk = 0, iseq = 0;    // next item to issue (wave-uniform)
+    auto issue = [&](Item<PLANES> &x) {
+        const bool live = iseq < n_items;
+        const int soff = live ? irow * row_bytes + ichunk * 1024 : oob;
+        const int soff_s = live ? (irow * G + ichunk * 16) * 2 : static_cast<int>(N * G * 2);
+        x.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, voff_plane, soff, kAuxStream));
+        if (PLANES == 2)
+            x.l = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, voff_plane, soff, kAuxStream));
+        if (!EXPORT) x.sbits = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_scale, soff_s, 0);
+        ++iseq;
+        if (++ichunk == C) {
+            ichunk = 0;
+            ++irow;
         }
-        sumq[i] = acc;
-        if (GA) sact[i] = sv;
+    };
+
+    // 1) codes (kPB 16-column blocks per thread and token cover K), the
+    //    activation scales, then the first D items
+    const int nb16 = K >> 4;
+    u32x4 pre[M][kPB];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int t = 0; t < kPB; ++t) {
+            const int j = threadIdx.x + t * kThreads;
+            if (j < nb16) pre[m][t] = *reinterpret_cast<const u32x4 *>(a.xq + static_cast<size_t>(m) * K + j * 16);
+        }
+    float tok_scale[M];
+    if (!GA && !EXPORT) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) tok_scale[m] = a.xs[m];
+    }
+    constexpr int kGAPer = (kGroup * 8 + kThreads - 1) / kThreads;
+    float gscale[kGAPer];
+    if (GA) {
+#pragma unroll
+        for (int t = 0; t < kGAPer; ++t) {
+            const int i = threadIdx.x + t * kThreads;     // flat [G][kMP]
+            gscale[t] = 0.0f;
+            if (i < G * kMP) {
+                const int g = i / kMP, m = i - (i / kMP) * kMP;
+                if (m < M) gscale[t] = a.xs[static_cast<size_t>(m) * G + g];
+            }
+        }
+    }
+    Item<PLANES> ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(ring[d]);
+
+    // 2) stage the codes into LDS while the ring is in flight
+    unsigned char *act = smem;                                                    // [M][2][slots][16]
+    float *sact = reinterpret_cast<float *>(smem + static_cast<size_t>(M) * K);   // [G][kMP] (GA)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int t = 0; t < kPB; ++t) {
+            const int j = threadIdx.x + t * kThreads;
+            if (j < nb16) stage_block(act + static_cast<size_t>(m) * K, j, row_bytes, pre[m][t]);
+        }
+    if (GA) {
+#pragma unroll
+        for (int t = 0; t < kGAPer; ++t) {
+            const int i = threadIdx.x + t * kThreads;
+            if (i < G * kMP) sact[i] = gscale[t];
+        }
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int C = (slots + 63) >> 6;
-    const float fscale = PLANES == 2 ? 0.0625f : 1.0f;    // scale / 16 for the target
-    constexpr int kOff = PLANES == 2 ? 136 : 8;             // 16*8 + 8, or 8
     const u32x4 *act4 = reinterpret_cast<const u32x4 *>(act);
     const int tok4 = K >> 4;     // u32x4 per token
     const int half4 = K >> 5;    // u32x4 per half (= slots)
 
-    for (int row = blockIdx.x * kWaves + wave; row < N; row += gridDim.x * kWaves) {
-        const uint8_t *hrow = a.hi + static_cast<size_t>(row) * row_bytes;
-        const uint8_t *lrow = PLANES == 2 ? a.lo + static_cast<size_t>(row) * row_bytes : nullptr;
-        const uint16_t *srow = a.scale + static_cast<size_t>(row) * G;
-
-        u32x4 wh[CB], wl[CB];
-        float sc[CB];
+    float acc[M];
 #pragma unroll
-        for (int b = 0; b < CB; ++b) {
-            const int s = b * 64 + lane;
-            wh[b] = u32x4{0u, 0u, 0u, 0u};
-            wl[b] = u32x4{0u, 0u, 0u, 0u};
-            sc[b] = 0.0f;
-            if (b < C && s < slots) {
-                wh[b] = load_stream16(hrow + s * 16);
-                if (PLANES == 2) wl[b] = load_stream16(lrow + s * 16);
-                if (!EXPORT) sc[b] = half_bits_to_float(srow[s >> 2]) * fscale;
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+    // consume one item: its group partials, accumulated into the row sums;
+    // the last chunk of a row ends the row.
+    int crow = row_begin, cchunk = 0;          // next item to consume (wave-uniform)
+    auto consume = [&](const Item<PLANES> &x) {
+        const int row = crow;
+        const int s = cchunk * 64 + lane;
+        const bool valid = s < slots;            // uniform within each quad
+        const int ss = valid ? s : 0;
+        const int g = ss >> 2;
+        const float sc = half_bits_to_float(static_cast<uint16_t>(x.sbits)) * fscale;
+        const Signed16 nh = to_signed16(x.h);
+        Signed16 nl;
+        if (PLANES == 2) nl = to_signed16(x.l);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const u32x4 a0 = act4[m * tok4 + ss];
+            const u32x4 a1 = act4[m * tok4 + half4 + ss];
+            if (EXPORT) {
+                const int ph = quad_sum_i32(dot_slot16(nh, a0, a1)) >> 4;
+                int pl = 0;
+                if (PLANES == 2) pl = quad_sum_i32(dot_slot16(nl, a0, a1)) >> 4;
+                if (valid && (lane & 3) == 0) {
+                    const size_t o = (static_cast<size_t>(m) * N + row) * G + g;
+                    a.p_hi[o] = ph;
+                    if (PLANES == 2) {
+                        a.p_lo[o] = pl;
+                        a.p8[o] = 16 * ph + pl;
+                    }
+                }
+            } else {
+                // draft: 16 P_hi; target: 16 (16 P_hi) + 16 P_lo = 16 P8
+                int p = dot_slot16(nh, a0, a1);
+                if (PLANES == 2) p = 16 * p + dot_slot16(nl, a0, a1);
+                p = quad_sum_i32(p);
+                const float w = GA ? sc * sact[g * kMP + m] : sc;
+                acc[m] += valid ? static_cast<float>(p) * w : 0.0f;
             }
         }
-
-        float acc[M];
+        if (++cchunk == C) {                     // row complete (uniform)
+            cchunk = 0;
+            ++crow;
+            if (!EXPORT) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-
-#pragma unroll
-        for (int b = 0; b < CB; ++b) {
-            if (b >= C) break;                       // uniform across the wave
-            const int s = b * 64 + lane;
-            const bool valid = s < slots;            // uniform within each quad
-            const int ss = valid ? s : 0;
-            const int g = ss >> 2;
-            const Nibbles nh = unpack(wh[b]);
-            Nibbles nl;
-            if (PLANES == 2) nl = unpack(wl[b]);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const u32x4 a0 = act4[m * tok4 + ss];
-                const u32x4 a1 = act4[m * tok4 + half4 + ss];
-                const int sq = sumq[g * kMP + m];
-                if (EXPORT) {
-                    const int ph = quad_sum_i32(dot_slot(nh, a0, a1)) - 8 * sq;
-                    int pl = 0;
-                    if (PLANES == 2) pl = quad_sum_i32(dot_slot(nl, a0, a1)) - 8 * sq;
-                    if (valid && (lane & 3) == 0) {
-                        const size_t o = (static_cast<size_t>(m) * N + row) * G + g;
-                        a.p_hi[o] = ph;
-                        if (PLANES == 2) {
-                            a.p_lo[o] = pl;
-                            a.p8[o] = 16 * ph + pl;
-                        }
-                    }
-                } else {
-                    int p = dot_slot(nh, a0, a1);
-                    if (PLANES == 2) p = 16 * p + dot_slot(nl, a0, a1);
-                    p = quad_sum_i32(p) - kOff * sq;
-                    const float w = GA ? sc[b] * sact[g * kMP + m] : sc[b];
-                    const float f = static_cast<float>(p) * w;
-                    acc[m] += valid ? f : 0.0f;
+                for (int m = 0; m < M; ++m) {
+                    const float v = sum_quads_to_lane63(acc[m]);
+                    if (lane == 63) a.y[static_cast<size_t>(m) * N + row] = GA ? v : v * tok_scale[m];
+                    acc[m] = 0.0f;
                 }
             }
         }
-        if (!EXPORT) {
+    };
+
+    // steady state: consume item i, then issue item i + D into its slot
+    for (int base = 0; base < n_items; base += D) {
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float v = sum_over_quads_f32(acc[m]);
-                if (lane == 0) a.y[static_cast<size_t>(m) * N + row] = GA ? v : v * a.xs[m];
-            }
+        for (int d = 0; d < D; ++d) {
+            if (base + d < n_items) consume(ring[d]);    // uniform
+            issue(ring[d]);
         }
     }
 }
 
 typedef void (*GemvKernel)(const LinearArgs);
 
-template <int PLANES, int M, int CB>
-GemvKernel pick_mode(bool grouped, bool exporting) {
-    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, CB>;
-    return grouped ? gemv_planes_kernel<PLANES, M, true, false, CB>
-                   : gemv_planes_kernel<PLANES, M, false, false, CB>;
+// Launch shape: waves per workgroup and items (1 KiB chunks per plane) in
+// flight per wave.
+constexpr int kGemvWaves = 8;
+// (Measured on MI355X over the Llama-3-8B shapes: 2-4 items per wave with
+// 8-wave workgroups beat deeper rings, which cost occupancy.)
+template <int PLANES, int M>
+constexpr int items_in_flight() {
+    return PLANES == 1 ? 4 : 2;
 }
 
 template <int PLANES, int M>
-GemvKernel pick_cb(int C, bool grouped, bool exporting) {
-    return C <= 2 ? pick_mode<PLANES, M, 2>(grouped, exporting)
-                  : pick_mode<PLANES, M, 8>(grouped, exporting);
+GemvKernel pick_mode(bool grouped, bool exporting) {
+    constexpr int D = items_in_flight<PLANES, M>();
+    constexpr int W = kGemvWaves;
+    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W>;
+    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W>
+                   : gemv_planes_kernel<PLANES, M, false, false, D, W>;
 }
 
 template <int PLANES>
-GemvKernel pick_m(int M, int C, bool grouped, bool exporting) {
+GemvKernel pick_m(int M, bool grouped, bool exporting) {
     switch (M) {
-        case 1: return pick_cb<PLANES, 1>(C, grouped, exporting);
-        case 2: return pick_cb<PLANES, 2>(C, grouped, exporting);
-        case 3: return pick_cb<PLANES, 3>(C, grouped, exporting);
-        case 4: return pick_cb<PLANES, 4>(C, grouped, exporting);
-        case 5: return pick_cb<PLANES, 5>(C, grouped, exporting);
-        case 6: return pick_cb<PLANES, 6>(C, grouped, exporting);
-        case 7: return pick_cb<PLANES, 7>(C, grouped, exporting);
+        case 1: return pick_mode<PLANES, 1>(grouped, exporting);
+        case 2: return pick_mode<PLANES, 2>(grouped, exporting);
+        case 3: return pick_mode<PLANES, 3>(grouped, exporting);
+        case 4: return pick_mode<PLANES, 4>(grouped, exporting);
+        case 5: return pick_mode<PLANES, 5>(grouped, exporting);
+        case 6: return pick_mode<PLANES, 6>(grouped, exporting);
+        case 7: return pick_mode<PLANES, 7>(grouped, exporting);
         default: return nullptr;
     }
 }
@@ -272,13 +369,11 @@ size_t gemv_lds_bytes(int M, int K, bool grouped) {
 }  // namespace
 
 hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream) {
-    const int slots = a.K / 32;
-    const int C = (slots + 63) / 64;
     const bool target = a.lo != nullptr;
     const bool grouped = a.act_group == kGroup && !export_partials;
-    GemvKernel k = target ? pick_m<2>(a.M, C, grouped, export_partials)
-                          : pick_m<1>(a.M, C, grouped, export_partials);
-    if (!k || C > 8) return hipErrorInvalidValue;
+    GemvKernel k = target ? pick_m<2>(a.M, grouped, export_partials)
+                          : pick_m<1>(a.M, grouped, export_partials);
+    if (!k) return hipErrorInvalidValue;
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
@@ -289,9 +384,17 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    const int rows_blocks = (a.N + kWaves - 1) / kWaves;
-    const int blocks = rows_blocks < dev.cus * 2 ? rows_blocks : dev.cus * 2;
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(kThreads), lds, stream, a);
+    // One resident wave of workgroups (as many as the occupancy of this
+    // instantiation allows), never more workgroups than rows / waves.
+    int occ = 0;
+    const int threads = 64 * kGemvWaves;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(k), threads, lds);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    const int rows_blocks = (a.N + kGemvWaves - 1) / kGemvWaves;
+    const int full = dev.cus * occ;
+    const int blocks = rows_blocks < full ? rows_blocks : full;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), lds, stream, a);
     return hipGetLastError();
 }
 

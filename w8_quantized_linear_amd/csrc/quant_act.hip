@@ -14,7 +14,8 @@
 namespace bitnest {
 namespace {
 
-constexpr int kQuantThreads = 256;
+constexpr int kQuantThreads = 256;     // grouped kernel
+constexpr int kTokenThreads = 1024;    // per-token kernel
 
 __device__ __forceinline__ int code_of(float x, float s) {
     if (s == 0.0f) return 0;
@@ -34,34 +35,40 @@ __device__ __forceinline__ float absmax4(const float4 &v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
-// One token per workgroup; each thread keeps up to NV float4 of the row.
+// One token per workgroup of 1024 threads; each thread keeps up to NV float4
+// of the row in registers. All loads are issued unconditionally (clamped
+// index) before any use, so the row costs one memory round trip.
 template <int NV>
-__global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(
+__global__ __launch_bounds__(kTokenThreads) void quant_token_kernel(
     const float *__restrict__ x, int K, int8_t *__restrict__ q, float *__restrict__ s) {
-    __shared__ float part[kQuantThreads / 64];
+    __shared__ float part[kTokenThreads / 64];
     const int m = blockIdx.x;
     const float4 *xr = reinterpret_cast<const float4 *>(x + static_cast<size_t>(m) * K);
     const int n4 = K >> 2;
     float4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = threadIdx.x + i * kTokenThreads;
+        v[i] = xr[idx < n4 ? idx : 0];
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int idx = threadIdx.x + i * kQuantThreads;
-        if (idx < n4) {
-            v[i] = xr[idx];
-            amax = fmaxf(amax, absmax4(v[i]));
-        }
+        const int idx = threadIdx.x + i * kTokenThreads;
+        if (idx < n4) amax = fmaxf(amax, absmax4(v[i]));
     }
     amax = wave_max_f32(amax);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    amax = part[0];
+#pragma unroll
+    for (int w = 1; w < kTokenThreads / 64; ++w) amax = fmaxf(amax, part[w]);
     const float sc = amax / 127.0f;
     if (threadIdx.x == 0) s[m] = sc;
     unsigned *qr = reinterpret_cast<unsigned *>(q + static_cast<size_t>(m) * K);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int idx = threadIdx.x + i * kQuantThreads;
+        const int idx = threadIdx.x + i * kTokenThreads;
         if (idx < n4) qr[idx] = pack4(v[i], sc);
     }
 }
@@ -97,17 +104,13 @@ hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t 
         hipLaunchKernelGGL(quant_group_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x,
                            total, xq, xs);
     } else {
-        const int nv = (K / 4 + kQuantThreads - 1) / kQuantThreads;   // float4 per thread
+        const int nv = (K / 4 + kTokenThreads - 1) / kTokenThreads;   // float4 per thread
         if (nv <= 1)
-            hipLaunchKernelGGL(quant_token_kernel<1>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+            hipLaunchKernelGGL(quant_token_kernel<1>, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
         else if (nv <= 2)
-            hipLaunchKernelGGL(quant_token_kernel<2>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+            hipLaunchKernelGGL(quant_token_kernel<2>, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
         else if (nv <= 4)
-            hipLaunchKernelGGL(quant_token_kernel<4>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
-        else if (nv <= 8)
-            hipLaunchKernelGGL(quant_token_kernel<8>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
-        else if (nv <= 16)
-            hipLaunchKernelGGL(quant_token_kernel<16>, dim3(M), dim3(kQuantThreads), 0, stream, x, K, xq, xs);
+            hipLaunchKernelGGL(quant_token_kernel<4>, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
         else
             return hipErrorInvalidValue;   // K > kMaxK: rejected by the ABI before this point
     }

@@ -15,7 +15,8 @@ weight package, which is not available):
 * activations: fp32 N(0, 1); in the layer workloads round(0.005 K) channels,
   the same for every token of a call, are multiplied by 20 (outliers).
 
-Every tensor has its own seed, derived from (seed, layer, linear, tensor) by
+Every tensor has its own seed, derived from (seed, layer, linear, tensor,
+decoding step) by
 numpy's SeedSequence, and is drawn with torch's generator on the device the
 tensor is made on (CPU and GPU generators give different, equally seeded,
 streams).
@@ -43,8 +44,8 @@ LLAMA3_8B_LAYERS = 32
 _TENSOR_IDS = {"hi": 0, "lo": 1, "scale": 2, "x": 3, "outliers": 4}
 
 
-def derive_seed(seed: int, layer: int, linear: int, tensor: str) -> int:
-    ss = np.random.SeedSequence([int(seed), int(layer), int(linear), _TENSOR_IDS[tensor]])
+def derive_seed(seed: int, layer: int, linear: int, tensor: str, step: int = 0) -> int:
+    ss = np.random.SeedSequence([int(seed), int(layer), int(linear), _TENSOR_IDS[tensor], int(step)])
     return int(ss.generate_state(1, np.uint64)[0] >> np.uint64(1))
 
 
@@ -114,11 +115,12 @@ def n_outliers(K: int) -> int:
 
 
 def make_activations(M: int, K: int, seed: int = 0, layer: int = 0, linear: int = 0,
-                     outliers: bool = True, device="cpu") -> torch.Tensor:
-    g = _gen(device, derive_seed(seed, layer, linear, "x"))
+                     outliers: bool = True, device="cpu", step: int = 0) -> torch.Tensor:
+    """fp32 [M, K]; `step` tells apart the inputs of successive decoding steps."""
+    g = _gen(device, derive_seed(seed, layer, linear, "x", step))
     x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
     if outliers:
-        go = _gen("cpu", derive_seed(seed, layer, linear, "outliers"))
+        go = _gen("cpu", derive_seed(seed, layer, linear, "outliers", step))
         idx = torch.randperm(K, generator=go)[: n_outliers(K)].to(device)
         x[:, idx] *= 20.0
     return x
