@@ -47,6 +47,8 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU work for the oracle baseline sample")
     p.add_argument("--no-kernel-timing", dest="kernel_timing", action="store_false", default=True)
+    p.add_argument("--unfused", action="store_true",
+                   help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
     return p.parse_args(argv)
 
@@ -89,23 +91,36 @@ class Stack:
         return self.layers * per_layer * (GAMMA * 1 + 2)
 
     def gemv_algorithmic_bytes_per_round(self):
-        """Bytes every GEMV launch of a round must move at least (planes, scales,
-        codes, activation scales, outputs), summed over the round."""
+        """Bytes the round's linear launches must move at least, summed: plane
+        bytes, fp16 scales, the activation input (fp32 x for a fused launch,
+        int8 codes otherwise), the codes and scales a fused launch writes,
+        and the fp32 outputs."""
+        import w8_quantized_linear_amd as bn
         tot = 0
         for M, planes, passes in ((1, 1, GAMMA), (GAMMA + 1, 2, 1)):
             for (_, N, K, g) in self.linears:
                 S = 1 if g == 0 else K // 128
-                tot += passes * self.layers * (planes * N * K // 2 + N * (K // 128) * 2 + M * K + M * S * 4 + M * N * 4)
+                b = planes * N * K // 2 + N * (K // 128) * 2 + M * N * 4
+                if bn.fused_in_one_launch(M, K):
+                    b += 4 * M * K + M * K + 4 * M * S
+                else:
+                    b += M * K + 4 * M * S
+                tot += passes * self.layers * b
         return tot
 
     def gemv_launches_per_round(self):
         return (GAMMA + 1) * self.layers * len(self.linears)
 
 
-def run_round(stack, bn, quant=True):
+def run_round(stack, bn, mode="fused"):
     """One speculative round: 3 draft passes at M = 1, one verify pass at M = 4.
-    quant=False launches only the GEMVs (on the codes already in the buffers),
-    which is how the GEMV launches are timed on their own."""
+
+    mode "fused": each linear quantises its fp32 input and runs the nested
+    linear in one call (bitnest_quant_linear_*); "unfused": bitnest_quant_act
+    then bitnest_linear_*; "linear_only": the linear launches of the fused
+    round and nothing else (linears whose fused call is two launches run only
+    their linear, on the codes already in the buffers) - used to time the
+    dominant kernel on its own."""
     for p in range(GAMMA + 1):
         verify = p == GAMMA
         M = GAMMA + 1 if verify else 1
@@ -113,8 +128,15 @@ def run_round(stack, bn, quant=True):
             for i, (_, N, K, g) in enumerate(stack.linears):
                 xq, xs, y = stack.buf[(M, i)]
                 w = stack.w[l][i]
-                if quant:
-                    x = stack.x_verify[l][i] if verify else stack.x_draft[p][l][i]
+                x = stack.x_verify[l][i] if verify else stack.x_draft[p][l][i]
+                one = bn.fused_in_one_launch(M, K)
+                if mode == "fused" or (mode == "linear_only" and one):
+                    if verify:
+                        bn.bitnest_quant_linear_target(x, w.hi, w.lo, w.scale, g, y=y, xq=xq, xs=xs)
+                    else:
+                        bn.bitnest_quant_linear_draft(x, w.hi, w.scale, g, y=y, xq=xq, xs=xs)
+                    continue
+                if mode == "unfused":
                     bn.bitnest_quant_act(x, g, xq=xq, xs=xs)
                 if verify:
                     bn.bitnest_linear_target(xq, xs, w.hi, w.lo, w.scale, g, y=y)
@@ -138,14 +160,15 @@ def capture(fn):
 
 
 def gemv_kernel_timing(stack, bn, steps):
-    """Average GEMV launch duration: the round's 512 GEMV launches (same
-    shapes, weights and order, without the quantisation launches) replayed
+    """Average launch duration of the linear kernel: the round's 512 linear
+    launches (same shapes, weights and order as the timed round, without the
+    separate quantisation launches of the linears that need one) replayed
     back to back from a HIP graph, timed with HIP events on the stream they
-    run on, divided by the number of launches. The short gaps between
-    dispatches are included, so this slightly overstates the duration."""
+    run on, divided by the number of launches. Gaps between dispatches are
+    included, so this can only overstate the duration."""
     import torch
     n = stack.gemv_launches_per_round()
-    g = capture(lambda: run_round(stack, bn, quant=False))
+    g = capture(lambda: run_round(stack, bn, mode="linear_only"))
     g.replay()
     torch.cuda.synchronize()
     per = []
@@ -212,7 +235,8 @@ def main(argv=None):
     log("stack ready: %d layers, %.2f GB of planes per round, %.1f s"
         % (args.layers, stack.plane_bytes_per_round() / 1e9, time.perf_counter() - t0))
 
-    graph = capture(lambda: run_round(stack, bn))
+    fused = not args.unfused
+    graph = capture(lambda: run_round(stack, bn, mode="fused" if fused else "unfused"))
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -237,7 +261,8 @@ def main(argv=None):
         achieved = per_launch_bytes / t_gemv / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "gemv_planes_kernel (draft M=1 and target M=4 instantiations)",
+                    "kernel": "gemv_planes_kernel (draft M=1 and target M=4 instantiations, fused "
+                              "quantisation where the round uses it)",
                     "avg_launch_us": round(t_gemv * 1e6, 3),
                     "algorithmic_bytes_per_launch": int(per_launch_bytes)}
         log("GEMV: %.3f us per launch (events), %.1f GB/s algorithmic" % (t_gemv * 1e6, achieved))
@@ -264,7 +289,8 @@ def main(argv=None):
                                "round: %d draft passes M=1 (hi plane) + 1 verify pass M=%d (hi+lo planes), "
                                "act quant + nested linear per linear" % (args.layers, GAMMA, GAMMA + 1),
                    "layers": args.layers, "gamma": GAMMA, "plane_bytes_per_round": plane_bytes,
-                   "launches_per_round": 2 * stack.gemv_launches_per_round(), "replay": "hip_graph"},
+                   "quant": "fused into the linear launch" if fused else "separate launch",
+                   "replay": "hip_graph"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -122,7 +122,29 @@ bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_
                                      float *y, int M, int N, int K, void *stream);
 
 /*
- * The integer partials of the two calls above, from the same kernels' integer
+ * Activation quantisation fused with the draft linear: the same codes, scales
+ * and y, bit for bit, as bitnest_quant_act(x, M, K, act_group, xq, xs, stream)
+ * followed by bitnest_linear_draft(xq, xs, act_group, hi, scale, y, M, N, K,
+ * stream). For one token (M == 1) each workgroup quantises x itself and the
+ * whole linear is one launch; otherwise the call makes the two launches.
+ *   x    fp32 [M, K] input;  xq int8 [M, K], xs fp32 [M] or [M, K/128]:
+ *        outputs, as written by bitnest_quant_act (always required)
+ *   hi, scale, y as for bitnest_linear_draft (may be NULL when N == 0).
+ */
+bitnest_status bitnest_quant_linear_draft(const float *x, int act_group,
+                                          const uint8_t *hi, const uint16_t *scale,
+                                          float *y, int8_t *xq, float *xs,
+                                          int M, int N, int K, void *stream);
+
+/* The same for the target linear (bitnest_quant_act + bitnest_linear_target). */
+bitnest_status bitnest_quant_linear_target(const float *x, int act_group,
+                                           const uint8_t *hi, const uint8_t *lo,
+                                           const uint16_t *scale,
+                                           float *y, int8_t *xq, float *xs,
+                                           int M, int N, int K, void *stream);
+
+/*
+ * The integer partials of the draft and target calls above, from the same kernels' integer
  * loop (for checking; not a fast path).
  *   p_hi  int32 [M, N, K/128] <- P_hi (always written)
  *   p_lo  int32 [M, N, K/128] <- P_lo              (only if lo != NULL)

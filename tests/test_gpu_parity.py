@@ -290,3 +290,95 @@ def test_llama_layer_full_size(llama_layer, M, target):
             r = oracle.partials(q_ref, hi[:64], lo[:64])
             for a, b in zip(p, r):
                 assert np.array_equal(a.cpu().numpy(), b), name
+
+
+# --------------------------------------------------------------------------- fused quant + linear
+
+FUSED_SHAPES = [(256, 512), (37, 640), (70, 2176), (33, 14336), (129, 4096), (17, 16384)]
+
+
+@pytest.mark.parametrize("N,K", FUSED_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 8, 32])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_fused_quant_linear_equals_two_calls(M, N, K, act_group, target):
+    # One fused call must give the codes, scales and y of quant_act followed by
+    # the linear, bit for bit (one launch when M*K <= 16384, else two).
+    w, x = _problem(M, N, K, seed=9)
+    xd, hi, lo, sc = _dev(x), _dev(w.hi), _dev(w.lo), _dev(w.scale)
+    xq, xs = bn.bitnest_quant_act(xd, act_group)
+    if target:
+        y_ref = bn.bitnest_linear_target(xq, xs, hi, lo, sc, act_group)
+        y, fq, fs = bn.bitnest_quant_linear_target(xd, hi, lo, sc, act_group)
+    else:
+        y_ref = bn.bitnest_linear_draft(xq, xs, hi, sc, act_group)
+        y, fq, fs = bn.bitnest_quant_linear_draft(xd, hi, sc, act_group)
+    torch.cuda.synchronize()
+    assert torch.equal(fq, xq)
+    assert torch.equal(fs.view(torch.int32), xs.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(fq.cpu().numpy(), q)
+    hi_n, lo_n, sc_n = w.numpy()
+    _check_y(y, oracle.linear(q, s, hi_n, sc_n, lo_n if target else None, act_group), "fused")
+
+
+def test_fused_quant_linear_with_no_rows_still_quantises():
+    x = synth.make_activations(3, 512, seed=10)
+    xd = _dev(x)
+    hi0 = torch.zeros((0, 256), dtype=torch.uint8, device="cuda")
+    sc0 = torch.zeros((0, 4), dtype=torch.int16, device="cuda")
+    y, fq, fs = bn.bitnest_quant_linear_draft(xd, hi0, sc0)
+    torch.cuda.synchronize()
+    q, s = oracle.quant_act(x.numpy())
+    assert y.shape == (3, 0)
+    assert np.array_equal(fq.cpu().numpy(), q) and np.array_equal(fs.cpu().numpy(), s)
+
+
+def _near_tie_rows(K=512):
+    """Rows whose elements sit within a few ulps of (k + 1/2) * s, s = amax/127:
+    the places where a reciprocal-multiply rounds differently from x / s."""
+    rows = []
+    for amax in (139.7, 3.3, 5.7, 0.91, 77.77, 1234.5, 17.0, 101.3):
+        a = np.float32(amax)
+        s = a / np.float32(127)
+        vals = [a]
+        for k in range(0, 126):
+            x = np.float32((k + 0.5) * np.float64(s))
+            for _ in range(3):
+                x = np.nextafter(x, np.float32(-np.inf))
+            for _ in range(7):
+                vals.append(x if k % 2 else -x)
+                x = np.nextafter(x, np.float32(np.inf))
+        row = np.zeros(K * ((len(vals) + K - 1) // K), np.float32)
+        row[:len(vals)] = vals
+        rows.append(row)
+    width = max(len(r) for r in rows)
+    return np.stack([np.pad(r, (0, width - len(r))) for r in rows])
+
+
+def test_quant_near_ties_bit_exact():
+    x = _near_tie_rows()
+    q_ref, s_ref = oracle.quant_act(x)
+    xq, xs = bn.bitnest_quant_act(_dev(torch.from_numpy(x)))
+    torch.cuda.synchronize()
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    # the fused prologue, one token at a time (M * K within one launch)
+    for m in range(x.shape[0]):
+        xm = torch.from_numpy(x[m:m + 1].copy())
+        K = xm.shape[1]
+        w = synth.make_weights(16, K)
+        _, fq, fs = bn.bitnest_quant_linear_draft(_dev(xm), _dev(w.hi), _dev(w.scale))
+        torch.cuda.synchronize()
+        assert np.array_equal(fq.cpu().numpy()[0], q_ref[m])
+        assert fs.item() == s_ref[m]
+
+
+def test_quant_grouped_near_ties_bit_exact():
+    x = _near_tie_rows(K=128)[:, :1024]
+    q_ref, s_ref = oracle.quant_act(x, 128)
+    xq, xs = bn.bitnest_quant_act(_dev(torch.from_numpy(x)), 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)

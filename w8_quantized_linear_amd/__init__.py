@@ -19,6 +19,7 @@ __all__ = [
     "BitnestError", "GROUP", "MAX_M", "MAX_K", "library_path", "lib",
     "bitnest_abi_version", "bitnest_status_string", "bitnest_quant_act",
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
+    "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
 ]
 
 GROUP = 128
@@ -57,8 +58,10 @@ def lib() -> ctypes.CDLL:
         L.bitnest_linear_draft.argtypes = [P, P, I, P, P, P, I, I, I, P]
         L.bitnest_linear_target.argtypes = [P, P, I, P, P, P, P, I, I, I, P]
         L.bitnest_linear_partials.argtypes = [P, P, P, P, P, P, I, I, I, P]
+        L.bitnest_quant_linear_draft.argtypes = [P, I, P, P, P, P, P, I, I, I, P]
+        L.bitnest_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
-                  "bitnest_linear_partials"):
+                  "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -184,8 +187,66 @@ def bitnest_linear_partials(xq: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor
     return p_hi if lo is None else (p_hi, p_lo, p8)
 
 
+def _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, what):
+    _need(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    scale = _scale_tensor(scale)
+    _need(hi, "hi", torch.uint8)
+    if hi.dim() != 2 or hi.shape[1] * 2 != K:
+        raise ValueError("hi must be [N, K/2] with K=%d, got %s" % (K, tuple(hi.shape)))
+    N = hi.shape[0]
+    _need(scale, "scale", torch.int16, (N, K // GROUP))
+    if lo is not None:
+        _need(lo, "lo", torch.uint8, tuple(hi.shape))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,) if act_group == 0 else (M, K // GROUP), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (M, N))
+    _need(xq, "xq", torch.int8, (M, K))
+    _need(xs, "xs", torch.float32, (M,) if act_group == 0 else (M, K // GROUP))
+    if lo is None:
+        st = lib().bitnest_quant_linear_draft(_p(x), act_group, _p(hi), _p(scale), _p(y), _p(xq), _p(xs),
+                                              M, N, K, _stream(x))
+    else:
+        st = lib().bitnest_quant_linear_target(_p(x), act_group, _p(hi), _p(lo), _p(scale), _p(y), _p(xq),
+                                               _p(xs), M, N, K, _stream(x))
+    _call(st, what)
+    return y, xq, xs
+
+
+FUSED_MAX_MK = 16384
+
+
+def fused_in_one_launch(M: int, K: int) -> bool:
+    """Whether bitnest_quant_linear_* runs as a single kernel launch for this
+    shape (otherwise it is a quantisation launch followed by the linear); the
+    library's rule: one token and K <= 16384."""
+    return M == 1 and K <= FUSED_MAX_MK
+
+
+def bitnest_quant_linear_draft(x: torch.Tensor, hi: torch.Tensor, scale: torch.Tensor, act_group: int = 0,
+                               y: torch.Tensor | None = None, xq: torch.Tensor | None = None,
+                               xs: torch.Tensor | None = None):
+    """Quantise x and run the draft linear in one call: returns (y, xq, xs)."""
+    return _quant_linear(x, hi, None, scale, act_group, y, xq, xs, "bitnest_quant_linear_draft")
+
+
+def bitnest_quant_linear_target(x: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor, scale: torch.Tensor,
+                                act_group: int = 0, y: torch.Tensor | None = None,
+                                xq: torch.Tensor | None = None, xs: torch.Tensor | None = None):
+    """Quantise x and run the target linear in one call: returns (y, xq, xs)."""
+    return _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, "bitnest_quant_linear_target")
+
+
 # Short aliases
 quant_act = bitnest_quant_act
 linear_draft = bitnest_linear_draft
 linear_target = bitnest_linear_target
 linear_partials = bitnest_linear_partials
+quant_linear_draft = bitnest_quant_linear_draft
+quant_linear_target = bitnest_quant_linear_target

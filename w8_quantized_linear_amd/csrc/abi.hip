@@ -118,6 +118,49 @@ bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_
     return run_linear(a, false, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two fused calls: quantise, then the linear; one launch
+// when the fused GEMV takes the shape.
+bitnest_status quant_linear(const float *x, int act_group, const uint8_t *hi, const uint8_t *lo,
+                            const uint16_t *scale, float *y, int8_t *xq, float *xs, int M, int N, int K,
+                            void *stream) {
+    if (act_group != 0 && act_group != kGroup) return BITNEST_EINVAL;
+    bitnest_status st = check_sizes(M, N, K);
+    if (st != BITNEST_OK) return st;
+    if (M == 0) return BITNEST_OK;                  // empty: pointers may be NULL
+    if (!x || !xq || !xs) return BITNEST_EINVAL;
+    if (N > 0 && (!hi || !scale || !y)) return BITNEST_EINVAL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return BITNEST_EALIGN;
+    if (N > 0 && (!aligned16(hi) || !aligned16(scale) || !aligned16(y) || (lo && !aligned16(lo))))
+        return BITNEST_EALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bitnest::LinearArgs a{xq, xs, hi, lo, scale, y, nullptr, nullptr, nullptr, M, N, K, act_group, x, xq, xs};
+    if (N > 0 && bitnest::fused_in_one_launch(M, K))
+        return to_status(bitnest::launch_gemv_fused(a, s));
+    st = to_status(bitnest::launch_quant_act(x, M, K, act_group, xq, xs, s));
+    if (st != BITNEST_OK || N == 0) return st;
+    return run_linear(a, false, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+bitnest_status bitnest_quant_linear_draft(const float *x, int act_group, const uint8_t *hi, const uint16_t *scale,
+                                          float *y, int8_t *xq, float *xs, int M, int N, int K, void *stream) {
+    return quant_linear(x, act_group, hi, nullptr, scale, y, xq, xs, M, N, K, stream);
+}
+
+bitnest_status bitnest_quant_linear_target(const float *x, int act_group, const uint8_t *hi, const uint8_t *lo,
+                                           const uint16_t *scale, float *y, int8_t *xq, float *xs, int M, int N,
+                                           int K, void *stream) {
+    if (M > 0 && N > 0 && !lo) return BITNEST_EINVAL;
+    return quant_linear(x, act_group, hi, lo, scale, y, xq, xs, M, N, K, stream);
+}
+
 bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo, int32_t *p_hi,
                                        int32_t *p_lo, int32_t *p8, int M, int N, int K, void *stream) {
     bitnest_status st = check_sizes(M, N, K);

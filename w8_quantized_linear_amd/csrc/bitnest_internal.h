@@ -32,6 +32,11 @@ struct LinearArgs {
     int32_t *p8;
     int M, N, K;
     int act_group;              // 0 or 128
+    // fused activation quantisation (launch_gemv_fused): fp32 input; the
+    // codes and scales are also written to xq_out / xs_out
+    const float *x;
+    int8_t *xq_out;
+    float *xs_out;
 };
 
 hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t *xq, float *xs,
@@ -39,6 +44,17 @@ hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t 
 
 // M <= kGemvMaxM. export_partials selects the integer export instead of y.
 hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream);
+
+// Activation quantisation fused into the GEMV prologue: every workgroup
+// quantises the fp32 input itself and workgroup 0 writes the codes and
+// scales to a.xq_out / a.xs_out. Worth it only while the per-workgroup
+// quantisation is small next to the launch it saves: on MI355X that holds
+// for one token (M == 1) and not for the 4-token verify batch. Other shapes
+// return hipErrorNotSupported; the caller then runs launch_quant_act and a
+// linear launch.
+constexpr int kFusedMaxMK = 16384;
+inline bool fused_in_one_launch(int M, int K) { return M == 1 && K <= kFusedMaxMK; }
+hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream);
 
 // 8 <= M <= kMaxM.
 hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStream_t stream);

@@ -73,6 +73,40 @@ __device__ __forceinline__ float wave_max_f32(float v) {
     return v;
 }
 
+// The activation quantisation rule of the public header: q = 0 if s == 0,
+// else clamp(round_half_even(x / s), -127, 127), x / s an IEEE fp32 division.
+//
+// Computed without a division per element: with r = fl(1/s) and
+// t = fl(x * r), |t - x/s| <= |x/s| (2u + u^2) and the correctly rounded
+// quotient q = fl(x/s) has |q - x/s| <= |x/s| u (u = 2^-24), so
+// |t - q| <= 3.0001 u |x/s| <= 2.3e-5 for |x/s| <= 127.5 (|x| <= amax, hence
+// |x/s| <= 127 (1 + u)). When t is farther than that from every half-integer
+// tie, rint(t) == rint(q); only the rare elements within 3e-5 of a tie take
+// the exact division (hipcc's default division is correctly rounded).
+__device__ __forceinline__ int quant_code_r(float x, float s, float r) {
+    if (s == 0.0f) return 0;
+    const float t = x * r;
+    float c = rintf(t);                     // v_rndne_f32: ties to even
+    if (!(fabsf(t - c) <= 0.49997f)) c = rintf(x / s);   // near a tie, or r overflowed
+    c = fminf(fmaxf(c, -127.0f), 127.0f);
+    return static_cast<int>(c);
+}
+
+__device__ __forceinline__ float quant_recip(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+
+// Four codes packed into a dword (first element in the low byte); r is
+// quant_recip(s).
+__device__ __forceinline__ unsigned quant_pack4(const float4 &v, float s, float r) {
+    return (static_cast<unsigned>(quant_code_r(v.x, s, r)) & 0xFFu) |
+           ((static_cast<unsigned>(quant_code_r(v.y, s, r)) & 0xFFu) << 8) |
+           ((static_cast<unsigned>(quant_code_r(v.z, s, r)) & 0xFFu) << 16) |
+           ((static_cast<unsigned>(quant_code_r(v.w, s, r)) & 0xFFu) << 24);
+}
+
+__device__ __forceinline__ float absmax4(const float4 &v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
 __device__ __forceinline__ int sdot4(unsigned a, unsigned b, int acc) {
     return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), acc, false);
 }

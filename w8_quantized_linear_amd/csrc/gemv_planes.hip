@@ -87,9 +87,13 @@ __device__ __forceinline__ int dot_slot16(const Signed16 &n, const u32x4 a0, con
 template <int M>
 struct GemvLds {
     static constexpr int kMP = (M + 3) & ~3;   // tokens padded to 4 in the grouped-scale table
-    static size_t bytes(int K, bool grouped_act) {
+    // codes [M][K] bytes, then either the grouped activation scales [G][kMP]
+    // or (fused per-token quantisation) a [waves][M] scratch for the maxima
+    static size_t bytes(int K, bool grouped_act, bool fused = false, int waves = 16) {
         const size_t G = K / kGroup;
-        return static_cast<size_t>(M) * K + (grouped_act ? G * kMP * sizeof(float) : 0);
+        size_t tail = grouped_act ? G * kMP * sizeof(float) : 0;
+        if (fused && !grouped_act) tail = static_cast<size_t>(waves) * M * sizeof(float);
+        return static_cast<size_t>(M) * K + tail;
     }
 };
 
@@ -143,7 +147,7 @@ struct Item {
 // (scalar registers) plus a fixed lane offset, so address arithmetic stays
 // off the vector ALU; loads past the end of a plane return 0. The workgroup
 // stages the codes once into LDS while its first D items are in flight.
-template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES>
+template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArgs a) {
     constexpr int kThreads = 64 * WAVES;
     constexpr int kPB = (kMaxK / 16 + kThreads - 1) / kThreads;   // code blocks per thread and token
@@ -196,57 +200,150 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
         }
     };
 
-    // 1) codes (kPB 16-column blocks per thread and token cover K), the
-    //    activation scales, then the first D items
-    const int nb16 = K >> 4;
-    u32x4 pre[M][kPB];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int t = 0; t < kPB; ++t) {
-            const int j = threadIdx.x + t * kThreads;
-            if (j < nb16) pre[m][t] = *reinterpret_cast<const u32x4 *>(a.xq + static_cast<size_t>(m) * K + j * 16);
-        }
-    float tok_scale[M];
-    if (!GA && !EXPORT) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) tok_scale[m] = a.xs[m];
-    }
-    constexpr int kGAPer = (kGroup * 8 + kThreads - 1) / kThreads;
-    float gscale[kGAPer];
-    if (GA) {
-#pragma unroll
-        for (int t = 0; t < kGAPer; ++t) {
-            const int i = threadIdx.x + t * kThreads;     // flat [G][kMP]
-            gscale[t] = 0.0f;
-            if (i < G * kMP) {
-                const int g = i / kMP, m = i - (i / kMP) * kMP;
-                if (m < M) gscale[t] = a.xs[static_cast<size_t>(m) * G + g];
-            }
-        }
-    }
-    Item<PLANES> ring[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue(ring[d]);
-
-    // 2) stage the codes into LDS while the ring is in flight
     unsigned char *act = smem;                                                    // [M][2][slots][16]
     float *sact = reinterpret_cast<float *>(smem + static_cast<size_t>(M) * K);   // [G][kMP] (GA)
+    const int nb16 = K >> 4;
+    float tok_scale[M];
+    Item<PLANES> ring[D];
+
+    if constexpr (!FUSED) {
+        // 1) codes (kPB 16-column blocks per thread and token cover K), the
+        //    activation scales, then the first D items
+        u32x4 pre[M][kPB];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int t = 0; t < kPB; ++t) {
-            const int j = threadIdx.x + t * kThreads;
-            if (j < nb16) stage_block(act + static_cast<size_t>(m) * K, j, row_bytes, pre[m][t]);
+            for (int t = 0; t < kPB; ++t) {
+                const int j = threadIdx.x + t * kThreads;
+                if (j < nb16) pre[m][t] = *reinterpret_cast<const u32x4 *>(a.xq + static_cast<size_t>(m) * K + j * 16);
+            }
+        if (!GA && !EXPORT) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) tok_scale[m] = a.xs[m];
         }
-    if (GA) {
+        constexpr int kGAPer = (kGroup * 8 + kThreads - 1) / kThreads;
+        float gscale[kGAPer];
+        if (GA) {
 #pragma unroll
-        for (int t = 0; t < kGAPer; ++t) {
-            const int i = threadIdx.x + t * kThreads;
-            if (i < G * kMP) sact[i] = gscale[t];
+            for (int t = 0; t < kGAPer; ++t) {
+                const int i = threadIdx.x + t * kThreads;     // flat [G][kMP]
+                gscale[t] = 0.0f;
+                if (i < G * kMP) {
+                    const int g = i / kMP, m = i - (i / kMP) * kMP;
+                    if (m < M) gscale[t] = a.xs[static_cast<size_t>(m) * G + g];
+                }
+            }
         }
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(ring[d]);
+
+        // 2) stage the codes into LDS while the ring is in flight
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int t = 0; t < kPB; ++t) {
+                const int j = threadIdx.x + t * kThreads;
+                if (j < nb16) stage_block(act + static_cast<size_t>(m) * K, j, row_bytes, pre[m][t]);
+            }
+        if (GA) {
+#pragma unroll
+            for (int t = 0; t < kGAPer; ++t) {
+                const int i = threadIdx.x + t * kThreads;
+                if (i < G * kMP) sact[i] = gscale[t];
+            }
+        }
+        __syncthreads();
+    } else {
+        // 1) the fp32 activations: 8-column units u = m * K/8 + j of the
+        //    row-major [M, K] input (offset 8 u), units tid, tid + threads, ...
+        //    per thread (M * K <= kFusedMaxMK, so kXU units cover them), then
+        //    the ring
+        constexpr int kXU = (kFusedMaxMK / 8 + kThreads - 1) / kThreads;
+        const int nb8 = K >> 3;
+        const int nunit = M * nb8;
+        float4 xv[kXU][2];
+#pragma unroll
+        for (int k = 0; k < kXU; ++k) {
+            const int u = threadIdx.x + k * kThreads;
+            const float4 *src = reinterpret_cast<const float4 *>(a.x) + static_cast<size_t>(u < nunit ? u : 0) * 2;
+            xv[k][0] = src[0];
+            xv[k][1] = src[1];
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(ring[d]);
+
+        // 2) scales: per 128-column group (16 consecutive units = 16
+        //    consecutive lanes) or per token (a workgroup-wide maximum)
+        float uscale[kXU];
+        if (GA) {
+#pragma unroll
+            for (int k = 0; k < kXU; ++k) {
+                const int u = threadIdx.x + k * kThreads;
+                float am = fmaxf(absmax4(xv[k][0]), absmax4(xv[k][1]));
+                am = fmaxf(am, __shfl_xor(am, 1));
+                am = fmaxf(am, __shfl_xor(am, 2));
+                am = fmaxf(am, __shfl_xor(am, 4));
+                am = fmaxf(am, __shfl_xor(am, 8));
+                uscale[k] = am / 127.0f;
+                if (u < nunit && (u & 15) == 0) {
+                    const int gm = u >> 4;                  // flat (m, g) = m * G + g
+                    const int m = gm / G, g = gm - (gm / G) * G;
+                    sact[g * kMP + m] = uscale[k];
+                    if (blockIdx.x == 0) a.xs_out[gm] = uscale[k];
+                }
+            }
+        } else {
+            float *part = sact;                             // [WAVES][M] scratch (no grouped table)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float am = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kXU; ++k) {
+                    const int u = threadIdx.x + k * kThreads;
+                    if (u < nunit && u / nb8 == m) am = fmaxf(am, fmaxf(absmax4(xv[k][0]), absmax4(xv[k][1])));
+                }
+                am = wave_max_f32(am);
+                if (lane == 0) part[wave * M + m] = am;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float am = part[m];
+#pragma unroll
+                for (int w = 1; w < WAVES; ++w) am = fmaxf(am, part[w * M + m]);
+                tok_scale[m] = am / 127.0f;
+                if (blockIdx.x == 0 && threadIdx.x == 0) a.xs_out[m] = tok_scale[m];
+            }
+#pragma unroll
+            for (int k = 0; k < kXU; ++k) {
+                const int m = (threadIdx.x + k * kThreads) / nb8;
+                float sc = tok_scale[0];
+#pragma unroll
+                for (int mm = 1; mm < M; ++mm) sc = m == mm ? tok_scale[mm] : sc;
+                uscale[k] = sc;
+            }
+        }
+        // 3) codes -> LDS, permuted (unit j of a token is the 8-byte
+        //    [even | odd] pair (j & 1) of half (j >> 1) & 1 of slot j >> 2),
+        //    and to xq_out from workgroup 0
+#pragma unroll
+        for (int k = 0; k < kXU; ++k) {
+            const int u = threadIdx.x + k * kThreads;
+            if (u < nunit) {
+                const float r = quant_recip(uscale[k]);
+                const unsigned c0 = quant_pack4(xv[k][0], uscale[k], r);
+                const unsigned c1 = quant_pack4(xv[k][1], uscale[k], r);
+                const int m = u / nb8;
+                const int j = u - m * nb8;
+                unsigned char *dst = act + static_cast<size_t>(m) * K + ((j >> 1) & 1) * row_bytes + (j >> 2) * 16 +
+                                     (j & 1) * 8;
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(__builtin_amdgcn_perm(c1, c0, kSelEven),
+                                                             __builtin_amdgcn_perm(c1, c0, kSelOdd));
+                if (blockIdx.x == 0) *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(u) * 8) = make_uint2(c0, c1);
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     const u32x4 *act4 = reinterpret_cast<const u32x4 *>(act);
     const int tok4 = K >> 4;     // u32x4 per token
@@ -321,63 +418,62 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
 typedef void (*GemvKernel)(const LinearArgs);
 
 // Launch shape: waves per workgroup and items (1 KiB chunks per plane) in
-// flight per wave.
+// flight per wave. (Measured on MI355X over the Llama-3-8B shapes: 2-4 items
+// per wave with 8-wave workgroups beat deeper rings, which cost occupancy.)
 constexpr int kGemvWaves = 8;
-// (Measured on MI355X over the Llama-3-8B shapes: 2-4 items per wave with
-// 8-wave workgroups beat deeper rings, which cost occupancy.)
 template <int PLANES, int M>
 constexpr int items_in_flight() {
     return PLANES == 1 ? 4 : 2;
 }
 
 template <int PLANES, int M>
-GemvKernel pick_mode(bool grouped, bool exporting) {
+GemvKernel pick_mode(bool grouped, bool exporting, bool fused) {
     constexpr int D = items_in_flight<PLANES, M>();
     constexpr int W = kGemvWaves;
-    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W>;
-    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W>
-                   : gemv_planes_kernel<PLANES, M, false, false, D, W>;
+    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, false>;
+    if (fused)
+        return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, true>
+                       : gemv_planes_kernel<PLANES, M, false, false, D, W, true>;
+    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, false>
+                   : gemv_planes_kernel<PLANES, M, false, false, D, W, false>;
 }
 
 template <int PLANES>
-GemvKernel pick_m(int M, bool grouped, bool exporting) {
+GemvKernel pick_m(int M, bool grouped, bool exporting, bool fused) {
     switch (M) {
-        case 1: return pick_mode<PLANES, 1>(grouped, exporting);
-        case 2: return pick_mode<PLANES, 2>(grouped, exporting);
-        case 3: return pick_mode<PLANES, 3>(grouped, exporting);
-        case 4: return pick_mode<PLANES, 4>(grouped, exporting);
-        case 5: return pick_mode<PLANES, 5>(grouped, exporting);
-        case 6: return pick_mode<PLANES, 6>(grouped, exporting);
-        case 7: return pick_mode<PLANES, 7>(grouped, exporting);
+        case 1: return pick_mode<PLANES, 1>(grouped, exporting, fused);
+        case 2: return pick_mode<PLANES, 2>(grouped, exporting, fused);
+        case 3: return pick_mode<PLANES, 3>(grouped, exporting, fused);
+        case 4: return pick_mode<PLANES, 4>(grouped, exporting, fused);
+        case 5: return pick_mode<PLANES, 5>(grouped, exporting, fused);
+        case 6: return pick_mode<PLANES, 6>(grouped, exporting, fused);
+        case 7: return pick_mode<PLANES, 7>(grouped, exporting, fused);
         default: return nullptr;
     }
 }
 
-size_t gemv_lds_bytes(int M, int K, bool grouped) {
+size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused) {
     switch (M) {
-        case 1: return GemvLds<1>::bytes(K, grouped);
-        case 2: return GemvLds<2>::bytes(K, grouped);
-        case 3: return GemvLds<3>::bytes(K, grouped);
-        case 4: return GemvLds<4>::bytes(K, grouped);
-        case 5: return GemvLds<5>::bytes(K, grouped);
-        case 6: return GemvLds<6>::bytes(K, grouped);
-        case 7: return GemvLds<7>::bytes(K, grouped);
+        case 1: return GemvLds<1>::bytes(K, grouped, fused, kGemvWaves);
+        case 2: return GemvLds<2>::bytes(K, grouped, fused, kGemvWaves);
+        case 3: return GemvLds<3>::bytes(K, grouped, fused, kGemvWaves);
+        case 4: return GemvLds<4>::bytes(K, grouped, fused, kGemvWaves);
+        case 5: return GemvLds<5>::bytes(K, grouped, fused, kGemvWaves);
+        case 6: return GemvLds<6>::bytes(K, grouped, fused, kGemvWaves);
+        case 7: return GemvLds<7>::bytes(K, grouped, fused, kGemvWaves);
         default: return 0;
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream) {
+hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t stream) {
     const bool target = a.lo != nullptr;
-    const bool grouped = a.act_group == kGroup && !export_partials;
-    GemvKernel k = target ? pick_m<2>(a.M, grouped, export_partials)
-                          : pick_m<1>(a.M, grouped, export_partials);
+    const bool grouped = a.act_group == kGroup && !exporting;
+    GemvKernel k = target ? pick_m<2>(a.M, grouped, exporting, fused) : pick_m<1>(a.M, grouped, exporting, fused);
     if (!k) return hipErrorInvalidValue;
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
-    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped);
+    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
     if (lds > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
@@ -396,6 +492,17 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
     const int blocks = rows_blocks < full ? rows_blocks : full;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), lds, stream, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream) {
+    return launch(a, export_partials, false, stream);
+}
+
+hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream) {
+    if (!fused_in_one_launch(a.M, a.K)) return hipErrorNotSupported;
+    return launch(a, false, true, stream);
 }
 
 }  // namespace bitnest

@@ -3,7 +3,7 @@
 // o_proj). The rule, which the pages leave open and the public header states:
 //   s = amax / 127 (IEEE fp32 division), q = 0 if s == 0, otherwise
 //   q = clamp(round_half_even(x / s), -127, 127) with x / s an IEEE fp32
-//   division (hipcc's default division is correctly rounded; no fast-math).
+//   division (quant_code_r in device_common.h, shared with the fused GEMV).
 //
 // The work is a few KiB per token and latency-bound: one workgroup per token
 // holds its whole row in registers (one HBM round trip), reduces |x| with
@@ -16,24 +16,6 @@ namespace {
 
 constexpr int kQuantThreads = 256;     // grouped kernel
 constexpr int kTokenThreads = 1024;    // per-token kernel
-
-__device__ __forceinline__ int code_of(float x, float s) {
-    if (s == 0.0f) return 0;
-    float r = rintf(x / s);                 // v_rndne_f32: ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return static_cast<int>(r);
-}
-
-__device__ __forceinline__ unsigned pack4(const float4 &v, float s) {
-    return (static_cast<unsigned>(code_of(v.x, s)) & 0xFFu) |
-           ((static_cast<unsigned>(code_of(v.y, s)) & 0xFFu) << 8) |
-           ((static_cast<unsigned>(code_of(v.z, s)) & 0xFFu) << 16) |
-           ((static_cast<unsigned>(code_of(v.w, s)) & 0xFFu) << 24);
-}
-
-__device__ __forceinline__ float absmax4(const float4 &v) {
-    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-}
 
 // One token per workgroup of 1024 threads; each thread keeps up to NV float4
 // of the row in registers. All loads are issued unconditionally (clamped
@@ -64,12 +46,13 @@ __global__ __launch_bounds__(kTokenThreads) void quant_token_kernel(
 #pragma unroll
     for (int w = 1; w < kTokenThreads / 64; ++w) amax = fmaxf(amax, part[w]);
     const float sc = amax / 127.0f;
+    const float rc = quant_recip(sc);
     if (threadIdx.x == 0) s[m] = sc;
     unsigned *qr = reinterpret_cast<unsigned *>(q + static_cast<size_t>(m) * K);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = threadIdx.x + i * kTokenThreads;
-        if (idx < n4) qr[idx] = pack4(v[i], sc);
+        if (idx < n4) qr[idx] = quant_pack4(v[i], sc, rc);
     }
 }
 
@@ -87,9 +70,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     const float sc = amax / 127.0f;
+    const float rc = quant_recip(sc);
     if (active) {
         if (l == 0) s[gid] = sc;
-        reinterpret_cast<unsigned *>(q + static_cast<size_t>(gid) * kGroup)[l] = pack4(v, sc);
+        reinterpret_cast<unsigned *>(q + static_cast<size_t>(gid) * kGroup)[l] = quant_pack4(v, sc, rc);
     }
 }
 
