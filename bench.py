@@ -47,6 +47,9 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU work for the oracle baseline sample")
     p.add_argument("--no-kernel-timing", dest="kernel_timing", action="store_false", default=True)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="run one plain device copy of MIB MiB before timing (a known-size "
+                        "reference dispatch for hardware byte counters)")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -183,6 +186,25 @@ def gemv_kernel_timing(stack, bn, steps):
     return per[len(per) // 2] * 1e-3     # seconds per launch, median over replays
 
 
+def measured_traffic():
+    """HBM bytes per linear launch from the committed hardware-counter
+    profile (rocprofv3 FETCH_SIZE and WRITE_SIZE of the round's launches,
+    scaled by a known-size copy), or None when the kernel sources have
+    changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_planes_round_traffic.json")
+    try:
+        with open(path) as f:
+            prof = json.load(f)
+        h = hashlib.sha256()
+        for src in prof["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return prof["traffic_bytes_per_launch"] if h.hexdigest() == prof["sources_sha256"] else None
+
+
 def cpu_baseline(stack, budget_s):
     """The oracle on the machine's host cores over a bounded sample of the round:
     the first layer(s) of the stack, 3 draft passes + 1 verify pass each,
@@ -235,6 +257,16 @@ def main(argv=None):
     log("stack ready: %d layers, %.2f GB of planes per round, %.1f s"
         % (args.layers, stack.plane_bytes_per_round() / 1e9, time.perf_counter() - t0))
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
+
     fused = not args.unfused
     graph = capture(lambda: run_round(stack, bn, mode="fused" if fused else "unfused"))
     for _ in range(args.warmup):
@@ -260,7 +292,7 @@ def main(argv=None):
         per_launch_bytes = stack.gemv_algorithmic_bytes_per_round() / stack.gemv_launches_per_round()
         achieved = per_launch_bytes / t_gemv / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                     "kernel": "gemv_planes_kernel (draft M=1 and target M=4 instantiations, fused "
                               "quantisation where the round uses it)",
                     "avg_launch_us": round(t_gemv * 1e6, 3),
