@@ -50,6 +50,8 @@ def parse_args(argv=None):
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="run one plain device copy of MIB MiB before timing (a known-size "
                         "reference dispatch for hardware byte counters)")
+    p.add_argument("--verify-batches", default="8,16,32",
+                   help="token counts for the batched-verify (matrix-core) layer timing; empty to skip")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -186,6 +188,60 @@ def gemv_kernel_timing(stack, bn, steps):
     return per[len(per) // 2] * 1e-3     # seconds per launch, median over replays
 
 
+INT8_DENSE_PEAK_OPS = 5.0e15       # MI355X dense int8 matrix-core peak, ops/s
+
+
+def batched_verify(stack, bn, batches, reps=20):
+    """Target linears of one layer at M in `batches` (several sequences of
+    gamma + 1 verify tokens), on the int8 matrix-core kernel. Each M is
+    timed as a HIP graph of `reps` passes over distinct layers (cold weights)
+    with HIP events; reports per-layer time, plane GB/s and the matrix-core
+    utilisation implied by the method's integer ops (2 M N K per plane)."""
+    import torch
+    from w8_quantized_linear_amd import synth
+    out = {}
+    layers = list(range(min(stack.layers, reps)))
+    for M in batches:
+        xs_in = [synth.make_activations(M, K, seed=7, layer=l, linear=i, step=M, device="cuda")
+                 for l in layers for i, (_, _, K, _) in enumerate(stack.linears)]
+        bufs = [(torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                 torch.empty((M,) if g == 0 else (M, K // 128), dtype=torch.float32, device="cuda"),
+                 torch.empty((M, N), dtype=torch.float32, device="cuda")) for (_, N, K, g) in stack.linears]
+        xq_all = []
+        for j, x in enumerate(xs_in):
+            i = j % len(stack.linears)
+            g = stack.linears[i][3]
+            xq_all.append(bn.bitnest_quant_act(x, g))
+
+        def layer_pass():
+            for j, l in enumerate(layers):
+                for i, (_, N, K, g) in enumerate(stack.linears):
+                    xq, xs = xq_all[j * len(stack.linears) + i]
+                    w = stack.w[l][i]
+                    bn.bitnest_linear_target(xq, xs, w.hi, w.lo, w.scale, g, y=bufs[i][2])
+        graph = capture(layer_pass)
+        graph.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3 / len(layers))
+        t = sorted(times)[len(times) // 2]
+        plane = sum(N * K for (_, N, K, _) in stack.linears)          # both planes: 2 * N*K/2
+        ops = 2 * M * 2 * sum(N * K for (_, N, K, _) in stack.linears)
+        out[str(M)] = {"layer_us": round(t * 1e6, 2), "plane_GBps": round(plane / t / 1e9, 1),
+                       "pct_hbm_peak": round(100 * plane / t / 1e9 / HBM_PEAK_GBS, 2),
+                       "int_ops_per_s": float("%.4g" % (ops / t)),
+                       "mfma_util_pct": round(100 * ops / t / INT8_DENSE_PEAK_OPS, 2)}
+        log("batched verify M=%d: %.2f us/layer, %.1f GB/s, MFMA util %.2f%%"
+            % (M, t * 1e6, plane / t / 1e9, 100 * ops / t / INT8_DENSE_PEAK_OPS))
+    return out
+
+
 def measured_traffic():
     """HBM bytes per linear launch from the committed hardware-counter
     profile (rocprofv3 FETCH_SIZE and WRITE_SIZE of the round's launches,
@@ -299,6 +355,11 @@ def main(argv=None):
                     "algorithmic_bytes_per_launch": int(per_launch_bytes)}
         log("GEMV: %.3f us per launch (events), %.1f GB/s algorithmic" % (t_gemv * 1e6, achieved))
 
+    verify = None
+    batches = [int(v) for v in args.verify_batches.split(",") if v.strip()]
+    if batches:
+        verify = batched_verify(stack, bn, batches)
+
     cpu = None
     if args.cpu_baseline:
         cpu = cpu_baseline(stack, args.cpu_seconds)
@@ -325,6 +386,7 @@ def main(argv=None):
                    "replay": "hip_graph"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
+        "batched_verify": verify,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -76,31 +76,76 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // The activation quantisation rule of the public header: q = 0 if s == 0,
 // else clamp(round_half_even(x / s), -127, 127), x / s an IEEE fp32 division.
 //
-// Computed without a division per element: with r = fl(1/s) and
-// t = fl(x * r), |t - x/s| <= |x/s| (2u + u^2) and the correctly rounded
-// quotient q = fl(x/s) has |q - x/s| <= |x/s| u (u = 2^-24), so
-// |t - q| <= 3.0001 u |x/s| <= 2.3e-5 for |x/s| <= 127.5 (|x| <= amax, hence
-// |x/s| <= 127 (1 + u)). When t is farther than that from every half-integer
-// tie, rint(t) == rint(q); only the rare elements within 3e-5 of a tie take
-// the exact division (hipcc's default division is correctly rounded).
-__device__ __forceinline__ int quant_code_r(float x, float s, float r) {
-    if (s == 0.0f) return 0;
-    const float t = x * r;
-    float c = rintf(t);                     // v_rndne_f32: ties to even
-    if (!(fabsf(t - c) <= 0.49997f)) c = rintf(x / s);   // near a tie, or r overflowed
-    c = fminf(fmaxf(c, -127.0f), 127.0f);
-    return static_cast<int>(c);
+// Computed without a division per element. With r = fl(1/s), the exact
+// product x r is within u |x/s| of x/s, and so is the correctly rounded
+// quotient fl(x/s) (u = 2^-24, |x/s| <= 127 (1 + u) because |x| <= amax), so
+// the two are within 1.6e-5 of each other. One fma rounds x r to the nearest
+// integer c (ties to even; see kRoundMagic) and a second one gives the
+// distance |x r - c| to a rounding error of 2^-25. When that distance is at
+// most 0.49997, x r is at least 3e-5 from every half-integer, fl(x/s) lies on
+// the same side of all of them, and rint(fl(x/s)) == c. Otherwise (a value
+// within 3e-5 of a tie, or 1/s overflowed) the whole unit of values is
+// redone with the exact division. The clamp can never act: |x/s| <= 127 (1+u)
+// rounds to at most 127.
+//
+// kRoundMagic = 1.5 * 2^23: for |v| < 2^22, v + kRoundMagic lies in [2^23,
+// 2^24), where the fp32 spacing is 1, so the sum is v rounded to an integer
+// (ties to even: kRoundMagic is even), and the low byte of its bit pattern is
+// that integer modulo 256, i.e. the int8 code.
+constexpr float kRoundMagic = 12582912.0f;
+
+// Codes of n values with one scale: y[i] holds code i in its low byte.
+template <int n>
+__device__ __forceinline__ void quant_codes(const float (&x)[n], float s, float r, unsigned (&y)[n]) {
+    float dist = 0.0f;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        const float v = __builtin_fmaf(x[i], r, kRoundMagic);
+        dist = fmaxf(dist, fabsf(__builtin_fmaf(x[i], r, -(v - kRoundMagic))));
+        y[i] = __builtin_bit_cast(unsigned, v);
+    }
+    if (!(dist <= 0.49997f) || !(r <= 3.0e38f)) {
+#pragma unroll
+        for (int i = 0; i < n; ++i) y[i] = __builtin_bit_cast(unsigned, rintf(x[i] / s) + kRoundMagic);
+    }
 }
 
 __device__ __forceinline__ float quant_recip(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
 
+// The low bytes of y0..y3 as one dword, y0's in the lowest byte.
+__device__ __forceinline__ unsigned pack_low_bytes(unsigned y0, unsigned y1, unsigned y2, unsigned y3) {
+    const unsigned p01 = __builtin_amdgcn_perm(y1, y0, 0x0c0c0400u);
+    const unsigned p23 = __builtin_amdgcn_perm(y3, y2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+}
+
 // Four codes packed into a dword (first element in the low byte); r is
 // quant_recip(s).
 __device__ __forceinline__ unsigned quant_pack4(const float4 &v, float s, float r) {
-    return (static_cast<unsigned>(quant_code_r(v.x, s, r)) & 0xFFu) |
-           ((static_cast<unsigned>(quant_code_r(v.y, s, r)) & 0xFFu) << 8) |
-           ((static_cast<unsigned>(quant_code_r(v.z, s, r)) & 0xFFu) << 16) |
-           ((static_cast<unsigned>(quant_code_r(v.w, s, r)) & 0xFFu) << 24);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    unsigned y[4];
+    quant_codes<4>(x, s, r, y);
+    return pack_low_bytes(y[0], y[1], y[2], y[3]);
+}
+
+// Maximum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ float row16_max_f32(float v) {
+    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+    v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+    return v;
+}
+
+// Maximum over the wave, wave-uniform.
+__device__ __forceinline__ float wave_max_dpp_f32(float v) {
+    v = row16_max_f32(v);
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ float absmax4(const float4 &v) {

@@ -138,7 +138,8 @@ struct Item {
 
 // PLANES: 1 draft (hi), 2 target (hi + lo). GA: per-128-group activation
 // scales. EXPORT: write the integer partials instead of y. D: items in flight
-// per wave. WAVES: waves per workgroup.
+// per wave. WAVES: waves per workgroup. XU: 0, or (one token only) quantise
+// the fp32 input in the prologue, XU 8-column units per thread.
 //
 // A row of K columns is C = ceil(K / 2048) chunks; the (row, chunk) items of
 // the whole call are split into contiguous runs, one per wave, and each wave
@@ -147,8 +148,9 @@ struct Item {
 // (scalar registers) plus a fixed lane offset, so address arithmetic stays
 // off the vector ALU; loads past the end of a plane return 0. The workgroup
 // stages the codes once into LDS while its first D items are in flight.
-template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, bool FUSED>
+template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, int XU>
 __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArgs a) {
+    constexpr bool FUSED = XU > 0;
     constexpr int kThreads = 64 * WAVES;
     constexpr int kPB = (kMaxK / 16 + kThreads - 1) / kThreads;   // code blocks per thread and token
     constexpr int kMP = GemvLds<M>::kMP;
@@ -254,92 +256,92 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
         }
         __syncthreads();
     } else {
-        // 1) the fp32 activations: 8-column units u = m * K/8 + j of the
-        //    row-major [M, K] input (offset 8 u), units tid, tid + threads, ...
-        //    per thread (M * K <= kFusedMaxMK, so kXU units cover them), then
-        //    the ring
-        constexpr int kXU = (kFusedMaxMK / 8 + kThreads - 1) / kThreads;
-        const int nb8 = K >> 3;
-        const int nunit = M * nb8;
-        float4 xv[kXU][2];
+        static_assert(M == 1, "the fused prologue quantises one token");
+        // 1) the fp32 row in 8-column units u = tid + k * threads (k < XU),
+        //    two 16-byte loads each; waves wholly past the row skip them and
+        //    lanes past it read zeros; then the ring
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, static_cast<unsigned>(K) * 4u);
+        const int nunit = K >> 3;
+        u32x4 xr[XU][2];
 #pragma unroll
-        for (int k = 0; k < kXU; ++k) {
-            const int u = threadIdx.x + k * kThreads;
-            const float4 *src = reinterpret_cast<const float4 *>(a.x) + static_cast<size_t>(u < nunit ? u : 0) * 2;
-            xv[k][0] = src[0];
-            xv[k][1] = src[1];
+        for (int k = 0; k < XU; ++k) {
+            xr[k][0] = u32x4{0u, 0u, 0u, 0u};
+            xr[k][1] = xr[k][0];
+            if (k * kThreads + wave * 64 < nunit) {      // wave-uniform
+                const int off = (threadIdx.x + k * kThreads) * 32;
+                xr[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+                xr[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
+            }
         }
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(ring[d]);
 
-        // 2) scales: per 128-column group (16 consecutive units = 16
-        //    consecutive lanes) or per token (a workgroup-wide maximum)
-        float uscale[kXU];
+        // (each element is copied out before the bit cast: a bit cast applied
+        // directly to a vector-element lvalue reads element 0 with this
+        // compiler)
+        float xf[XU][8];
+#pragma unroll
+        for (int k = 0; k < XU; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xf[k][i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][0][i]));
+                xf[k][4 + i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][1][i]));
+            }
+        auto absmax8 = [](const float (&v)[8]) {
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+            return m;
+        };
+
+        // 2) scales: per 128-column group (16 consecutive units = one row of
+        //    16 lanes) or per token (a workgroup-wide maximum)
+        float us[XU], ur[XU];
         if (GA) {
 #pragma unroll
-            for (int k = 0; k < kXU; ++k) {
+            for (int k = 0; k < XU; ++k) {
                 const int u = threadIdx.x + k * kThreads;
-                float am = fmaxf(absmax4(xv[k][0]), absmax4(xv[k][1]));
-                am = fmaxf(am, __shfl_xor(am, 1));
-                am = fmaxf(am, __shfl_xor(am, 2));
-                am = fmaxf(am, __shfl_xor(am, 4));
-                am = fmaxf(am, __shfl_xor(am, 8));
-                uscale[k] = am / 127.0f;
+                us[k] = row16_max_f32(absmax8(xf[k])) / 127.0f;
+                ur[k] = quant_recip(us[k]);
                 if (u < nunit && (u & 15) == 0) {
-                    const int gm = u >> 4;                  // flat (m, g) = m * G + g
-                    const int m = gm / G, g = gm - (gm / G) * G;
-                    sact[g * kMP + m] = uscale[k];
-                    if (blockIdx.x == 0) a.xs_out[gm] = uscale[k];
+                    sact[(u >> 4) * kMP] = us[k];
+                    if (blockIdx.x == 0) a.xs_out[u >> 4] = us[k];
                 }
             }
         } else {
-            float *part = sact;                             // [WAVES][M] scratch (no grouped table)
+            float *part = sact;                 // [WAVES] scratch (no grouped table)
+            float am = 0.0f;
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float am = 0.0f;
-#pragma unroll
-                for (int k = 0; k < kXU; ++k) {
-                    const int u = threadIdx.x + k * kThreads;
-                    if (u < nunit && u / nb8 == m) am = fmaxf(am, fmaxf(absmax4(xv[k][0]), absmax4(xv[k][1])));
-                }
-                am = wave_max_f32(am);
-                if (lane == 0) part[wave * M + m] = am;
-            }
+            for (int k = 0; k < XU; ++k) am = fmaxf(am, absmax8(xf[k]));
+            am = wave_max_dpp_f32(am);
+            if (lane == 0) part[wave] = am;
             __syncthreads();
+            am = part[0];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float am = part[m];
+            for (int w = 1; w < WAVES; ++w) am = fmaxf(am, part[w]);
+            tok_scale[0] = am / 127.0f;
+            const float r = quant_recip(tok_scale[0]);
+            if (blockIdx.x == 0 && threadIdx.x == 0) a.xs_out[0] = tok_scale[0];
 #pragma unroll
-                for (int w = 1; w < WAVES; ++w) am = fmaxf(am, part[w * M + m]);
-                tok_scale[m] = am / 127.0f;
-                if (blockIdx.x == 0 && threadIdx.x == 0) a.xs_out[m] = tok_scale[m];
-            }
-#pragma unroll
-            for (int k = 0; k < kXU; ++k) {
-                const int m = (threadIdx.x + k * kThreads) / nb8;
-                float sc = tok_scale[0];
-#pragma unroll
-                for (int mm = 1; mm < M; ++mm) sc = m == mm ? tok_scale[mm] : sc;
-                uscale[k] = sc;
+            for (int k = 0; k < XU; ++k) {
+                us[k] = tok_scale[0];
+                ur[k] = r;
             }
         }
-        // 3) codes -> LDS, permuted (unit j of a token is the 8-byte
-        //    [even | odd] pair (j & 1) of half (j >> 1) & 1 of slot j >> 2),
-        //    and to xq_out from workgroup 0
+        // 3) codes -> LDS, unit u as the 8-byte [even | odd] pair (u & 1) of
+        //    half (u >> 1) & 1 of slot u >> 2; and to xq_out from workgroup 0
 #pragma unroll
-        for (int k = 0; k < kXU; ++k) {
+        for (int k = 0; k < XU; ++k) {
             const int u = threadIdx.x + k * kThreads;
             if (u < nunit) {
-                const float r = quant_recip(uscale[k]);
-                const unsigned c0 = quant_pack4(xv[k][0], uscale[k], r);
-                const unsigned c1 = quant_pack4(xv[k][1], uscale[k], r);
-                const int m = u / nb8;
-                const int j = u - m * nb8;
-                unsigned char *dst = act + static_cast<size_t>(m) * K + ((j >> 1) & 1) * row_bytes + (j >> 2) * 16 +
-                                     (j & 1) * 8;
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(__builtin_amdgcn_perm(c1, c0, kSelEven),
-                                                             __builtin_amdgcn_perm(c1, c0, kSelOdd));
-                if (blockIdx.x == 0) *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(u) * 8) = make_uint2(c0, c1);
+                unsigned y[8];
+                quant_codes<8>(xf[k], us[k], ur[k], y);
+                unsigned char *dst = act + ((u >> 1) & 1) * row_bytes + (u >> 2) * 16 + (u & 1) * 8;
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_low_bytes(y[0], y[2], y[4], y[6]),
+                                                             pack_low_bytes(y[1], y[3], y[5], y[7]));
+                if (blockIdx.x == 0)
+                    *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(u) * 8) =
+                        make_uint2(pack_low_bytes(y[0], y[1], y[2], y[3]), pack_low_bytes(y[4], y[5], y[6], y[7]));
             }
         }
         __syncthreads();
@@ -421,46 +423,66 @@ typedef void (*GemvKernel)(const LinearArgs);
 // flight per wave. (Measured on MI355X over the Llama-3-8B shapes: 2-4 items
 // per wave with 8-wave workgroups beat deeper rings, which cost occupancy.)
 constexpr int kGemvWaves = 8;
-template <int PLANES, int M>
+// The fused single-token kernel quantises the whole row in every workgroup,
+// so it runs one workgroup per compute unit. (Measured on MI355X: 8 waves
+// and one workgroup per CU beat 16-wave and two-per-CU shapes on all four
+// Llama-3-8B shapes.)
+constexpr int kFusedWaves = 8;
+template <int PLANES>
 constexpr int items_in_flight() {
     return PLANES == 1 ? 4 : 2;
 }
 
 template <int PLANES, int M>
-GemvKernel pick_mode(bool grouped, bool exporting, bool fused) {
-    constexpr int D = items_in_flight<PLANES, M>();
+GemvKernel pick_mode(bool grouped, bool exporting) {
+    constexpr int D = items_in_flight<PLANES>();
     constexpr int W = kGemvWaves;
-    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, false>;
-    if (fused)
-        return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, true>
-                       : gemv_planes_kernel<PLANES, M, false, false, D, W, true>;
-    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, false>
-                   : gemv_planes_kernel<PLANES, M, false, false, D, W, false>;
+    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, 0>;
+    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, 0>
+                   : gemv_planes_kernel<PLANES, M, false, false, D, W, 0>;
 }
 
 template <int PLANES>
-GemvKernel pick_m(int M, bool grouped, bool exporting, bool fused) {
+GemvKernel pick_m(int M, bool grouped, bool exporting) {
     switch (M) {
-        case 1: return pick_mode<PLANES, 1>(grouped, exporting, fused);
-        case 2: return pick_mode<PLANES, 2>(grouped, exporting, fused);
-        case 3: return pick_mode<PLANES, 3>(grouped, exporting, fused);
-        case 4: return pick_mode<PLANES, 4>(grouped, exporting, fused);
-        case 5: return pick_mode<PLANES, 5>(grouped, exporting, fused);
-        case 6: return pick_mode<PLANES, 6>(grouped, exporting, fused);
-        case 7: return pick_mode<PLANES, 7>(grouped, exporting, fused);
+        case 1: return pick_mode<PLANES, 1>(grouped, exporting);
+        case 2: return pick_mode<PLANES, 2>(grouped, exporting);
+        case 3: return pick_mode<PLANES, 3>(grouped, exporting);
+        case 4: return pick_mode<PLANES, 4>(grouped, exporting);
+        case 5: return pick_mode<PLANES, 5>(grouped, exporting);
+        case 6: return pick_mode<PLANES, 6>(grouped, exporting);
+        case 7: return pick_mode<PLANES, 7>(grouped, exporting);
         default: return nullptr;
     }
 }
 
-size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused) {
+// fp32 8-column units per thread that cover a row of K <= kFusedMaxMK.
+constexpr int fused_units(int K) { return (K / 8 + 64 * kFusedWaves - 1) / (64 * kFusedWaves); }
+static_assert(fused_units(kFusedMaxMK) <= 4, "pick_fused covers up to four units per thread");
+
+template <int PLANES, int XU>
+GemvKernel pick_fused_xu(bool grouped) {
+    constexpr int D = items_in_flight<PLANES>();
+    return grouped ? gemv_planes_kernel<PLANES, 1, true, false, D, kFusedWaves, XU>
+                   : gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU>;
+}
+
+template <int PLANES>
+GemvKernel pick_fused(int K, bool grouped) {
+    const int xu = fused_units(K);
+    return xu <= 1 ? pick_fused_xu<PLANES, 1>(grouped)
+                   : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped) : pick_fused_xu<PLANES, 4>(grouped);
+}
+
+size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused, int waves) {
     switch (M) {
-        case 1: return GemvLds<1>::bytes(K, grouped, fused, kGemvWaves);
-        case 2: return GemvLds<2>::bytes(K, grouped, fused, kGemvWaves);
-        case 3: return GemvLds<3>::bytes(K, grouped, fused, kGemvWaves);
-        case 4: return GemvLds<4>::bytes(K, grouped, fused, kGemvWaves);
-        case 5: return GemvLds<5>::bytes(K, grouped, fused, kGemvWaves);
-        case 6: return GemvLds<6>::bytes(K, grouped, fused, kGemvWaves);
-        case 7: return GemvLds<7>::bytes(K, grouped, fused, kGemvWaves);
+        case 1: return GemvLds<1>::bytes(K, grouped, fused, waves);
+        case 2: return GemvLds<2>::bytes(K, grouped, fused, waves);
+        case 3: return GemvLds<3>::bytes(K, grouped, fused, waves);
+        case 4: return GemvLds<4>::bytes(K, grouped, fused, waves);
+        case 5: return GemvLds<5>::bytes(K, grouped, fused, waves);
+        case 6: return GemvLds<6>::bytes(K, grouped, fused, waves);
+        case 7: return GemvLds<7>::bytes(K, grouped, fused, waves);
         default: return 0;
     }
 }
@@ -468,12 +490,17 @@ size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused) {
 hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t stream) {
     const bool target = a.lo != nullptr;
     const bool grouped = a.act_group == kGroup && !exporting;
-    GemvKernel k = target ? pick_m<2>(a.M, grouped, exporting, fused) : pick_m<1>(a.M, grouped, exporting, fused);
+    GemvKernel k;
+    if (fused)
+        k = target ? pick_fused<2>(a.K, grouped) : pick_fused<1>(a.K, grouped);
+    else
+        k = target ? pick_m<2>(a.M, grouped, exporting) : pick_m<1>(a.M, grouped, exporting);
     if (!k) return hipErrorInvalidValue;
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
-    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused);
+    const int waves = fused ? kFusedWaves : kGemvWaves;
+    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused, waves);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
     if (lds > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
@@ -481,13 +508,16 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
         if (e != hipSuccess) return e;
     }
     // One resident wave of workgroups (as many as the occupancy of this
-    // instantiation allows), never more workgroups than rows / waves.
-    int occ = 0;
-    const int threads = 64 * kGemvWaves;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(k), threads, lds);
-    if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
-    const int rows_blocks = (a.N + kGemvWaves - 1) / kGemvWaves;
+    // instantiation allows; one per compute unit for the fused kernel),
+    // never more workgroups than rows / waves.
+    int occ = 1;
+    const int threads = 64 * waves;
+    if (!fused) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(k), threads, lds);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+    }
+    const int rows_blocks = (a.N + waves - 1) / waves;
     const int full = dev.cus * occ;
     const int blocks = rows_blocks < full ? rows_blocks : full;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), lds, stream, a);

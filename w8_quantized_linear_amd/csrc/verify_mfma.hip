@@ -21,12 +21,14 @@
 //  - the activation bytes of the same 32 columns are split into the even and
 //    the odd columns with v_perm_b32, matching the weight operand byte for
 //    byte.
-// Two MFMAs (even, odd columns) per plane and token tile give 16 * P_hi and
-// 16 * P_lo for one 128-column group exactly; P8 = 16 P_hi + P_lo =
-// D_hi + (D_lo >> 4). The 8-bit code is never formed as an int8; each plane
-// has its own contraction, combined in int32.
-// Epilogue per group: fp32 accumulate of float(P) * scale (/16 for the
-// target) (* the group's activation scale for o_proj).
+// Two MFMAs (even, odd columns) per plane and token tile give D_hi = 16 P_hi
+// and D_lo = 16 P_lo for one 128-column group exactly; the target combines
+// them in int32 as 16 D_hi + D_lo = 16 P8 (|16 P8| < 2^26). The 8-bit code is
+// never formed as an int8; each plane has its own contraction.
+// Epilogue per group: fp32 accumulate of float(16 P) * scale / 16 (draft) or
+// float(16 P8) * scale / 256 (target), times the group's activation scale
+// for o_proj; both factors are powers of two, so the draft and the target
+// round alike.
 //
 // Work split: a workgroup owns 16 weight rows; its 8 waves split the groups
 // of K into contiguous ranges (one read of every plane byte), and the
@@ -37,8 +39,6 @@
 namespace bitnest {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 16;
 constexpr unsigned kSelEven = 0x06040200u;
 constexpr unsigned kSelOdd = 0x07050301u;
@@ -62,25 +62,67 @@ __device__ __forceinline__ void split_act(const u32x4 v0, const u32x4 v1, i32x4 
                 static_cast<int>(__builtin_amdgcn_perm(v1.w, v1.z, kSelOdd))};
 }
 
-// T: 16-token tiles (1 for M <= 16, 2 for M <= 32).
-template <int PLANES, int T, bool GA, bool EXPORT>
-__global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs a) {
+// Buffer descriptor over [p, p + bytes): loads beyond it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+constexpr int kAuxStream = 2;   // non-temporal: plane bytes are read once
+constexpr int kOOB = 0x7FFFFFF0;
+
+
+// One item = one 128-column group of the wave's 16-row tile: 16 plane bytes
+// per lane per plane, the group's scale bits for the lane's row, and the 32
+// activation bytes of the lane's token (per 16-token tile) in the same
+// columns.
+template <int PLANES, int T>
+struct VItem {
+    u32x4 h, l;
+    unsigned sbits;
+    u32x4 x[T][2];
+};
+
+// T: 16-token tiles (1 for M <= 16, 2 for M <= 32). SPLIT: waves per tile
+// (each streams a contiguous range of the K groups). D: items in flight.
+//
+// A workgroup owns one 16-row tile. Lane l works on weight row l % 16 and
+// token l % 16 (+16 t) in quarter l / 16 of each group, so every load has a
+// lane-constant vector offset and a wave-uniform scalar offset; rows past N
+// and tokens past M fall outside the buffer descriptors and read as zero.
+template <int PLANES, int T, bool GA, bool EXPORT, int SPLIT, int D>
+__global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    float *red = reinterpret_cast<float *>(smem);                       // [kWaves][T][4][64]
-    float *sact = red + kWaves * T * 4 * 64;                             // [G][16 T] (GA)
+    float *red = reinterpret_cast<float *>(smem);                       // [SPLIT][T][4][64]
+    float *sact = red + SPLIT * T * 4 * 64;                              // [G][16 T] (GA)
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int K = a.K, N = a.N, M = a.M;
     const int G = K >> 7;
     const int row_bytes = K >> 1;
     const int col = lane & 15;          // weight row within the tile; token within an A tile
     const int kq = lane >> 4;           // quarter of the group; token quad of a D tile
-    const int row = blockIdx.x * kRowsPerBlock + col;
-    const bool row_ok = row < N;
+    const int row0 = blockIdx.x * kRowsPerBlock;
+    const int rows = N - row0 < kRowsPerBlock ? N - row0 : kRowsPerBlock;
+    // draft: (16 P_hi) * scale / 16; target: 16 (16 P_hi + P_lo) * scale / 256
+    const float fscale = PLANES == 2 ? 0.00390625f : 0.0625f;
+
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hi + static_cast<size_t>(row0) * row_bytes,
+                                                static_cast<unsigned>(rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc((PLANES == 2 ? a.lo : a.hi) + static_cast<size_t>(row0) * row_bytes,
+                                                static_cast<unsigned>(rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + static_cast<size_t>(row0) * G,
+                                                static_cast<unsigned>(rows) * G * 2u);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, static_cast<unsigned>(M) * K);
+    const int voff_w = col * row_bytes + kq * 16;
+    const int voff_s = col * G * 2;
+    int voff_x[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) voff_x[t] = (16 * t + col) * K + kq * 32;
 
     if (GA && !EXPORT) {
-        for (int i = threadIdx.x; i < G * 16 * T; i += kThreads) {
+        for (int i = threadIdx.x; i < G * 16 * T; i += 64 * SPLIT) {
             const int g = i / (16 * T);
             const int t = i - g * 16 * T;
             sact[i] = t < M ? a.xs[static_cast<size_t>(t) * G + g] : 0.0f;
@@ -88,13 +130,28 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs 
         __syncthreads();
     }
 
-    const int g0 = (G * wave) / kWaves;
-    const int g1 = (G * (wave + 1)) / kWaves;
-    const float fscale = PLANES == 2 ? 0.0625f : 1.0f;
-    const size_t roff = static_cast<size_t>(row_ok ? row : 0) * row_bytes + kq * 16;
-    const uint8_t *hrow = a.hi + roff;
-    const uint8_t *lrow = PLANES == 2 ? a.lo + roff : nullptr;
-    const uint16_t *srow = a.scale + static_cast<size_t>(row_ok ? row : 0) * G;
+    // this wave's groups [g_begin, g_end)
+    const int g_begin = G * wave / SPLIT;
+    const int g_end = G * (wave + 1) / SPLIT;
+    const int n_items = g_end - g_begin;
+
+    int iseq = 0;
+    auto issue = [&](VItem<PLANES, T> &x) {
+        const int g = g_begin + iseq;
+        const bool live = iseq < n_items;
+        const int sw = live ? g * 64 : kOOB;
+        x.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, voff_w, sw, kAuxStream));
+        if (PLANES == 2)
+            x.l = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, voff_w, sw, kAuxStream));
+        if (!EXPORT) x.sbits = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, live ? g * 2 : kOOB, 0);
+        const int sx = live ? g * kGroup : kOOB;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            x.x[t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[t], sx, 0));
+            x.x[t][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[t] + 16, sx, 0));
+        }
+        ++iseq;
+    };
 
     float yacc[T][4];
 #pragma unroll
@@ -102,35 +159,18 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs 
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[t][r] = 0.0f;
 
-#pragma unroll 2
-    for (int g = g0; g < g1; ++g) {
-        u32x4 wh = u32x4{0u, 0u, 0u, 0u}, wl = u32x4{0u, 0u, 0u, 0u};
-        float sc = 0.0f;
-        if (row_ok) {
-            wh = load_stream16(hrow + g * 64);
-            if (PLANES == 2) wl = load_stream16(lrow + g * 64);
-            if (!EXPORT) sc = half_bits_to_float(srow[g]) * fscale;
-        }
-        u32x4 av[T][2];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int tok = 16 * t + col;
-            av[t][0] = u32x4{0u, 0u, 0u, 0u};
-            av[t][1] = u32x4{0u, 0u, 0u, 0u};
-            if (tok < M) {
-                const u32x4 *p = reinterpret_cast<const u32x4 *>(
-                    a.xq + static_cast<size_t>(tok) * K + g * kGroup + kq * 32);
-                av[t][0] = p[0];
-                av[t][1] = p[1];
-            }
-        }
+    int cseq = 0;
+    auto consume = [&](const VItem<PLANES, T> &x) {
+        const int g = g_begin + cseq;
+        ++cseq;
         i32x4 bhe, bho, ble, blo;
-        signed16(wh, bhe, bho);
-        if (PLANES == 2) signed16(wl, ble, blo);
+        signed16(x.h, bhe, bho);
+        if (PLANES == 2) signed16(x.l, ble, blo);
+        const float sc = half_bits_to_float(static_cast<uint16_t>(x.sbits)) * fscale;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             i32x4 ae, ao;
-            split_act(av[t][0], av[t][1], ae, ao);
+            split_act(x.x[t][0], x.x[t][1], ae, ao);
             const i32x4 zero = {0, 0, 0, 0};
             i32x4 dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, bhe, zero, 0, 0, 0);
             dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao, bho, dh, 0, 0, 0);
@@ -143,14 +183,14 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tok = 16 * t + 4 * kq + r;
-                    if (tok < M && row_ok) {
-                        const size_t o = (static_cast<size_t>(tok) * N + row) * G + g;
+                    if (tok < M && col < rows) {
+                        const size_t o = (static_cast<size_t>(tok) * N + row0 + col) * G + g;
                         const int ph = dh[r] >> 4;
                         a.p_hi[o] = ph;
                         if (PLANES == 2) {
                             const int pl = dl[r] >> 4;
                             a.p_lo[o] = pl;
-                            a.p8[o] = dh[r] + pl;
+                            a.p8[o] = 16 * ph + pl;
                         }
                     }
                 }
@@ -162,11 +202,23 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs 
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int p = PLANES == 2 ? dh[r] + (dl[r] >> 4) : (dh[r] >> 4);
+                    // draft: 16 P_hi; target: 16 (16 P_hi) + 16 P_lo = 16 P8
+                    const int p = PLANES == 2 ? 16 * dh[r] + dl[r] : dh[r];
                     const float w = GA ? sc * sa[r] : sc;
                     yacc[t][r] += static_cast<float>(p) * w;
                 }
             }
+        }
+    };
+
+    VItem<PLANES, T> ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(ring[d]);
+    for (int base = 0; base < n_items; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (base + d < n_items) consume(ring[d]);     // uniform
+            issue(ring[d]);
         }
     }
 
@@ -177,16 +229,26 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs 
             for (int r = 0; r < 4; ++r) red[((wave * T + t) * 4 + r) * 64 + lane] = yacc[t][r];
         __syncthreads();
         if (wave == 0) {
+            float tok_scale[T][4];
+            if (!GA) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = 16 * t + 4 * kq + r;
+                        tok_scale[t][r] = tok < M ? a.xs[tok] : 0.0f;
+                    }
+            }
 #pragma unroll
             for (int t = 0; t < T; ++t) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float v = red[((0 * T + t) * 4 + r) * 64 + lane];
 #pragma unroll
-                    for (int w = 1; w < kWaves; ++w) v += red[((w * T + t) * 4 + r) * 64 + lane];
+                    for (int w = 1; w < SPLIT; ++w) v += red[((w * T + t) * 4 + r) * 64 + lane];
                     const int tok = 16 * t + 4 * kq + r;
-                    if (tok < M && row_ok)
-                        a.y[static_cast<size_t>(tok) * N + row] = GA ? v : v * a.xs[tok];
+                    if (tok < M && col < rows)
+                        a.y[static_cast<size_t>(tok) * N + row0 + col] = GA ? v : v * tok_scale[t][r];
                 }
             }
         }
@@ -195,10 +257,14 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(const LinearArgs 
 
 typedef void (*VerifyKernel)(const LinearArgs);
 
+constexpr int kSplit = 8;     // waves per 16-row tile
+constexpr int kVerifyItems = 2;
+
 template <int PLANES, int T>
 VerifyKernel pick_mode(bool grouped, bool exporting) {
-    if (exporting) return verify_mfma_kernel<PLANES, T, false, true>;
-    return grouped ? verify_mfma_kernel<PLANES, T, true, false> : verify_mfma_kernel<PLANES, T, false, false>;
+    if (exporting) return verify_mfma_kernel<PLANES, T, false, true, kSplit, kVerifyItems>;
+    return grouped ? verify_mfma_kernel<PLANES, T, true, false, kSplit, kVerifyItems>
+                   : verify_mfma_kernel<PLANES, T, false, false, kSplit, kVerifyItems>;
 }
 
 }  // namespace
@@ -213,9 +279,10 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
         k = T == 1 ? pick_mode<2, 1>(grouped, export_partials) : pick_mode<2, 2>(grouped, export_partials);
     else
         k = T == 1 ? pick_mode<1, 1>(grouped, export_partials) : pick_mode<1, 2>(grouped, export_partials);
+    // the partial-sum exchange [kSplit][T][4][64] and the grouped
+    // activation-scale table [G][16 T]
     const size_t G = a.K / kGroup;
-    const size_t lds = static_cast<size_t>(kWaves) * T * 4 * 64 * sizeof(float) +
-                       (grouped ? G * 16 * T * sizeof(float) : 0);
+    const size_t lds = static_cast<size_t>(kSplit) * T * 4 * 64 * 4 + (grouped ? G * 16 * T * 4 : 0);
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
@@ -226,7 +293,7 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
         if (e != hipSuccess) return e;
     }
     const int blocks = (a.N + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(64 * kSplit), lds, stream, a);
     return hipGetLastError();
 }
 
