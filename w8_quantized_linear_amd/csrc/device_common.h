@@ -26,6 +26,7 @@ enum : int {
     kDppQuadSwap2 = 0x4E,   // quad_perm [2,3,0,1]
     kDppRowRor4 = 0x124,    // rotate right by 4 within each row of 16 lanes
     kDppRowRor8 = 0x128,    // rotate right by 8 within each row of 16 lanes
+    kDppRowHalfMirror = 0x141, // reverse each half-row of 8 lanes
     kDppRowBcast15 = 0x142, // lane 15 of each row to the whole next row
     kDppRowBcast31 = 0x143, // lane 31 to rows 2 and 3
 };

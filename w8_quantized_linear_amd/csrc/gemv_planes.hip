@@ -84,16 +84,37 @@ __device__ __forceinline__ int dot_slot16(const Signed16 &n, const u32x4 a0, con
     return acc;
 }
 
+// Target operands of one 16-byte slot of each plane: one signed byte per
+// column, 16 (hi - 8) + lo in [-128, 127] (the hi nibble xor 8 in the high
+// half, the unsigned lo nibble in the low half), so that one dot product per
+// dword covers both planes: sum q * (16 (hi - 8) + lo) = P8 + 8 sum(q).
+__device__ __forceinline__ Signed16 to_combined16(const u32x4 h, const u32x4 l) {
+    Signed16 n;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const unsigned hx = h[d] ^ 0x88888888u, lw = l[d];
+        n.e[d] = ((hx << 4) & kHighNibbles) | (lw & ~kHighNibbles);
+        n.o[d] = (hx & kHighNibbles) | ((lw >> 4) & ~kHighNibbles);
+    }
+    return n;
+}
+
 template <int M>
 struct GemvLds {
-    static constexpr int kMP = (M + 3) & ~3;   // tokens padded to 4 in the grouped-scale table
-    // codes [M][K] bytes, then either the grouped activation scales [G][kMP]
-    // or (fused per-token quantisation) a [waves][M] scratch for the maxima
-    static size_t bytes(int K, bool grouped_act, bool fused = false, int waves = 16) {
+    static constexpr int kMP = (M + 3) & ~3;   // tokens padded to 4 in the per-group tables
+    // codes [M][K] bytes; then either the grouped activation scales
+    // [G][kMP] or (fused per-token quantisation) a [waves][M] scratch for
+    // the maxima, padded to 16 bytes; then (target) the code sums [G][kMP]
+    __host__ __device__ static size_t scales_bytes(int K, bool grouped_act, bool fused, int waves) {
         const size_t G = K / kGroup;
         size_t tail = grouped_act ? G * kMP * sizeof(float) : 0;
         if (fused && !grouped_act) tail = static_cast<size_t>(waves) * M * sizeof(float);
-        return static_cast<size_t>(M) * K + tail;
+        return (tail + 15) & ~static_cast<size_t>(15);
+    }
+    static size_t bytes(int K, bool grouped_act, bool fused, int waves, bool code_sums) {
+        const size_t G = K / kGroup;
+        return static_cast<size_t>(M) * K + scales_bytes(K, grouped_act, fused, waves) +
+               (code_sums ? G * kMP * sizeof(int) : 0);
     }
 };
 
@@ -163,8 +184,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
     const int C = (slots + 63) >> 6;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // draft: (16 P_hi) * scale / 16; target: 16 (16 P_hi + P_lo) * scale / 256
-    const float fscale = PLANES == 2 ? 0.00390625f : 0.0625f;
+    // draft: (16 P_hi) * scale / 16; target: P8 * scale / 16
+    const float fscale = 0.0625f;
+    constexpr bool kSums = PLANES == 2 && !EXPORT;   // the target's code sums
 
     const unsigned plane_bytes = static_cast<unsigned>(N) * static_cast<unsigned>(row_bytes);
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hi, plane_bytes);
@@ -204,6 +226,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
 
     unsigned char *act = smem;                                                    // [M][2][slots][16]
     float *sact = reinterpret_cast<float *>(smem + static_cast<size_t>(M) * K);   // [G][kMP] (GA)
+    int *qsum = reinterpret_cast<int *>(smem + static_cast<size_t>(M) * K +
+                                        GemvLds<M>::scales_bytes(K, GA, FUSED, WAVES));   // [G][kMP]
     const int nb16 = K >> 4;
     float tok_scale[M];
     Item<PLANES> ring[D];
@@ -239,13 +263,27 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(ring[d]);
 
-        // 2) stage the codes into LDS while the ring is in flight
+        // 2) stage the codes into LDS while the ring is in flight; for the
+        //    target, also the per-(group, token) code sums (the eight blocks of
+        //    a group are eight consecutive lanes)
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int t = 0; t < kPB; ++t) {
                 const int j = threadIdx.x + t * kThreads;
                 if (j < nb16) stage_block(act + static_cast<size_t>(m) * K, j, row_bytes, pre[m][t]);
+                if (kSums) {
+                    int cs = 0;
+                    if (j < nb16) {
+                        cs = sdot4(pre[m][t].x, 0x01010101u, cs);
+                        cs = sdot4(pre[m][t].y, 0x01010101u, cs);
+                        cs = sdot4(pre[m][t].z, 0x01010101u, cs);
+                        cs = sdot4(pre[m][t].w, 0x01010101u, cs);
+                    }
+                    cs = quad_sum_i32(cs);
+                    cs += dpp_i32<kDppRowHalfMirror>(cs);
+                    if (j < nb16 && (j & 7) == 0) qsum[(j >> 3) * kMP + m] = cs;
+                }
             }
         if (GA) {
 #pragma unroll
@@ -333,15 +371,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
             const int u = threadIdx.x + k * kThreads;
+            int cs = 0;
             if (u < nunit) {
                 unsigned y[8];
                 quant_codes<8>(xf[k], us[k], ur[k], y);
                 unsigned char *dst = act + ((u >> 1) & 1) * row_bytes + (u >> 2) * 16 + (u & 1) * 8;
                 *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_low_bytes(y[0], y[2], y[4], y[6]),
                                                              pack_low_bytes(y[1], y[3], y[5], y[7]));
+                const unsigned c0 = pack_low_bytes(y[0], y[1], y[2], y[3]);
+                const unsigned c1 = pack_low_bytes(y[4], y[5], y[6], y[7]);
                 if (blockIdx.x == 0)
-                    *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(u) * 8) =
-                        make_uint2(pack_low_bytes(y[0], y[1], y[2], y[3]), pack_low_bytes(y[4], y[5], y[6], y[7]));
+                    *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(u) * 8) = make_uint2(c0, c1);
+                if (kSums) cs = sdot4(c1, 0x01010101u, sdot4(c0, 0x01010101u, 0));
+            }
+            if (kSums) {
+                // a group is 16 units = one row of 16 lanes
+                cs = quad_sum_i32(cs);
+                cs += dpp_i32<kDppRowRor4>(cs);
+                cs += dpp_i32<kDppRowRor8>(cs);
+                if (u < nunit && (u & 15) == 0) qsum[(u >> 4) * kMP] = cs;
             }
         }
         __syncthreads();
@@ -365,14 +413,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
         const int ss = valid ? s : 0;
         const int g = ss >> 2;
         const float sc = half_bits_to_float(static_cast<uint16_t>(x.sbits)) * fscale;
-        const Signed16 nh = to_signed16(x.h);
-        Signed16 nl;
-        if (PLANES == 2) nl = to_signed16(x.l);
+        if (EXPORT) {
+            // the planes' partials separately
+            const Signed16 nh = to_signed16(x.h);
+            Signed16 nl;
+            if (PLANES == 2) nl = to_signed16(x.l);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const u32x4 a0 = act4[m * tok4 + ss];
-            const u32x4 a1 = act4[m * tok4 + half4 + ss];
-            if (EXPORT) {
+            for (int m = 0; m < M; ++m) {
+                const u32x4 a0 = act4[m * tok4 + ss];
+                const u32x4 a1 = act4[m * tok4 + half4 + ss];
                 const int ph = quad_sum_i32(dot_slot16(nh, a0, a1)) >> 4;
                 int pl = 0;
                 if (PLANES == 2) pl = quad_sum_i32(dot_slot16(nl, a0, a1)) >> 4;
@@ -384,11 +433,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
                         a.p8[o] = 16 * ph + pl;
                     }
                 }
-            } else {
-                // draft: 16 P_hi; target: 16 (16 P_hi) + 16 P_lo = 16 P8
-                int p = dot_slot16(nh, a0, a1);
-                if (PLANES == 2) p = 16 * p + dot_slot16(nl, a0, a1);
-                p = quad_sum_i32(p);
+            }
+        } else {
+            // draft: 16 P_hi; target: P8 = sum q (16 (hi - 8) + lo) - 8 sum q
+            const Signed16 n = PLANES == 2 ? to_combined16(x.h, x.l) : to_signed16(x.h);
+            int cs[kMP];
+            if (PLANES == 2) {
+#pragma unroll
+                for (int i = 0; i < kMP; i += 4) {
+                    const i32x4 v = *reinterpret_cast<const i32x4 *>(qsum + g * kMP + i);
+                    cs[i] = v.x; cs[i + 1] = v.y; cs[i + 2] = v.z; cs[i + 3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const u32x4 a0 = act4[m * tok4 + ss];
+                const u32x4 a1 = act4[m * tok4 + half4 + ss];
+                int p = quad_sum_i32(dot_slot16(n, a0, a1));
+                if (PLANES == 2) p -= 8 * cs[m];
                 const float w = GA ? sc * sact[g * kMP + m] : sc;
                 acc[m] += valid ? static_cast<float>(p) * w : 0.0f;
             }
@@ -474,15 +536,15 @@ GemvKernel pick_fused(int K, bool grouped) {
                    : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped) : pick_fused_xu<PLANES, 4>(grouped);
 }
 
-size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused, int waves) {
+size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused, int waves, bool sums) {
     switch (M) {
-        case 1: return GemvLds<1>::bytes(K, grouped, fused, waves);
-        case 2: return GemvLds<2>::bytes(K, grouped, fused, waves);
-        case 3: return GemvLds<3>::bytes(K, grouped, fused, waves);
-        case 4: return GemvLds<4>::bytes(K, grouped, fused, waves);
-        case 5: return GemvLds<5>::bytes(K, grouped, fused, waves);
-        case 6: return GemvLds<6>::bytes(K, grouped, fused, waves);
-        case 7: return GemvLds<7>::bytes(K, grouped, fused, waves);
+        case 1: return GemvLds<1>::bytes(K, grouped, fused, waves, sums);
+        case 2: return GemvLds<2>::bytes(K, grouped, fused, waves, sums);
+        case 3: return GemvLds<3>::bytes(K, grouped, fused, waves, sums);
+        case 4: return GemvLds<4>::bytes(K, grouped, fused, waves, sums);
+        case 5: return GemvLds<5>::bytes(K, grouped, fused, waves, sums);
+        case 6: return GemvLds<6>::bytes(K, grouped, fused, waves, sums);
+        case 7: return GemvLds<7>::bytes(K, grouped, fused, waves, sums);
         default: return 0;
     }
 }
@@ -500,7 +562,7 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
     const int waves = fused ? kFusedWaves : kGemvWaves;
-    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused, waves);
+    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused, waves, target && !exporting);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
     if (lds > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
