@@ -14,12 +14,6 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
-// 16 bytes that are read exactly once per call: non-temporal, so the plane
-// stream does not evict the activations and scales from the caches.
-__device__ __forceinline__ u32x4 load_stream16(const uint8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
 // DPP lane moves (gfx9 encodings of the dpp_ctrl field).
 enum : int {
     kDppQuadSwap1 = 0xB1,   // quad_perm [1,0,3,2]
@@ -54,23 +48,6 @@ __device__ __forceinline__ float dpp_f32_masked(float v) {
 __device__ __forceinline__ int quad_sum_i32(int v) {
     v += dpp_i32<kDppQuadSwap1>(v);
     v += dpp_i32<kDppQuadSwap2>(v);
-    return v;
-}
-
-// Sum over the 16 quads of a wave of a value that is uniform within each quad.
-// The association order is fixed, so the result is deterministic. Lane 0
-// holds the sum (all lanes do, with lane-dependent association).
-__device__ __forceinline__ float sum_over_quads_f32(float v) {
-    v += dpp_f32<kDppRowRor4>(v);
-    v += dpp_f32<kDppRowRor8>(v);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
 

@@ -7,7 +7,9 @@
 //
 // The work is a few KiB per token and latency-bound: one workgroup per token
 // holds its whole row in registers (one HBM round trip), reduces |x| with
-// wave shuffles and writes packed codes with 4-byte stores.
+// DPP and LDS and writes packed codes with 4-byte stores. (Measured on
+// MI355X: 512-thread workgroups finish sooner than 1024-thread ones, and
+// splitting a row's quantisation over several workgroups does not pay.)
 #include "bitnest_internal.h"
 #include "device_common.h"
 
@@ -15,9 +17,9 @@ namespace bitnest {
 namespace {
 
 constexpr int kQuantThreads = 256;     // grouped kernel
-constexpr int kTokenThreads = 1024;    // per-token kernel
+constexpr int kTokenThreads = 512;     // per-token kernel
 
-// One token per workgroup of 1024 threads; each thread keeps up to NV float4
+// One token per workgroup of 512 threads; each thread keeps up to NV float4
 // of the row in registers. All loads are issued unconditionally (clamped
 // index) before any use, so the row costs one memory round trip.
 template <int NV>
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kTokenThreads) void quant_token_kernel(
         const int idx = threadIdx.x + i * kTokenThreads;
         if (idx < n4) amax = fmaxf(amax, absmax4(v[i]));
     }
-    amax = wave_max_f32(amax);
+    amax = wave_max_dpp_f32(amax);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
     __syncthreads();
     amax = part[0];
@@ -89,14 +91,19 @@ hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t 
                            total, xq, xs);
     } else {
         const int nv = (K / 4 + kTokenThreads - 1) / kTokenThreads;   // float4 per thread
-        if (nv <= 1)
-            hipLaunchKernelGGL(quant_token_kernel<1>, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
-        else if (nv <= 2)
-            hipLaunchKernelGGL(quant_token_kernel<2>, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
-        else if (nv <= 4)
-            hipLaunchKernelGGL(quant_token_kernel<4>, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
-        else
-            return hipErrorInvalidValue;   // K > kMaxK: rejected by the ABI before this point
+        void (*k)(const float *, int, int8_t *, float *);
+        switch (nv) {
+            case 1: k = quant_token_kernel<1>; break;
+            case 2: k = quant_token_kernel<2>; break;
+            case 3: k = quant_token_kernel<3>; break;
+            case 4: k = quant_token_kernel<4>; break;
+            case 5: k = quant_token_kernel<5>; break;
+            case 6: k = quant_token_kernel<6>; break;
+            case 7: k = quant_token_kernel<7>; break;
+            case 8: k = quant_token_kernel<8>; break;
+            default: return hipErrorInvalidValue;   // K > kMaxK: rejected by the ABI before this point
+        }
+        hipLaunchKernelGGL(k, dim3(M), dim3(kTokenThreads), 0, stream, x, K, xq, xs);
     }
     return hipGetLastError();
 }
