@@ -3,7 +3,8 @@
 // o_proj). The rule, which the pages leave open and the public header states:
 //   s = amax / 127 (IEEE fp32 division), q = 0 if s == 0, otherwise
 //   q = clamp(round_half_even(x / s), -127, 127) with x / s an IEEE fp32
-//   division (quant_code_r in device_common.h, shared with the fused GEMV).
+//   division (computed by quant_codes in device_common.h, shared with the
+//   fused GEMV).
 //
 // The work is a few KiB per token and latency-bound: one workgroup per token
 // holds its whole row in registers (one HBM round trip), reduces |x| with
