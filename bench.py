@@ -52,6 +52,8 @@ def parse_args(argv=None):
                         "reference dispatch for hardware byte counters)")
     p.add_argument("--verify-batches", default="8,16,32",
                    help="token counts for the batched-verify (matrix-core) layer timing; empty to skip")
+    p.add_argument("--no-per-linear", dest="per_linear", action="store_false", default=True,
+                   help="skip the per-linear timing (each shape on its own, draft/target M=1, target M=4)")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -189,6 +191,65 @@ def gemv_kernel_timing(stack, bn, steps):
 
 
 INT8_DENSE_PEAK_OPS = 5.0e15       # MI355X dense int8 matrix-core peak, ops/s
+
+
+def per_linear(stack, bn, reps=5):
+    """Each linear shape on its own: one launch per layer of the stack (cold
+    weights, a different layer each launch) replayed from a HIP graph and
+    timed with HIP events; us per launch and plane GB/s with its fraction of
+    the 8 TB/s peak. Modes: draft M=1 and target M=1 (the fused call, one
+    launch), target M=4 (the linear on ready codes; its separate
+    quantisation launch is timed on its own as quant_M4)."""
+    import torch
+    out = {}
+    L = stack.layers
+
+    def timed(fn, n):
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3 / n)
+        return sorted(ts)[len(ts) // 2]
+
+    for mode in ("draft_M1", "target_M1", "target_M4", "quant_M4"):
+        res = {}
+        for i, (name, N, K, g) in enumerate(stack.linears):
+            M = 4 if mode.endswith("M4") else 1
+            xq, xs, y = stack.buf[(M, i)]
+
+            def fn(i=i, g=g, xq=xq, xs=xs, y=y):
+                for l in range(L):
+                    w = stack.w[l][i]
+                    if mode == "draft_M1":
+                        bn.bitnest_quant_linear_draft(stack.x_draft[0][l][i], w.hi, w.scale, g, y=y, xq=xq, xs=xs)
+                    elif mode == "target_M1":
+                        bn.bitnest_quant_linear_target(stack.x_draft[0][l][i], w.hi, w.lo, w.scale, g,
+                                                       y=y, xq=xq, xs=xs)
+                    elif mode == "target_M4":
+                        bn.bitnest_linear_target(xq, xs, w.hi, w.lo, w.scale, g, y=y)
+                    else:
+                        bn.bitnest_quant_act(stack.x_verify[l][i], g, xq=xq, xs=xs)
+            if mode == "target_M4":
+                bn.bitnest_quant_act(stack.x_verify[0][i], g, xq=xq, xs=xs)
+            t = timed(fn, L)
+            entry = {"us": round(t * 1e6, 3)}
+            if mode != "quant_M4":
+                plane = N * K // 2 * (1 if mode == "draft_M1" else 2)
+                gbs = plane / t / 1e9
+                entry.update({"plane_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+            res[name] = entry
+        out[mode] = res
+        log("per linear %s: %s" % (mode, ", ".join("%s %.2f us%s" % (k, v["us"], (" %.0f GB/s" % v["plane_GBps"])
+                                                                      if "plane_GBps" in v else "")
+                                                     for k, v in res.items())))
+    return out
 
 
 def batched_verify(stack, bn, batches, reps=20):
@@ -355,6 +416,8 @@ def main(argv=None):
                     "algorithmic_bytes_per_launch": int(per_launch_bytes)}
         log("GEMV: %.3f us per launch (events), %.1f GB/s algorithmic" % (t_gemv * 1e6, achieved))
 
+    linears = per_linear(stack, bn) if args.per_linear else None
+
     verify = None
     batches = [int(v) for v in args.verify_batches.split(",") if v.strip()]
     if batches:
@@ -386,6 +449,7 @@ def main(argv=None):
                    "replay": "hip_graph"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
+        "per_linear": linears,
         "batched_verify": verify,
         "cpu_baseline": cpu,
     }

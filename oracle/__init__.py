@@ -53,9 +53,10 @@ def _load():
         lib.oracle_partials.argtypes = [P, P, P, I, I, I, P, P, P, I]
         lib.oracle_dequant.argtypes = [I, P, P, P, I, I, P]
         lib.oracle_linear.argtypes = [I, P, P, I, P, P, P, I, I, I, P, I]
+        lib.oracle_hadamard_rotate.argtypes = [P, I, I, I, P]
         lib.oracle_max_threads.argtypes = []
         for f in ("oracle_unpack_plane", "oracle_quant_act", "oracle_partials",
-                  "oracle_dequant", "oracle_linear", "oracle_max_threads"):
+                  "oracle_dequant", "oracle_linear", "oracle_hadamard_rotate", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -176,3 +177,23 @@ def linear(q: np.ndarray, xs: np.ndarray, hi: np.ndarray, scale: np.ndarray,
                                  _ptr(lo), _ptr(scale), M, N, K, _ptr(y), threads or max_threads()),
            "linear")
     return y
+
+
+def hadamard_rotate(x: np.ndarray, block: int) -> np.ndarray:
+    """fp32 [M, K] -> fp32 [M, K]: each token's blocks of ``block`` columns
+    times the normalised Sylvester-Hadamard matrix (the R4 reading in the C
+    file's header: fp32 fast transform, stages 1, 2, ..., block/2, then one
+    multiply by the fp32 value nearest 1/sqrt(block))."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_hadamard_rotate(_ptr(x), M, K, int(block), _ptr(y)), "hadamard_rotate")
+    return y
+
+
+def hadamard_quant_act(x: np.ndarray, block: int):
+    """The down_proj input path: R4 rotation, then per-token int8
+    quantisation. Returns (codes int8 [M, K], scales fp32 [M], rotated fp32 [M, K])."""
+    r = hadamard_rotate(x, block)
+    q, s = quant_act(r, 0)
+    return q, s, r

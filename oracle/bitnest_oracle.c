@@ -33,6 +33,22 @@
  *        P8 = 16 * P_hi + P_lo
  *    (the integer part of the target formula before the scale / 16).
  *
+ *  - Online rotation of the down_proj input: same recipe table, row
+ *    "Rotation" (an online Hadamard, R4, on the down_proj inputs; the R4
+ *    matrices ship in aux.safetensors, entry of section "Files", which is not
+ *    available, and the pages do not say how they are built). The reading
+ *    used here: R4 is block-diagonal, every block the normalised
+ *    Sylvester-Hadamard matrix H_b / sqrt(b) of order b (a power of two
+ *    dividing K; 512 for the Llama-3-8B down_proj, K = 14336 = 28 x 512),
+ *    applied to each token before its per-token quantisation:
+ *        y[m, blk] = (H_b x[m, blk]) * r_b,   r_b = the fp32 value nearest 1/sqrt(b),
+ *    with H_b x computed in fp32 by the iterative fast Walsh-Hadamard
+ *    transform, stages h = 1, 2, 4, ..., b/2 in that order, each stage
+ *    replacing every pair (a, c) = (z[i], z[i + h]) whose index i has bit h
+ *    clear by (a + c, a - c), then one fp32 multiply by r_b per element.
+ *    Fixing the stage order and the single multiply defines the rotated fp32
+ *    values, and therefore their int8 codes, to the bit.
+ *
  * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 and fp64
  * operation is the IEEE operation written.
  */
@@ -223,6 +239,33 @@ int oracle_linear(int mode, const int8_t *q, const float *xs, int act_group,
                 acc += xhat * weight_at(mode, hr, lr, sr, k);
             }
             y64[(size_t)m * N + n] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The R4 rotation reading stated at the top: every token's K columns in
+ * blocks of `block` (a power of two, 2 <= block <= K, K % block == 0). */
+int oracle_hadamard_rotate(const float *x, int M, int K, int block, float *y)
+{
+    if (!x || !y || M < 0 || K <= 0 || block < 2 || block > K || K % block) return ORACLE_EINVAL;
+    if (block & (block - 1)) return ORACLE_EINVAL;
+    if (fegetround() != FE_TONEAREST) return ORACLE_EINVAL;
+    const float rb = (float)(1.0 / sqrt((double)block));
+    for (int m = 0; m < M; ++m) {
+        for (int b0 = 0; b0 < K; b0 += block) {
+            float *z = y + (size_t)m * K + b0;
+            const float *xr = x + (size_t)m * K + b0;
+            for (int i = 0; i < block; ++i) z[i] = xr[i];
+            for (int h = 1; h < block; h *= 2) {
+                for (int i = 0; i < block; ++i) {
+                    if (i & h) continue;
+                    float a = z[i], c = z[i + h];
+                    z[i] = a + c;
+                    z[i + h] = a - c;
+                }
+            }
+            for (int i = 0; i < block; ++i) z[i] = z[i] * rb;
         }
     }
     return ORACLE_OK;

@@ -393,3 +393,109 @@ def test_oracle_rejects_bad_shapes():
         oracle.unpack_plane(np.zeros((2, 3), np.uint8), 4)
     with pytest.raises(oracle.OracleError):
         oracle.quant_act(np.zeros((1, 100), np.float32), act_group=GROUP)
+
+
+# --------------------------------------------------------------------------- R4 rotation (down_proj input)
+# Reading (model card, recipe table row "Rotation": an online Hadamard, R4, on
+# the down_proj inputs; the matrices themselves are not given): block-diagonal
+# normalised Sylvester-Hadamard H_b / sqrt(b), fp32 fast transform, one
+# multiply by the fp32 value nearest 1/sqrt(b).
+
+def _f32_bits(v):
+    return int(np.array([v], np.float32).view(np.uint32)[0])
+
+
+def _sylvester(b):
+    """H_b by the closed form H[i][j] = (-1)^popcount(i & j) (int64)."""
+    i = np.arange(b)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+def test_hadamard_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "hadamard.json")))
+    for case in g["cases"]:
+        b = case["block"]
+        x = np.array([case["x"]], np.float32)
+        y = oracle.hadamard_rotate(x, b)
+        if "y" in case:
+            assert np.array_equal(y[0], np.array(case["y"], np.float32))
+        r = np.array([int(case.get("r_bits", "0x3f000000"), 16)], np.uint32).view(np.float32)[0]
+        want = (np.array(case["Hx"], np.float32) * r).astype(np.float32)
+        assert np.array_equal(y[0], want), (b, y, want)
+    # the normalisation constant for the Llama-3-8B block
+    e0 = np.zeros((1, 512), np.float32)
+    e0[0, 0] = 1.0
+    assert _f32_bits(oracle.hadamard_rotate(e0, 512)[0, 0]) == int(g["r_512_bits"], 16)
+
+
+@pytest.mark.parametrize("b", [2, 8, 16, 64, 512])
+def test_hadamard_columns_closed_form(b):
+    # the transform of a one-hot vector e_j is column j of H_b times r_b, exactly
+    H = _sylvester(b)
+    r = oracle.hadamard_rotate(np.eye(1, b, 0, dtype=np.float32), b)[0, 0]
+    js = range(b) if b <= 64 else [0, 1, 2, 3, 5, 64, 255, 256, 300, 511]
+    for j in js:
+        e = np.zeros((1, b), np.float32)
+        e[0, j] = 1.0
+        y = oracle.hadamard_rotate(e, b)[0]
+        assert np.array_equal(y, (H[:, j] * r).astype(np.float32)), j
+
+
+@pytest.mark.parametrize("b", [2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 4096])
+def test_hadamard_constant_is_nearest_fp32(b):
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    r = oracle.hadamard_rotate(np.eye(1, b, 0, dtype=np.float32), b)[0, 0]
+    exact = Decimal(1) / Decimal(b).sqrt()
+    bits = _f32_bits(r)
+    err = abs(Decimal(float(r)) - exact)
+    for nb in (bits - 1, bits + 1):
+        other = float(np.array([nb], np.uint32).view(np.float32)[0])
+        assert err <= abs(Decimal(other) - exact)
+
+
+@pytest.mark.parametrize("b", [4, 16, 64, 256])
+def test_hadamard_involution_exact(b):
+    # for even log2(b) the constant is a power of two, so small integer inputs
+    # stay exact: R applied twice is the identity (H_b^2 = b I)
+    rng = np.random.default_rng(b)
+    x = rng.integers(-8, 9, size=(3, 4 * b)).astype(np.float32)
+    y = oracle.hadamard_rotate(oracle.hadamard_rotate(x, b), b)
+    assert np.array_equal(y, x)
+
+
+def test_hadamard_dense_fp64_and_norm():
+    # Llama-3-8B down_proj input: 28 blocks of 512, with outlier channels
+    b, K = 512, 14336
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, K)).astype(np.float32)
+    x[:, rng.choice(K, 72, replace=False)] *= 20
+    y = oracle.hadamard_rotate(x, b).astype(np.float64)
+    H = _sylvester(b).astype(np.float64) / np.sqrt(b)
+    ref = np.concatenate([x[:, i:i + b].astype(np.float64) @ H.T for i in range(0, K, b)], axis=1)
+    u = 2.0 ** -24
+    for i in range(0, K, b):
+        bound = (np.log2(b) + 2) * u * np.abs(x[:, i:i + b]).sum(axis=1, keepdims=True).astype(np.float64) / np.sqrt(b)
+        assert np.all(np.abs(y[:, i:i + b] - ref[:, i:i + b]) <= bound)
+        nx = np.linalg.norm(x[:, i:i + b].astype(np.float64), axis=1)
+        ny = np.linalg.norm(y[:, i:i + b], axis=1)
+        assert np.allclose(nx, ny, rtol=1e-5)
+
+
+def test_hadamard_blocks_independent_and_scaling():
+    b, K = 512, 14336
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    y = oracle.hadamard_rotate(x, b)
+    for i in (0, 512, 13824):
+        assert np.array_equal(y[:, i:i + b], oracle.hadamard_rotate(np.ascontiguousarray(x[:, i:i + b]), b))
+    assert np.array_equal(oracle.hadamard_rotate(x * 4, b), y * 4)
+    assert np.array_equal(oracle.hadamard_rotate(-x, b), -y)
+
+
+def test_hadamard_bad_args():
+    x = np.zeros((1, 96), np.float32)
+    for b in (0, 1, 3, 12, 64, 128):
+        with pytest.raises(oracle.OracleError):
+            oracle.hadamard_rotate(x, b)

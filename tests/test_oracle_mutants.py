@@ -37,6 +37,13 @@ MUTANTS = {
                               "double sa = act_group ? (double)xs[(size_t)m * G]"),
     "half exponent bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     "plane row stride": ("const uint8_t *hr = hi + (size_t)n * (K / 2);", "const uint8_t *hr = hi + (size_t)n * (K / 4);"),
+    "hadamard difference reversed": ("z[i + h] = a - c;", "z[i + h] = c - a;"),
+    "hadamard difference dropped": ("z[i + h] = a - c;", "z[i + h] = a + c;"),
+    "hadamard normalisation dropped": ("z[i] = z[i] * rb;", "z[i] = z[i];"),
+    "hadamard normalisation 1/sqrt(b/2)": ("(float)(1.0 / sqrt((double)block))", "(float)(1.0 / sqrt((double)block / 2))"),
+    "hadamard first stage skipped": ("for (int h = 1; h < block; h *= 2)", "for (int h = 2; h < block; h *= 2)"),
+    "hadamard last stage skipped": ("for (int h = 1; h < block; h *= 2)", "for (int h = 1; h < block / 2; h *= 2)"),
+    "hadamard input block offset": ("const float *xr = x + (size_t)m * K + b0;", "const float *xr = x + (size_t)m * K;"),
 }
 
 
