@@ -50,11 +50,12 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 1
+#define BITNEST_ABI_VERSION 2
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
 #define BITNEST_MAX_PLANE_BYTES 2147483647LL  /* largest N * K / 2 (bytes of one plane) */
+#define BITNEST_MAX_ROT_BLOCK 512 /* largest rotation block of the R4 calls */
 
 typedef enum bitnest_status {
     BITNEST_OK = 0,
@@ -142,6 +143,56 @@ bitnest_status bitnest_quant_linear_target(const float *x, int act_group,
                                            const uint16_t *scale,
                                            float *y, int8_t *xq, float *xs,
                                            int M, int N, int K, void *stream);
+
+/*
+ * The down_proj input path with its online rotation (model card, recipe table
+ * row "Rotation": an online Hadamard, R4, on the down_proj inputs; the R4
+ * matrices ship in aux.safetensors, which the pages do not reproduce, and
+ * their construction is not stated). This library's reading: R4 is block-
+ * diagonal, every block of `block` columns the normalised Sylvester-Hadamard
+ * matrix H_b / sqrt(b), H_b[i][j] = (-1)^popcount(i & j). Per token m and
+ * block, in fp32:
+ *     z = H_b x[m, blk]  by the fast transform, stages h = 1, 2, 4, ..., b/2
+ *                        in that order, each replacing the pair
+ *                        (a, c) = (z[i], z[i + h]) (bit h of i clear) by
+ *                        (a + c, a - c)
+ *     r[m, blk] = z * r_b  one fp32 multiply, r_b = the fp32 value nearest
+ *                        1/sqrt(b)
+ * then the quantisation rule of bitnest_quant_act with act_group 0 (one
+ * scale per token) on r. The stage order and the single multiply make the
+ * rotated values, and so the codes, exact functions of x.
+ *
+ *   x      fp32 [M, K], finite values
+ *   block  power of two, 2 <= block <= BITNEST_MAX_ROT_BLOCK, K % block == 0
+ *          (512 for the Llama-3-8B down_proj: K = 14336 = 28 x 512);
+ *          otherwise BITNEST_EINVAL
+ *   xq     int8 [M, K] codes, xs fp32 [M] scales: written
+ *   xr     fp32 [M, K]: the rotated values r, written if not NULL
+ * The weights of the linear that consumes these codes must carry the same
+ * rotation (applied offline), as the package's down_proj weights do.
+ */
+bitnest_status bitnest_hadamard_quant_act(const float *x, int M, int K, int block,
+                                          int8_t *xq, float *xs, float *xr, void *stream);
+
+/*
+ * Rotation and quantisation fused with the draft / target linear: the same
+ * codes, scales and y, bit for bit, as bitnest_hadamard_quant_act (xr NULL)
+ * followed by bitnest_linear_draft / bitnest_linear_target with act_group 0.
+ * For one token (M == 1) each workgroup rotates and quantises x itself and
+ * the whole linear is one launch; otherwise the call makes two launches.
+ * Arguments as for bitnest_quant_linear_draft / _target, with `block` in
+ * place of act_group.
+ */
+bitnest_status bitnest_hadamard_quant_linear_draft(const float *x, int block,
+                                                   const uint8_t *hi, const uint16_t *scale,
+                                                   float *y, int8_t *xq, float *xs,
+                                                   int M, int N, int K, void *stream);
+
+bitnest_status bitnest_hadamard_quant_linear_target(const float *x, int block,
+                                                    const uint8_t *hi, const uint8_t *lo,
+                                                    const uint16_t *scale,
+                                                    float *y, int8_t *xq, float *xs,
+                                                    int M, int N, int K, void *stream);
 
 /*
  * The integer partials of the draft and target calls above, from the same kernels' integer

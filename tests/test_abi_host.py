@@ -23,7 +23,9 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
-              "bitnest_linear_partials", "bitnest_status_string", "bitnest_abi_version"):
+              "bitnest_linear_partials", "bitnest_status_string", "bitnest_abi_version",
+              "bitnest_quant_linear_draft", "bitnest_quant_linear_target", "bitnest_hadamard_quant_act",
+              "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target"):
         assert n in names
 
 
@@ -40,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bn.bitnest_abi_version() == 1
+    assert bn.bitnest_abi_version() == 2
     seen = set()
     for s in range(5):
         txt = bn.bitnest_status_string(s)
@@ -76,6 +78,18 @@ def _t(xq, xs, g, hi, lo, sc, y, M, N, K):
 
 def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     return bn.lib().bitnest_linear_partials(xq, hi, lo, ph, pl, p8, M, N, K, None)
+
+
+def _h(x, M, K, b, xq, xs, xr):
+    return bn.lib().bitnest_hadamard_quant_act(x, M, K, b, xq, xs, xr, None)
+
+
+def _hd(x, b, hi, sc, y, xq, xs, M, N, K):
+    return bn.lib().bitnest_hadamard_quant_linear_draft(x, b, hi, sc, y, xq, xs, M, N, K, None)
+
+
+def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
+    return bn.lib().bitnest_hadamard_quant_linear_target(x, b, hi, lo, sc, y, xq, xs, M, N, K, None)
 
 
 @pytest.mark.parametrize("call,status", [
@@ -133,6 +147,28 @@ def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     (lambda: _t(NUL, NUL, 0, NUL, NUL, NUL, NUL, 3, 0, 128), bn.OK),
     (lambda: _p(NUL, NUL, NUL, NUL, NUL, NUL, 0, 0, 128), bn.OK),
     (lambda: _d(NUL, NUL, 0, NUL, NUL, NUL, 0, 8, 100), bn.EINVAL),
+    # R4 rotation + quantisation: block a power of two in [2, 512] dividing K
+    (lambda: _h(A, 1, 512, 0, B, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 512, 1, B, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 512, 96, B, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 512, 1024, B, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 384, 256, B, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 100, 4, B, C, NUL), bn.EINVAL),
+    (lambda: _h(NUL, 1, 512, 512, B, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 512, 512, NUL, C, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 512, 512, B, NUL, NUL), bn.EINVAL),
+    (lambda: _h(A, 1, 512, 512, B, C, MIS), bn.EALIGN),
+    (lambda: _h(MIS, 1, 512, 512, B, C, NUL), bn.EALIGN),
+    (lambda: _h(A, 1, 16384 + 512, 512, B, C, NUL), bn.EUNSUPPORTED),
+    (lambda: _h(NUL, 0, 512, 512, NUL, NUL, NUL), bn.OK),
+    (lambda: _hd(A, 0, B, C, D, E, F, 1, 8, 512), bn.EINVAL),
+    (lambda: _hd(A, 3, B, C, D, E, F, 1, 8, 512), bn.EINVAL),
+    (lambda: _hd(A, 512, B, C, D, E, F, 1, 8, 640), bn.EINVAL),
+    (lambda: _hd(A, 512, NUL, C, D, E, F, 1, 8, 512), bn.EINVAL),
+    (lambda: _hd(A, 512, B, C, D, E, F, 33, 8, 512), bn.EUNSUPPORTED),
+    (lambda: _hd(NUL, 512, NUL, NUL, NUL, NUL, NUL, 0, 8, 512), bn.OK),
+    (lambda: _ht(A, 512, B, NUL, C, D, E, F, 1, 8, 512), bn.EINVAL),
+    (lambda: _ht(A, 512, B, MIS, C, D, E, F, 1, 8, 512), bn.EALIGN),
 ])
 def test_host_validation(call, status):
     assert call() == status

@@ -20,11 +20,13 @@ __all__ = [
     "bitnest_abi_version", "bitnest_status_string", "bitnest_quant_act",
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
     "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
+    "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
 ]
 
 GROUP = 128
 MAX_M = 32
 MAX_K = 16384
+MAX_ROT_BLOCK = 512
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libbitnest.so")
@@ -60,8 +62,13 @@ def lib() -> ctypes.CDLL:
         L.bitnest_linear_partials.argtypes = [P, P, P, P, P, P, I, I, I, P]
         L.bitnest_quant_linear_draft.argtypes = [P, I, P, P, P, P, P, I, I, I, P]
         L.bitnest_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
+        L.bitnest_hadamard_quant_act.argtypes = [P, I, I, I, P, P, P, P]
+        L.bitnest_hadamard_quant_linear_draft.argtypes = [P, I, P, P, P, P, P, I, I, I, P]
+        L.bitnest_hadamard_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
-                  "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target"):
+                  "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
+                  "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
+                  "bitnest_hadamard_quant_linear_target"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -187,7 +194,32 @@ def bitnest_linear_partials(xq: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor
     return p_hi if lo is None else (p_hi, p_lo, p8)
 
 
-def _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, what):
+def bitnest_hadamard_quant_act(x: torch.Tensor, block: int, xq: torch.Tensor | None = None,
+                               xs: torch.Tensor | None = None, xr: torch.Tensor | None = None,
+                               rotated: bool = False):
+    """R4 rotation (blocks of ``block`` columns) then per-token quantisation:
+    x fp32 [M, K] -> (xq int8 [M, K], xs fp32 [M]), plus the rotated fp32
+    [M, K] as a third value when ``rotated`` (or ``xr``) is given."""
+    _need(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if xr is None and rotated:
+        xr = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _need(xq, "xq", torch.int8, (M, K))
+    _need(xs, "xs", torch.float32, (M,))
+    if xr is not None:
+        _need(xr, "xr", torch.float32, (M, K))
+    _call(lib().bitnest_hadamard_quant_act(_p(x), M, K, int(block), _p(xq), _p(xs), _p(xr), _stream(x)),
+          "bitnest_hadamard_quant_act")
+    return (xq, xs) if xr is None else (xq, xs, xr)
+
+
+def _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, what, block=0):
     _need(x, "x", torch.float32)
     if x.dim() != 2:
         raise ValueError("x must be [M, K]")
@@ -209,7 +241,14 @@ def _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, what):
     _need(y, "y", torch.float32, (M, N))
     _need(xq, "xq", torch.int8, (M, K))
     _need(xs, "xs", torch.float32, (M,) if act_group == 0 else (M, K // GROUP))
-    if lo is None:
+    if block:
+        if lo is None:
+            st = lib().bitnest_hadamard_quant_linear_draft(_p(x), int(block), _p(hi), _p(scale), _p(y), _p(xq),
+                                                           _p(xs), M, N, K, _stream(x))
+        else:
+            st = lib().bitnest_hadamard_quant_linear_target(_p(x), int(block), _p(hi), _p(lo), _p(scale), _p(y),
+                                                            _p(xq), _p(xs), M, N, K, _stream(x))
+    elif lo is None:
         st = lib().bitnest_quant_linear_draft(_p(x), act_group, _p(hi), _p(scale), _p(y), _p(xq), _p(xs),
                                               M, N, K, _stream(x))
     else:
@@ -243,6 +282,20 @@ def bitnest_quant_linear_target(x: torch.Tensor, hi: torch.Tensor, lo: torch.Ten
     return _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, "bitnest_quant_linear_target")
 
 
+def bitnest_hadamard_quant_linear_draft(x: torch.Tensor, block: int, hi: torch.Tensor, scale: torch.Tensor,
+                                        y: torch.Tensor | None = None, xq: torch.Tensor | None = None,
+                                        xs: torch.Tensor | None = None):
+    """R4 rotation, per-token quantisation and the draft linear in one call: (y, xq, xs)."""
+    return _quant_linear(x, hi, None, scale, 0, y, xq, xs, "bitnest_hadamard_quant_linear_draft", block=block)
+
+
+def bitnest_hadamard_quant_linear_target(x: torch.Tensor, block: int, hi: torch.Tensor, lo: torch.Tensor,
+                                         scale: torch.Tensor, y: torch.Tensor | None = None,
+                                         xq: torch.Tensor | None = None, xs: torch.Tensor | None = None):
+    """R4 rotation, per-token quantisation and the target linear in one call: (y, xq, xs)."""
+    return _quant_linear(x, hi, lo, scale, 0, y, xq, xs, "bitnest_hadamard_quant_linear_target", block=block)
+
+
 # Short aliases
 quant_act = bitnest_quant_act
 linear_draft = bitnest_linear_draft
@@ -250,3 +303,6 @@ linear_target = bitnest_linear_target
 linear_partials = bitnest_linear_partials
 quant_linear_draft = bitnest_quant_linear_draft
 quant_linear_target = bitnest_quant_linear_target
+hadamard_quant_act = bitnest_hadamard_quant_act
+hadamard_quant_linear_draft = bitnest_hadamard_quant_linear_draft
+hadamard_quant_linear_target = bitnest_hadamard_quant_linear_target

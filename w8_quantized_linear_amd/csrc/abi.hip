@@ -6,6 +6,7 @@
 #include "bitnest_internal.h"
 
 #include <atomic>
+#include <cmath>
 
 namespace bitnest {
 
@@ -55,6 +56,15 @@ bitnest_status check_sizes(int M, int N, int K) {
 
 bitnest_status to_status(hipError_t e) { return e == hipSuccess ? BITNEST_OK : BITNEST_EHIP; }
 
+// Rotation block of the R4 calls: a power of two, 2 <= block <= the largest
+// supported, dividing K.
+bool valid_rot_block(int block, int K) {
+    return block >= 2 && block <= BITNEST_MAX_ROT_BLOCK && (block & (block - 1)) == 0 && K % block == 0;
+}
+
+// The fp32 value nearest 1 / sqrt(block) (block a power of two).
+float rot_scale_of(int block) { return static_cast<float>(1.0 / std::sqrt(static_cast<double>(block))); }
+
 bitnest_status run_linear(const bitnest::LinearArgs &a, bool exporting, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.M <= bitnest::kGemvMaxM) return to_status(bitnest::launch_gemv(a, exporting, s));
@@ -70,7 +80,7 @@ int bitnest_abi_version(void) { return BITNEST_ABI_VERSION; }
 const char *bitnest_status_string(int status) {
     switch (status) {
         case BITNEST_OK: return "ok";
-        case BITNEST_EINVAL: return "invalid argument (null pointer, negative size, K not a positive multiple of 128, or act_group not 0/128)";
+        case BITNEST_EINVAL: return "invalid argument (null pointer, negative size, K not a positive multiple of 128, act_group not 0/128, or an invalid rotation block)";
         case BITNEST_EALIGN: return "tensor pointer not 16-byte aligned";
         case BITNEST_EUNSUPPORTED: return "size beyond the library limits (M > BITNEST_MAX_M or K > BITNEST_MAX_K)";
         case BITNEST_EHIP: return "HIP runtime error while launching";
@@ -122,12 +132,13 @@ bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_
 
 namespace {
 
-// Shared body of the two fused calls: quantise, then the linear; one launch
-// when the fused GEMV takes the shape.
-bitnest_status quant_linear(const float *x, int act_group, const uint8_t *hi, const uint8_t *lo,
+// Shared body of the fused calls: (rotate and) quantise, then the linear;
+// one launch when the fused GEMV takes the shape. rot_block 0: no rotation.
+bitnest_status quant_linear(const float *x, int act_group, int rot_block, const uint8_t *hi, const uint8_t *lo,
                             const uint16_t *scale, float *y, int8_t *xq, float *xs, int M, int N, int K,
                             void *stream) {
     if (act_group != 0 && act_group != kGroup) return BITNEST_EINVAL;
+    if (rot_block != 0 && (act_group != 0 || !valid_rot_block(rot_block, K))) return BITNEST_EINVAL;
     bitnest_status st = check_sizes(M, N, K);
     if (st != BITNEST_OK) return st;
     if (M == 0) return BITNEST_OK;                  // empty: pointers may be NULL
@@ -137,10 +148,15 @@ bitnest_status quant_linear(const float *x, int act_group, const uint8_t *hi, co
     if (N > 0 && (!aligned16(hi) || !aligned16(scale) || !aligned16(y) || (lo && !aligned16(lo))))
         return BITNEST_EALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    bitnest::LinearArgs a{xq, xs, hi, lo, scale, y, nullptr, nullptr, nullptr, M, N, K, act_group, x, xq, xs};
+    const float rs = rot_block ? rot_scale_of(rot_block) : 0.0f;
+    bitnest::LinearArgs a{xq, xs, hi, lo, scale, y, nullptr, nullptr, nullptr, M, N, K, act_group, x, xq, xs,
+                          rot_block, rs};
     if (N > 0 && bitnest::fused_in_one_launch(M, K))
         return to_status(bitnest::launch_gemv_fused(a, s));
-    st = to_status(bitnest::launch_quant_act(x, M, K, act_group, xq, xs, s));
+    if (rot_block)
+        st = to_status(bitnest::launch_hadamard_quant_act(x, M, K, rot_block, rs, xq, xs, nullptr, s));
+    else
+        st = to_status(bitnest::launch_quant_act(x, M, K, act_group, xq, xs, s));
     if (st != BITNEST_OK || N == 0) return st;
     return run_linear(a, false, stream);
 }
@@ -151,14 +167,42 @@ extern "C" {
 
 bitnest_status bitnest_quant_linear_draft(const float *x, int act_group, const uint8_t *hi, const uint16_t *scale,
                                           float *y, int8_t *xq, float *xs, int M, int N, int K, void *stream) {
-    return quant_linear(x, act_group, hi, nullptr, scale, y, xq, xs, M, N, K, stream);
+    return quant_linear(x, act_group, 0, hi, nullptr, scale, y, xq, xs, M, N, K, stream);
 }
 
 bitnest_status bitnest_quant_linear_target(const float *x, int act_group, const uint8_t *hi, const uint8_t *lo,
                                            const uint16_t *scale, float *y, int8_t *xq, float *xs, int M, int N,
                                            int K, void *stream) {
     if (M > 0 && N > 0 && !lo) return BITNEST_EINVAL;
-    return quant_linear(x, act_group, hi, lo, scale, y, xq, xs, M, N, K, stream);
+    return quant_linear(x, act_group, 0, hi, lo, scale, y, xq, xs, M, N, K, stream);
+}
+
+bitnest_status bitnest_hadamard_quant_act(const float *x, int M, int K, int block, int8_t *xq, float *xs,
+                                          float *xr, void *stream) {
+    // like bitnest_quant_act: any number of tokens, K bounded
+    if (M < 0 || K <= 0 || K % kGroup != 0) return BITNEST_EINVAL;
+    if (!valid_rot_block(block, K)) return BITNEST_EINVAL;
+    if (K > BITNEST_MAX_K) return BITNEST_EUNSUPPORTED;
+    if (M == 0) return BITNEST_OK;                  // empty: pointers may be NULL
+    if (!x || !xq || !xs) return BITNEST_EINVAL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xs) || (xr && !aligned16(xr))) return BITNEST_EALIGN;
+    return to_status(bitnest::launch_hadamard_quant_act(x, M, K, block, rot_scale_of(block), xq, xs, xr,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
+bitnest_status bitnest_hadamard_quant_linear_draft(const float *x, int block, const uint8_t *hi,
+                                                   const uint16_t *scale, float *y, int8_t *xq, float *xs, int M,
+                                                   int N, int K, void *stream) {
+    if (block == 0) return BITNEST_EINVAL;
+    return quant_linear(x, 0, block, hi, nullptr, scale, y, xq, xs, M, N, K, stream);
+}
+
+bitnest_status bitnest_hadamard_quant_linear_target(const float *x, int block, const uint8_t *hi,
+                                                    const uint8_t *lo, const uint16_t *scale, float *y, int8_t *xq,
+                                                    float *xs, int M, int N, int K, void *stream) {
+    if (block == 0) return BITNEST_EINVAL;
+    if (M > 0 && N > 0 && !lo) return BITNEST_EINVAL;
+    return quant_linear(x, 0, block, hi, lo, scale, y, xq, xs, M, N, K, stream);
 }
 
 bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo, int32_t *p_hi,

@@ -37,10 +37,21 @@ struct LinearArgs {
     const float *x;
     int8_t *xq_out;
     float *xs_out;
+    // R4 rotation of the fp32 input before its quantisation (fused launch
+    // only): block size (0 = none) and the fp32 value nearest 1/sqrt(block)
+    int rot_block;
+    float rot_scale;
 };
+
+constexpr int kMaxRotBlock = 512;   // a rotation block stays inside one wave (64 lanes x 8)
 
 hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t *xq, float *xs,
                             hipStream_t stream);
+
+// R4 rotation (blocks of `block` columns, scaled by rot_scale) then per-token
+// quantisation; xr (may be null) receives the rotated fp32 values.
+hipError_t launch_hadamard_quant_act(const float *x, int M, int K, int block, float rot_scale, int8_t *xq,
+                                     float *xs, float *xr, hipStream_t stream);
 
 // M <= kGemvMaxM. export_partials selects the integer export instead of y.
 hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream);

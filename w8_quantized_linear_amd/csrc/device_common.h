@@ -126,6 +126,38 @@ __device__ __forceinline__ float wave_max_dpp_f32(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// One 8-value unit of the R4 rotation of the down_proj input (model card,
+// recipe table row "Rotation": an online Hadamard on the down_proj inputs;
+// the matrices are not given, the reading here is the Sylvester-Hadamard
+// transform per block of b columns). Lane `lane` holds elements
+// 8 j .. 8 j + 7 of its block, j = lane mod b/8 (b a power of two,
+// 2 <= b <= 512, so a block never leaves a wave). Stages h = 1, 2, ..., b/2
+// in that order, each replacing the pair (a, c) = (z[i], z[i + h]), i with
+// bit h clear, by (a + c, a - c): h < 8 inside the lane, h >= 8 with the
+// partner lane lane ^ (h / 8). The caller then scales by r_b.
+__device__ __forceinline__ void fwht_unit(float (&v)[8], int lane, int b) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+        if (h < b) {                                   // uniform
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i & h) continue;
+                const float a = v[i], c = v[i + h];
+                v[i] = a + c;
+                v[i + h] = a - c;
+            }
+        }
+    }
+    for (int m = 1; 8 * m < b; m <<= 1) {              // uniform
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = __shfl_xor(v[i], m);
+            v[i] = upper ? p - v[i] : v[i] + p;
+        }
+    }
+}
+
 __device__ __forceinline__ float absmax4(const float4 &v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }

@@ -160,7 +160,9 @@ struct Item {
 // PLANES: 1 draft (hi), 2 target (hi + lo). GA: per-128-group activation
 // scales. EXPORT: write the integer partials instead of y. D: items in flight
 // per wave. WAVES: waves per workgroup. XU: 0, or (one token only) quantise
-// the fp32 input in the prologue, XU 8-column units per thread.
+// the fp32 input in the prologue, XU 8-column units per thread. ROT (with XU):
+// apply the R4 rotation (fwht_unit, blocks of a.rot_block columns, times
+// a.rot_scale) to the fp32 input before quantising it.
 //
 // A row of K columns is C = ceil(K / 2048) chunks; the (row, chunk) items of
 // the whole call are split into contiguous runs, one per wave, and each wave
@@ -169,7 +171,7 @@ struct Item {
 // (scalar registers) plus a fixed lane offset, so address arithmetic stays
 // off the vector ALU; loads past the end of a plane return 0. The workgroup
 // stages the codes once into LDS while its first D items are in flight.
-template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, int XU>
+template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, int XU, bool ROT>
 __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArgs a) {
     constexpr bool FUSED = XU > 0;
     constexpr int kThreads = 64 * WAVES;
@@ -325,6 +327,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
                 xf[k][i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][0][i]));
                 xf[k][4 + i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][1][i]));
             }
+        if (ROT) {
+            // unit u = tid + k * threads: one wave's units at one k are 512
+            // consecutive columns, so every rotation block is inside a wave
+#pragma unroll
+            for (int k = 0; k < XU; ++k) {
+                fwht_unit(xf[k], lane, a.rot_block);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xf[k][i] = xf[k][i] * a.rot_scale;
+            }
+        }
         auto absmax8 = [](const float (&v)[8]) {
             float m = 0.0f;
 #pragma unroll
@@ -499,9 +511,9 @@ template <int PLANES, int M>
 GemvKernel pick_mode(bool grouped, bool exporting) {
     constexpr int D = items_in_flight<PLANES>();
     constexpr int W = kGemvWaves;
-    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, 0>;
-    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, 0>
-                   : gemv_planes_kernel<PLANES, M, false, false, D, W, 0>;
+    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, 0, false>;
+    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, 0, false>
+                   : gemv_planes_kernel<PLANES, M, false, false, D, W, 0, false>;
 }
 
 template <int PLANES>
@@ -523,17 +535,18 @@ constexpr int fused_units(int K) { return (K / 8 + 64 * kFusedWaves - 1) / (64 *
 static_assert(fused_units(kFusedMaxMK) <= 4, "pick_fused covers up to four units per thread");
 
 template <int PLANES, int XU>
-GemvKernel pick_fused_xu(bool grouped) {
+GemvKernel pick_fused_xu(bool grouped, bool rot) {
     constexpr int D = items_in_flight<PLANES>();
-    return grouped ? gemv_planes_kernel<PLANES, 1, true, false, D, kFusedWaves, XU>
-                   : gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU>;
+    if (rot) return gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, true>;
+    return grouped ? gemv_planes_kernel<PLANES, 1, true, false, D, kFusedWaves, XU, false>
+                   : gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, false>;
 }
 
 template <int PLANES>
-GemvKernel pick_fused(int K, bool grouped) {
+GemvKernel pick_fused(int K, bool grouped, bool rot) {
     const int xu = fused_units(K);
-    return xu <= 1 ? pick_fused_xu<PLANES, 1>(grouped)
-                   : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped) : pick_fused_xu<PLANES, 4>(grouped);
+    return xu <= 1 ? pick_fused_xu<PLANES, 1>(grouped, rot)
+                   : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped, rot) : pick_fused_xu<PLANES, 4>(grouped, rot);
 }
 
 size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused, int waves, bool sums) {
@@ -554,7 +567,7 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
     const bool grouped = a.act_group == kGroup && !exporting;
     GemvKernel k;
     if (fused)
-        k = target ? pick_fused<2>(a.K, grouped) : pick_fused<1>(a.K, grouped);
+        k = target ? pick_fused<2>(a.K, grouped, a.rot_block > 0) : pick_fused<1>(a.K, grouped, a.rot_block > 0);
     else
         k = target ? pick_m<2>(a.M, grouped, exporting) : pick_m<1>(a.M, grouped, exporting);
     if (!k) return hipErrorInvalidValue;
@@ -594,6 +607,7 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
 
 hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream) {
     if (!fused_in_one_launch(a.M, a.K)) return hipErrorNotSupported;
+    if (a.rot_block > 0 && (a.act_group != 0 || a.rot_block > kMaxRotBlock)) return hipErrorInvalidValue;
     return launch(a, false, true, stream);
 }
 
