@@ -54,6 +54,8 @@ def parse_args(argv=None):
                    help="token counts for the batched-verify (matrix-core) layer timing; empty to skip")
     p.add_argument("--no-per-linear", dest="per_linear", action="store_false", default=True,
                    help="skip the per-linear timing (each shape on its own, draft/target M=1, target M=4)")
+    p.add_argument("--no-r4", dest="r4", action="store_false", default=True,
+                   help="skip the R4 (rotated down_proj input) timing")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -119,7 +121,7 @@ class Stack:
         return (GAMMA + 1) * self.layers * len(self.linears)
 
 
-def run_round(stack, bn, mode="fused"):
+def run_round(stack, bn, mode="fused", rot_block=0):
     """One speculative round: 3 draft passes at M = 1, one verify pass at M = 4.
 
     mode "fused": each linear quantises its fp32 input and runs the nested
@@ -127,16 +129,24 @@ def run_round(stack, bn, mode="fused"):
     then bitnest_linear_*; "linear_only": the linear launches of the fused
     round and nothing else (linears whose fused call is two launches run only
     their linear, on the codes already in the buffers) - used to time the
-    dominant kernel on its own."""
+    dominant kernel on its own. rot_block > 0 (with mode "fused"): the
+    down_proj input also takes the R4 rotation (blocks of rot_block columns)
+    before its quantisation, as the model card's recipe does."""
     for p in range(GAMMA + 1):
         verify = p == GAMMA
         M = GAMMA + 1 if verify else 1
         for l in range(stack.layers):
-            for i, (_, N, K, g) in enumerate(stack.linears):
+            for i, (name, N, K, g) in enumerate(stack.linears):
                 xq, xs, y = stack.buf[(M, i)]
                 w = stack.w[l][i]
                 x = stack.x_verify[l][i] if verify else stack.x_draft[p][l][i]
                 one = bn.fused_in_one_launch(M, K)
+                if rot_block and mode == "fused" and name == "down":
+                    if verify:
+                        bn.bitnest_hadamard_quant_linear_target(x, rot_block, w.hi, w.lo, w.scale, y=y, xq=xq, xs=xs)
+                    else:
+                        bn.bitnest_hadamard_quant_linear_draft(x, rot_block, w.hi, w.scale, y=y, xq=xq, xs=xs)
+                    continue
                 if mode == "fused" or (mode == "linear_only" and one):
                     if verify:
                         bn.bitnest_quant_linear_target(x, w.hi, w.lo, w.scale, g, y=y, xq=xq, xs=xs)
@@ -303,6 +313,70 @@ def batched_verify(stack, bn, batches, reps=20):
     return out
 
 
+def r4_timing(stack, bn, block=512, steps=10, reps=5):
+    """The down_proj input with the R4 rotation (model card recipe: an online
+    Hadamard on the down_proj inputs; here blocks of `block` columns): the
+    fused one-token draft and target launches, the rotation + quantisation
+    launch at M=4, each over the stack's layers from a HIP graph; and the
+    whole round with the rotation on every down_proj input."""
+    import torch
+    i = [n for (n, _, _, _) in stack.linears].index("down")
+    _, N, K, _ = stack.linears[i]
+    L = stack.layers
+    out = {"block": block}
+
+    def timed(fn, n):
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3 / n)
+        return sorted(ts)[len(ts) // 2]
+
+    xq1, xs1, y1 = stack.buf[(1, i)]
+    xq4, xs4, y4 = stack.buf[(GAMMA + 1, i)]
+    for mode in ("draft_M1", "target_M1"):
+        def fn(mode=mode):
+            for l in range(L):
+                w = stack.w[l][i]
+                if mode == "draft_M1":
+                    bn.bitnest_hadamard_quant_linear_draft(stack.x_draft[0][l][i], block, w.hi, w.scale,
+                                                           y=y1, xq=xq1, xs=xs1)
+                else:
+                    bn.bitnest_hadamard_quant_linear_target(stack.x_draft[0][l][i], block, w.hi, w.lo, w.scale,
+                                                            y=y1, xq=xq1, xs=xs1)
+        t = timed(fn, L)
+        plane = N * K // 2 * (1 if mode == "draft_M1" else 2)
+        out["down_" + mode] = {"us": round(t * 1e6, 3), "plane_GBps": round(plane / t / 1e9, 1),
+                               "frac": round(plane / t / 1e9 / HBM_PEAK_GBS, 4)}
+    t = timed(lambda: [bn.bitnest_hadamard_quant_act(stack.x_verify[l][i], block, xq=xq4, xs=xs4)
+                       for l in range(L)], L)
+    out["rotate_quant_M4_us"] = round(t * 1e6, 3)
+    g = capture(lambda: run_round(stack, bn, mode="fused", rot_block=block))
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = stack.plane_bytes_per_round() / (ms * 1e-3) / 1e9
+    out["round_ms"] = round(ms, 4)
+    out["round_plane_GBps"] = round(gbs, 1)
+    out["round_pct_hbm_peak"] = round(100 * gbs / HBM_PEAK_GBS, 2)
+    log("R4 (block %d): down draft M=1 %.2f us, target M=1 %.2f us, rotate+quant M=4 %.2f us; round %.3f ms"
+        % (block, out["down_draft_M1"]["us"], out["down_target_M1"]["us"], out["rotate_quant_M4_us"], ms))
+    return out
+
+
 def measured_traffic():
     """HBM bytes per linear launch from the committed hardware-counter
     profile (rocprofv3 FETCH_SIZE and WRITE_SIZE of the round's launches,
@@ -417,6 +491,7 @@ def main(argv=None):
         log("GEMV: %.3f us per launch (events), %.1f GB/s algorithmic" % (t_gemv * 1e6, achieved))
 
     linears = per_linear(stack, bn) if args.per_linear else None
+    r4 = r4_timing(stack, bn, steps=min(args.steps, 10)) if args.r4 else None
 
     verify = None
     batches = [int(v) for v in args.verify_batches.split(",") if v.strip()]
@@ -450,6 +525,7 @@ def main(argv=None):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
         "per_linear": linears,
+        "r4": r4,
         "batched_verify": verify,
         "cpu_baseline": cpu,
     }

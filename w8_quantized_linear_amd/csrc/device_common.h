@@ -126,6 +126,46 @@ __device__ __forceinline__ float wave_max_dpp_f32(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// One cross-lane stage of fwht_unit: lanes with bit m clear hold a = z[i],
+// their partners (lane ^ m) hold c = z[i + 8 m]; the lower lane keeps
+// a + c, the upper one a - c, computed as partner + (+-own) (an IEEE
+// subtraction is the addition of the negated operand, so the bits are those
+// of a - c). The partner's value comes without LDS traffic where the
+// hardware allows: DPP quad permutes (m = 1, 2), DPP row rotate by 8 (m = 8),
+// a swizzle (m = 4); for m = 16 and 32 the gfx950 row / half-wave swaps
+// exchange the two halves of (v, v), after which the first result holds the
+// lower lane's value and the second the upper lane's, in both lanes of a
+// pair.
+template <int m>
+__device__ __forceinline__ void fwht_cross_stage(float (&v)[8], int lane) {
+    static_assert(m == 1 || m == 2 || m == 4 || m == 8 || m == 16 || m == 32, "lane masks 1..32");
+    const unsigned neg = (lane & m) ? 0x80000000u : 0u;          // upper lanes subtract their own value
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const unsigned u = __builtin_bit_cast(unsigned, v[i]);
+        if constexpr (m == 16 || m == 32) {
+            unsigned lo, hi;
+            if constexpr (m == 16) {
+                const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                lo = r[0];
+                hi = r[1];
+            } else {
+                const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                lo = r[0];
+                hi = r[1];
+            }
+            v[i] = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi ^ neg);
+        } else {
+            float p;
+            if constexpr (m == 1) p = dpp_f32<kDppQuadSwap1>(v[i]);
+            else if constexpr (m == 2) p = dpp_f32<kDppQuadSwap2>(v[i]);
+            else if constexpr (m == 8) p = dpp_f32<kDppRowRor8>(v[i]);
+            else p = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(static_cast<int>(u), 0x1F | (4 << 10)));
+            v[i] = p + __builtin_bit_cast(float, u ^ neg);
+        }
+    }
+}
+
 // One 8-value unit of the R4 rotation of the down_proj input (model card,
 // recipe table row "Rotation": an online Hadamard on the down_proj inputs;
 // the matrices are not given, the reading here is the Sylvester-Hadamard
@@ -148,14 +188,12 @@ __device__ __forceinline__ void fwht_unit(float (&v)[8], int lane, int b) {
             }
         }
     }
-    for (int m = 1; 8 * m < b; m <<= 1) {              // uniform
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __shfl_xor(v[i], m);
-            v[i] = upper ? p - v[i] : v[i] + p;
-        }
-    }
+    if (b > 8) fwht_cross_stage<1>(v, lane);            // uniform conditions
+    if (b > 16) fwht_cross_stage<2>(v, lane);
+    if (b > 32) fwht_cross_stage<4>(v, lane);
+    if (b > 64) fwht_cross_stage<8>(v, lane);
+    if (b > 128) fwht_cross_stage<16>(v, lane);
+    if (b > 256) fwht_cross_stage<32>(v, lane);
 }
 
 __device__ __forceinline__ float absmax4(const float4 &v) {

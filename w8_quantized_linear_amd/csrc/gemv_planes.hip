@@ -332,9 +332,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
             // consecutive columns, so every rotation block is inside a wave
 #pragma unroll
             for (int k = 0; k < XU; ++k) {
-                fwht_unit(xf[k], lane, a.rot_block);
+                if (k * kThreads + wave * 64 < nunit) {  // wave-uniform: units past the row stay zero
+                    fwht_unit(xf[k], lane, a.rot_block);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xf[k][i] = xf[k][i] * a.rot_scale;
+                    for (int i = 0; i < 8; ++i) xf[k][i] = xf[k][i] * a.rot_scale;
+                }
             }
         }
         auto absmax8 = [](const float (&v)[8]) {

@@ -82,16 +82,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
 
 // The down_proj input path: the R4 rotation (fwht_unit per 8-column unit,
 // then one multiply by rot_scale), then the per-token rule above on the
-// rotated values. One token per workgroup of 512 threads; unit u = tid + k *
-// 512 (k < NU) holds columns 8 u .. 8 u + 7, so the units of one wave at one
+// rotated values. One token per workgroup of TH threads; unit u = tid + k *
+// TH (k < NU) holds columns 8 u .. 8 u + 7, so the units of one wave at one
 // k are 512 consecutive columns and every rotation block (<= 512 columns)
 // lies inside one wave. Units past K read as zero through the buffer
-// descriptor and are not written.
+// descriptor and are not written. (The transform makes this kernel
+// ALU-bound on its one compute unit, so it runs 16 waves, where the plain
+// quantisation is latency-bound and runs 8.)
+constexpr int kRotThreads = 1024;
+
 template <int NU>
-__global__ __launch_bounds__(kTokenThreads) void hadamard_quant_kernel(
+__global__ __launch_bounds__(kRotThreads) void hadamard_quant_kernel(
     const float *__restrict__ x, int K, int block, float rot_scale, int8_t *__restrict__ q, float *__restrict__ s,
     float *__restrict__ xr) {
-    __shared__ float part[kTokenThreads / 64];
+    constexpr int TH = kRotThreads;
+    __shared__ float part[TH / 64];
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int nunit = K >> 3;
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(kTokenThreads) void hadamard_quant_kernel(
     float v[NU][8];
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-        const int off = (threadIdx.x + k * kTokenThreads) * 32;
+        const int off = (threadIdx.x + k * TH) * 32;
         const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
         // (elements copied out before the bit cast: a bit cast of a
@@ -114,11 +119,13 @@ __global__ __launch_bounds__(kTokenThreads) void hadamard_quant_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-        fwht_unit(v[k], lane, block);
+        if (k * TH + (threadIdx.x & ~63) < nunit) {    // wave-uniform: units past K stay zero
+            fwht_unit(v[k], lane, block);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[k][i] = v[k][i] * rot_scale;
-            amax = fmaxf(amax, fabsf(v[k][i]));       // units past K hold zeros
+            for (int i = 0; i < 8; ++i) {
+                v[k][i] = v[k][i] * rot_scale;
+                amax = fmaxf(amax, fabsf(v[k][i]));
+            }
         }
     }
     amax = wave_max_dpp_f32(amax);
@@ -126,13 +133,13 @@ __global__ __launch_bounds__(kTokenThreads) void hadamard_quant_kernel(
     __syncthreads();
     amax = part[0];
 #pragma unroll
-    for (int w = 1; w < kTokenThreads / 64; ++w) amax = fmaxf(amax, part[w]);
+    for (int w = 1; w < TH / 64; ++w) amax = fmaxf(amax, part[w]);
     const float sc = amax / 127.0f;
     const float rc = quant_recip(sc);
     if (threadIdx.x == 0) s[m] = sc;
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-        const int u = threadIdx.x + k * kTokenThreads;
+        const int u = threadIdx.x + k * TH;
         if (u < nunit) {
             unsigned y[8];
             quant_codes<8>(v[k], sc, rc, y);
@@ -151,16 +158,14 @@ __global__ __launch_bounds__(kTokenThreads) void hadamard_quant_kernel(
 
 hipError_t launch_hadamard_quant_act(const float *x, int M, int K, int block, float rot_scale, int8_t *xq,
                                      float *xs, float *xr, hipStream_t stream) {
-    const int nu = (K / 8 + kTokenThreads - 1) / kTokenThreads;
+    const int nu = (K / 8 + kRotThreads - 1) / kRotThreads;
     void (*k)(const float *, int, int, float, int8_t *, float *, float *);
     switch (nu) {
         case 1: k = hadamard_quant_kernel<1>; break;
         case 2: k = hadamard_quant_kernel<2>; break;
-        case 3: k = hadamard_quant_kernel<3>; break;
-        case 4: k = hadamard_quant_kernel<4>; break;
         default: return hipErrorInvalidValue;   // K > kMaxK: rejected by the ABI before this point
     }
-    hipLaunchKernelGGL(k, dim3(M), dim3(kTokenThreads), 0, stream, x, K, block, rot_scale, xq, xs, xr);
+    hipLaunchKernelGGL(k, dim3(M), dim3(kRotThreads), 0, stream, x, K, block, rot_scale, xq, xs, xr);
     return hipGetLastError();
 }
 
