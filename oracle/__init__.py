@@ -54,9 +54,13 @@ def _load():
         lib.oracle_dequant.argtypes = [I, P, P, P, I, I, P]
         lib.oracle_linear.argtypes = [I, P, P, I, P, P, P, I, I, I, P, I]
         lib.oracle_hadamard_rotate.argtypes = [P, I, I, I, P]
+        lib.oracle_pack_nested.argtypes = [P, I, I, P, P, P]
+        lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+        lib.oracle_float_to_half.restype = ctypes.c_uint16
         lib.oracle_max_threads.argtypes = []
         for f in ("oracle_unpack_plane", "oracle_quant_act", "oracle_partials",
-                  "oracle_dequant", "oracle_linear", "oracle_hadamard_rotate", "oracle_max_threads"):
+                  "oracle_dequant", "oracle_linear", "oracle_hadamard_rotate", "oracle_pack_nested",
+                  "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -197,3 +201,21 @@ def hadamard_quant_act(x: np.ndarray, block: int):
     r = hadamard_rotate(x, block)
     q, s = quant_act(r, 0)
     return q, s, r
+
+
+def float_to_half_bits(f: float) -> int:
+    """fp32 value -> IEEE binary16 bit pattern, round to nearest even."""
+    return int(_load().oracle_float_to_half(float(np.float32(f))))
+
+
+def pack_nested(W: np.ndarray):
+    """fp32 weights [N, K] -> (hi uint8 [N, K/2], lo uint8 [N, K/2], scale fp16 bits uint16
+    [N, K/128]): the nested packing reading in the C file's header (symmetric 15-step RTN
+    high nibble with fp16 scale amax/7.5, closed-form residual low nibble)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    hi = np.empty((N, K // 2), np.uint8)
+    lo = np.empty((N, K // 2), np.uint8)
+    sc = np.empty((N, K // GROUP), np.uint16)
+    _check(_load().oracle_pack_nested(_ptr(W), N, K, _ptr(hi), _ptr(lo), _ptr(sc)), "pack_nested")
+    return hi, lo, sc

@@ -48,6 +48,21 @@
  *    clear by (a + c, a - c), then one fp32 multiply by r_b per element.
  *    Fixing the stage order and the single multiply defines the rotated fp32
  *    values, and therefore their int8 codes, to the bit.
+ *  - Offline nested packing of fp32 weights: model card introduction (the
+ *    high nibble is a GPTQ-W4 model fitted first, the low nibble the
+ *    closed-form residual back to W8) and the planes.safetensors entry (the
+ *    format both nibbles must land in). GPTQ itself needs calibration data;
+ *    the reading here is its symmetric round-to-nearest quantiser (15 steps,
+ *    zero point 8) per (row, 128-column group), with the stored fp16 scale:
+ *        amax = max |W| over the group,
+ *        s    = fp16(amax / 7.5)   (fp32 division, then round to nearest
+ *                                   even in binary16),
+ *        c_hi = clamp(rne(W / s), -8, 7),            hi = c_hi + 8,
+ *        R    = W - c_hi * s                          (fp32),
+ *        c_lo = clamp(rne(R / (s / 16)), -8, 7),     lo = c_lo + 8,
+ *    every division an IEEE fp32 division; s == 0 gives c_hi = c_lo = 0.
+ *    Then W4 = c_hi * s and W8 = (16 c_hi + c_lo) * s / 16 per the model
+ *    card's formulas, and |W8 - W| <= s / 32 wherever neither code clamps.
  *
  * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 and fp64
  * operation is the IEEE operation written.
@@ -266,6 +281,73 @@ int oracle_hadamard_rotate(const float *x, int M, int K, int block, float *y)
                 }
             }
             for (int i = 0; i < block; ++i) z[i] = z[i] * rb;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* IEEE binary32 -> binary16, round to nearest even, from the two formats'
+ * definitions (finite inputs; overflow gives infinity). */
+uint16_t oracle_float_to_half(float f)
+{
+    union { float f; uint32_t u; } v = { f };
+    uint32_t sign = (v.u >> 16) & 0x8000u;
+    float a = fabsf(f);
+    if (a != a) return (uint16_t)(sign | 0x7E00u);
+    if (a >= 65520.0f) return (uint16_t)(sign | 0x7C00u);        /* rounds past the largest finite */
+    if (a < 0x1p-14f) {
+        /* subnormal result: a multiple of 2^-24, rounded to nearest even */
+        float q = nearbyintf(a * 0x1p24f);                        /* exact scaling, then RNE */
+        return (uint16_t)(sign | (uint32_t)q);
+    }
+    int e;
+    float m = frexpf(a, &e);                                      /* a = m * 2^e, 0.5 <= m < 1 */
+    /* 11 significant bits: mantissa as an integer in [1024, 2048] after RNE */
+    float q = nearbyintf(ldexpf(m, 11));
+    if (q == 2048.0f) { q = 1024.0f; e += 1; }
+    uint32_t exp16 = (uint32_t)(e - 1 + 15);
+    if (exp16 >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (exp16 << 10) | ((uint32_t)q - 1024u));
+}
+
+static int rne_clamp(float t, int lo, int hi)
+{
+    float r = nearbyintf(t);
+    if (r < (float)lo) r = (float)lo;
+    if (r > (float)hi) r = (float)hi;
+    return (int)r;
+}
+
+/* The packing reading stated at the top: W fp32 [N, K] -> planes hi, lo
+ * uint8 [N, K/2] and scale fp16 bits [N, K/128]. */
+int oracle_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t *lo, uint16_t *scale)
+{
+    if (!W || !hi || !lo || !scale || N < 0 || K <= 0 || K % ORACLE_GROUP) return ORACLE_EINVAL;
+    if (fegetround() != FE_TONEAREST) return ORACLE_EINVAL;
+    const int G = K / ORACLE_GROUP;
+    for (int n = 0; n < N; ++n) {
+        for (int g = 0; g < G; ++g) {
+            const float *w = W + (size_t)n * K + (size_t)g * ORACLE_GROUP;
+            float amax = 0.0f;
+            for (int k = 0; k < ORACLE_GROUP; ++k)
+                if (fabsf(w[k]) > amax) amax = fabsf(w[k]);
+            uint16_t sb = oracle_float_to_half(amax / 7.5f);
+            scale[(size_t)n * G + g] = sb;
+            float s = (float)oracle_half_to_double(sb);            /* exact */
+            float s16th = s / 16.0f;                                /* exact: power of two */
+            for (int k = 0; k < ORACLE_GROUP; ++k) {
+                int ch = 0, cl = 0;
+                if (s != 0.0f) {
+                    ch = rne_clamp(w[k] / s, -8, 7);
+                    float r = w[k] - (float)ch * s;
+                    cl = rne_clamp(r / s16th, -8, 7);
+                }
+                size_t byte = (size_t)n * (K / 2) + (size_t)(g * ORACLE_GROUP + k) / 2;
+                int shift = (k % 2 == 0) ? 0 : 4;                     /* column 2j low nibble, 2j+1 high */
+                if (shift == 0) { hi[byte] = 0; lo[byte] = 0; }
+                hi[byte] |= (uint8_t)((ch + 8) << shift);
+                lo[byte] |= (uint8_t)((cl + 8) << shift);
+            }
         }
     }
     return ORACLE_OK;

@@ -499,3 +499,102 @@ def test_hadamard_bad_args():
     for b in (0, 1, 3, 12, 64, 128):
         with pytest.raises(oracle.OracleError):
             oracle.hadamard_rotate(x, b)
+
+
+# --------------------------------------------------------------------------- offline nested packing
+# Reading (model card introduction and planes.safetensors): symmetric 15-step
+# RTN high nibble with fp16 scale amax / 7.5, closed-form residual low nibble.
+
+def test_float_to_half_matches_ieee_library():
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.standard_normal(20000) * 1000, rng.standard_normal(20000) * 1e-6,
+                         [0.0, 6.1035156e-05, 5.96e-08, 2.98e-08, 65504.0, 65519.0, 1e-10, -3.0e-6, 0.5,
+                          1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]]).astype(np.float32)
+    got = np.array([oracle.float_to_half_bits(x) for x in xs], np.uint16)
+    assert np.array_equal(got, xs.astype(np.float16).view(np.uint16))
+
+
+def test_pack_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "pack.json")))
+    W = np.zeros((g["N"], g["K"]), np.float32)
+    for k, v in g["group0_values"].items():
+        W[0, int(k)] = v
+    hi, lo, sc = oracle.pack_nested(W)
+    fill = int(g["fill_byte"], 16)
+    want_hi = np.full(g["K"] // 2, fill, np.uint8)
+    want_lo = np.full(g["K"] // 2, fill, np.uint8)
+    want_hi[:4] = [int(b, 16) for b in g["hi_bytes_group0_first4"]]
+    want_lo[:4] = [int(b, 16) for b in g["lo_bytes_group0_first4"]]
+    assert np.array_equal(hi[0], want_hi)
+    assert np.array_equal(lo[0], want_lo)
+    assert [int(v) for v in sc[0]] == [int(b, 16) for b in g["scale_bits"]]
+
+
+def _packed_codes(W):
+    hi, lo, sc = oracle.pack_nested(W)
+    K = W.shape[1]
+    ch = oracle.unpack_plane(hi, K).astype(np.int64) - 8
+    cl = oracle.unpack_plane(lo, K).astype(np.int64) - 8
+    s = np.repeat(sc.view(np.float16).astype(np.float64), 128, axis=1)
+    return hi, lo, sc, ch, cl, s
+
+
+def test_pack_error_bounds_and_formulas():
+    rng = np.random.default_rng(12)
+    W = (rng.standard_t(4, size=(24, 1024)) * 0.02).astype(np.float32)
+    W[3, :128] = 0.0                                      # an all-zero group
+    hi, lo, sc, ch, cl, s = _packed_codes(W)
+    w = W.astype(np.float64)
+    # the scale is fp16(amax / 7.5) of its group
+    amax = np.abs(W).reshape(24, 8, 128).max(axis=2)
+    assert np.array_equal(sc, (amax / np.float32(7.5)).astype(np.float32).astype(np.float16).view(np.uint16))
+    # codes in range; a zero group gives zero codes
+    assert ch.min() >= -8 and ch.max() <= 7 and cl.min() >= -8 and cl.max() <= 7
+    assert not ch[3, :128].any() and not cl[3, :128].any()
+    # the model card's formulas: W4 = c_hi s, W8 = (16 c_hi + c_lo) s / 16
+    W4 = ch * s
+    W8 = (16 * ch + cl) * s / 16
+    assert np.allclose(oracle.dequant(hi, sc), W4, rtol=0, atol=0)
+    assert np.allclose(oracle.dequant(hi, sc, lo), W8, rtol=0, atol=0)
+    # where no clamp acts: |W4 - W| <= s/2 and |W8 - W| <= s/32
+    ss = np.where(s > 0, s, 1.0)
+    u = w / ss
+    t = (w - W4) * 16 / ss
+    free_hi = (s > 0) & (u > -8.5) & (u < 7.5)
+    free = free_hi & (t > -8.5) & (t < 7.5)
+    assert free_hi.mean() > 0.99 and free.mean() > 0.9
+    tol = 1 + 2.0 ** -20
+    assert np.all(np.abs(W4 - w)[free_hi] <= s[free_hi] / 2 * tol)
+    assert np.all(np.abs(W8 - w)[free] <= s[free] / 32 * tol)
+    # W8 is never worse than W4 by more than the residual clamp allows
+    assert np.all(np.abs(W8 - w) <= np.abs(W4 - w) + 1e-12)
+
+
+def test_pack_on_the_w4_grid_gives_lo_8():
+    # a group with amax 1.875 has s = fp16(0.25) exactly; values k * 0.25 for
+    # |k| <= 7 are on the W4 grid, so their residual code is 0 (lo = 8)
+    rng = np.random.default_rng(13)
+    W = (rng.integers(-7, 8, size=(4, 256)) * 0.25).astype(np.float32)
+    W[:, 0] = 1.875
+    W[:, 128] = -1.875
+    hi, lo, sc, ch, cl, s = _packed_codes(W)
+    assert np.all(sc == np.float16(0.25).view(np.uint16))
+    grid = np.ones(W.shape, bool)
+    grid[:, [0, 128]] = False
+    assert np.all(cl[grid] == 0)
+    assert np.array_equal(ch[grid], (W[grid] / 0.25).astype(np.int64))
+
+
+def test_pack_sign_and_power_of_two_symmetry():
+    rng = np.random.default_rng(14)
+    W = (rng.standard_normal((6, 512)) * 0.03).astype(np.float32)
+    hi, lo, sc, ch, cl, s = _packed_codes(W)
+    # doubling W doubles every scale exactly and keeps every code
+    hi2, lo2, sc2 = oracle.pack_nested(W * 2)
+    assert np.array_equal(hi2, hi) and np.array_equal(lo2, lo)
+    assert np.array_equal(sc2.view(np.float16), (sc.view(np.float16).astype(np.float32) * 2).astype(np.float16))
+    # negating W negates the codes except where the asymmetric range clamps
+    _, _, scn, chn, cln, _ = _packed_codes(-W)
+    assert np.array_equal(scn, sc)
+    ok = (ch > -8) & (ch < 7) & (cl > -8) & (cl < 7) & (np.abs((W / s).astype(np.float64) % 1) != 0.5)
+    assert np.array_equal(chn[ok], -ch[ok])

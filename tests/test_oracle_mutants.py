@@ -44,6 +44,15 @@ MUTANTS = {
     "hadamard first stage skipped": ("for (int h = 1; h < block; h *= 2)", "for (int h = 2; h < block; h *= 2)"),
     "hadamard last stage skipped": ("for (int h = 1; h < block; h *= 2)", "for (int h = 1; h < block / 2; h *= 2)"),
     "hadamard input block offset": ("const float *xr = x + (size_t)m * K + b0;", "const float *xr = x + (size_t)m * K;"),
+    "pack scale amax/7": ("oracle_float_to_half(amax / 7.5f)", "oracle_float_to_half(amax / 7.0f)"),
+    "pack rounding half away": ("    float r = nearbyintf(t);\n    if (r < (float)lo)", "    float r = roundf(t);\n    if (r < (float)lo)"),
+    "pack residual step s/8": ("float s16th = s / 16.0f;", "float s16th = s / 8.0f;"),
+    "pack nibble order": ("int shift = (k % 2 == 0) ? 0 : 4;", "int shift = (k % 2 == 0) ? 4 : 0;"),
+    "pack hi zero point 7": ("hi[byte] |= (uint8_t)((ch + 8) << shift);", "hi[byte] |= (uint8_t)((ch + 7) << shift);"),
+    "pack residual from W": ("float r = w[k] - (float)ch * s;", "float r = w[k];"),
+    "pack hi clamp -7": ("ch = rne_clamp(w[k] / s, -8, 7);", "ch = rne_clamp(w[k] / s, -7, 7);"),
+    "half conversion truncates": ("float q = nearbyintf(ldexpf(m, 11));", "float q = floorf(ldexpf(m, 11));"),
+    "half subnormal truncates": ("float q = nearbyintf(a * 0x1p24f);", "float q = floorf(a * 0x1p24f);"),
 }
 
 
