@@ -56,6 +56,8 @@ def parse_args(argv=None):
                    help="skip the per-linear timing (each shape on its own, draft/target M=1, target M=4)")
     p.add_argument("--no-r4", dest="r4", action="store_false", default=True,
                    help="skip the R4 (rotated down_proj input) timing")
+    p.add_argument("--no-pack", dest="pack", action="store_false", default=True,
+                   help="skip the offline packer timing")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -377,6 +379,47 @@ def r4_timing(stack, bn, block=512, steps=10, reps=5):
     return out
 
 
+def pack_timing(stack, bn, reps=5):
+    """The offline nested packer on each Llama-3-8B linear shape: fp32
+    weights (cold: buffers rotate through more memory than the caches hold)
+    -> hi / lo planes and fp16 scales. us per linear and GB/s of its
+    algorithmic bytes (4 N K read, N K planes + 2 N K/128 scales written)
+    with the fraction of the 8 TB/s peak."""
+    import torch
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    for (name, N, K, _) in stack.linears:
+        nbuf = max(2, -(-(512 << 20) // (4 * N * K)))          # > 512 MiB of inputs in rotation
+        Ws = [torch.randn((N, K), generator=g, device="cuda") * 0.02 for _ in range(nbuf)]
+        hi = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+        lo = torch.empty_like(hi)
+        sc = torch.empty((N, K // 128), dtype=torch.int16, device="cuda")
+
+        def fn():
+            for W in Ws:
+                bn.bitnest_pack_nested(W, hi, lo, sc)
+        graph = capture(fn)
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3 / nbuf)
+        t = sorted(ts)[len(ts) // 2]
+        nbytes = 4 * N * K + N * K + 2 * N * (K // 128)
+        gbs = nbytes / t / 1e9
+        out[name] = {"us": round(t * 1e6, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes}
+        del Ws
+        torch.cuda.empty_cache()
+    log("pack: " + ", ".join("%s %.1f us %.0f GB/s" % (k, v["us"], v["GBps"]) for k, v in out.items()))
+    return out
+
+
 def measured_traffic():
     """HBM bytes per linear launch from the committed hardware-counter
     profile (rocprofv3 FETCH_SIZE and WRITE_SIZE of the round's launches,
@@ -492,6 +535,7 @@ def main(argv=None):
 
     linears = per_linear(stack, bn) if args.per_linear else None
     r4 = r4_timing(stack, bn, steps=min(args.steps, 10)) if args.r4 else None
+    pack = pack_timing(stack, bn) if args.pack else None
 
     verify = None
     batches = [int(v) for v in args.verify_batches.split(",") if v.strip()]
@@ -526,6 +570,7 @@ def main(argv=None):
         "roofline": roofline,
         "per_linear": linears,
         "r4": r4,
+        "pack": pack,
         "batched_verify": verify,
         "cpu_baseline": cpu,
     }

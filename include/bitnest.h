@@ -195,6 +195,33 @@ bitnest_status bitnest_hadamard_quant_linear_target(const float *x, int block,
                                                     int M, int N, int K, void *stream);
 
 /*
+ * Offline nested packing of fp32 weights into the two planes (model card
+ * introduction: the high nibble is a GPTQ-W4 model fitted first, the low
+ * nibble the closed-form residual back to W8; section "Files", entry
+ * planes.safetensors: the format). GPTQ needs calibration data; this is the
+ * symmetric round-to-nearest quantiser it builds on (15 steps, zero point 8)
+ * per row and 128-column group, with the stored fp16 scale:
+ *     amax = max |W| over the group
+ *     s    = fp16(amax / 7.5)        IEEE fp32 division, then round to
+ *                                    nearest even in binary16
+ *     c_hi = clamp(rne(W / s), -8, 7)                 hi nibble = c_hi + 8
+ *     c_lo = clamp(rne((W - c_hi * s) / (s / 16)), -8, 7)  lo nibble = c_lo + 8
+ *   (fp32 arithmetic, IEEE divisions; s == 0 gives both codes 0). The draft
+ *   and target weights of the calls above are then W4 = c_hi * s and
+ *   W8 = (16 c_hi + c_lo) * s / 16, and |W8 - W| <= s / 32 wherever neither
+ *   code clamps.
+ *
+ *   W      fp32 [N, K], finite, |W| < 7.5 * 65504 (the fp16 scale must be finite)
+ *   hi, lo uint8 [N, K/2] planes (byte j: column 2j low nibble, 2j+1 high), written
+ *   scale  fp16 bit patterns [N, K/128], written
+ * Sizes as for the linear calls (K a positive multiple of 128, one plane at
+ * most BITNEST_MAX_PLANE_BYTES; M does not apply, K is not bounded by
+ * BITNEST_MAX_K); N == 0 is a no-op.
+ */
+bitnest_status bitnest_pack_nested(const float *W, int N, int K,
+                                   uint8_t *hi, uint8_t *lo, uint16_t *scale, void *stream);
+
+/*
  * The integer partials of the draft and target calls above, from the same kernels' integer
  * loop (for checking; not a fast path).
  *   p_hi  int32 [M, N, K/128] <- P_hi (always written)

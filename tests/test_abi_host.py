@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     for n in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
               "bitnest_linear_partials", "bitnest_status_string", "bitnest_abi_version",
               "bitnest_quant_linear_draft", "bitnest_quant_linear_target", "bitnest_hadamard_quant_act",
-              "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target"):
+              "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
+              "bitnest_pack_nested"):
         assert n in names
 
 
@@ -78,6 +79,10 @@ def _t(xq, xs, g, hi, lo, sc, y, M, N, K):
 
 def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     return bn.lib().bitnest_linear_partials(xq, hi, lo, ph, pl, p8, M, N, K, None)
+
+
+def _pk(W, N, K, hi, lo, sc):
+    return bn.lib().bitnest_pack_nested(W, N, K, hi, lo, sc, None)
 
 
 def _h(x, M, K, b, xq, xs, xr):
@@ -169,6 +174,17 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _hd(NUL, 512, NUL, NUL, NUL, NUL, NUL, 0, 8, 512), bn.OK),
     (lambda: _ht(A, 512, B, NUL, C, D, E, F, 1, 8, 512), bn.EINVAL),
     (lambda: _ht(A, 512, B, MIS, C, D, E, F, 1, 8, 512), bn.EALIGN),
+    # nested packing
+    (lambda: _pk(NUL, 4, 128, B, C, D), bn.EINVAL),
+    (lambda: _pk(A, 4, 128, NUL, C, D), bn.EINVAL),
+    (lambda: _pk(A, 4, 128, B, NUL, D), bn.EINVAL),
+    (lambda: _pk(A, 4, 128, B, C, NUL), bn.EINVAL),
+    (lambda: _pk(A, -1, 128, B, C, D), bn.EINVAL),
+    (lambda: _pk(A, 4, 100, B, C, D), bn.EINVAL),
+    (lambda: _pk(A, 4, 128, B, C, MIS), bn.EALIGN),
+    (lambda: _pk(MIS, 4, 128, B, C, D), bn.EALIGN),
+    (lambda: _pk(A, 300000, 16384, B, C, D), bn.EUNSUPPORTED),
+    (lambda: _pk(NUL, 0, 128, NUL, NUL, NUL), bn.OK),
 ])
 def test_host_validation(call, status):
     assert call() == status

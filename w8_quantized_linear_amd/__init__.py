@@ -21,6 +21,7 @@ __all__ = [
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
     "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
     "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
+    "bitnest_pack_nested",
 ]
 
 GROUP = 128
@@ -65,10 +66,11 @@ def lib() -> ctypes.CDLL:
         L.bitnest_hadamard_quant_act.argtypes = [P, I, I, I, P, P, P, P]
         L.bitnest_hadamard_quant_linear_draft.argtypes = [P, I, P, P, P, P, P, I, I, I, P]
         L.bitnest_hadamard_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
+        L.bitnest_pack_nested.argtypes = [P, I, I, P, P, P, P]
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
-                  "bitnest_hadamard_quant_linear_target"):
+                  "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -296,6 +298,28 @@ def bitnest_hadamard_quant_linear_target(x: torch.Tensor, block: int, hi: torch.
     return _quant_linear(x, hi, lo, scale, 0, y, xq, xs, "bitnest_hadamard_quant_linear_target", block=block)
 
 
+def bitnest_pack_nested(W: torch.Tensor, hi: torch.Tensor | None = None, lo: torch.Tensor | None = None,
+                        scale: torch.Tensor | None = None):
+    """fp32 weights [N, K] -> (hi uint8 [N, K/2], lo uint8 [N, K/2], scale int16 fp16 bits
+    [N, K/128]): the nested packing rule of bitnest.h."""
+    _need(W, "W", torch.float32)
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    N, K = W.shape
+    if hi is None:
+        hi = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if lo is None:
+        lo = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if scale is None:
+        scale = torch.empty((N, K // GROUP), dtype=torch.int16, device=W.device)
+    scale = _scale_tensor(scale)
+    _need(hi, "hi", torch.uint8, (N, K // 2))
+    _need(lo, "lo", torch.uint8, (N, K // 2))
+    _need(scale, "scale", torch.int16, (N, K // GROUP))
+    _call(lib().bitnest_pack_nested(_p(W), N, K, _p(hi), _p(lo), _p(scale), _stream(W)), "bitnest_pack_nested")
+    return hi, lo, scale
+
+
 # Short aliases
 quant_act = bitnest_quant_act
 linear_draft = bitnest_linear_draft
@@ -306,3 +330,4 @@ quant_linear_target = bitnest_quant_linear_target
 hadamard_quant_act = bitnest_hadamard_quant_act
 hadamard_quant_linear_draft = bitnest_hadamard_quant_linear_draft
 hadamard_quant_linear_target = bitnest_hadamard_quant_linear_target
+pack_nested = bitnest_pack_nested

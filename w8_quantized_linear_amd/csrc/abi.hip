@@ -205,6 +205,17 @@ bitnest_status bitnest_hadamard_quant_linear_target(const float *x, int block, c
     return quant_linear(x, 0, block, hi, lo, scale, y, xq, xs, M, N, K, stream);
 }
 
+bitnest_status bitnest_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t *lo, uint16_t *scale,
+                                   void *stream) {
+    if (N < 0 || K <= 0 || K % kGroup != 0) return BITNEST_EINVAL;
+    if (static_cast<long long>(N) * (K / 2) > static_cast<long long>(BITNEST_MAX_PLANE_BYTES))
+        return BITNEST_EUNSUPPORTED;
+    if (N == 0) return BITNEST_OK;                  // empty: pointers may be NULL
+    if (!W || !hi || !lo || !scale) return BITNEST_EINVAL;
+    if (!aligned16(W) || !aligned16(hi) || !aligned16(lo) || !aligned16(scale)) return BITNEST_EALIGN;
+    return to_status(bitnest::launch_pack_nested(W, N, K, hi, lo, scale, static_cast<hipStream_t>(stream)));
+}
+
 bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo, int32_t *p_hi,
                                        int32_t *p_lo, int32_t *p8, int M, int N, int K, void *stream) {
     bitnest_status st = check_sizes(M, N, K);

@@ -53,6 +53,10 @@ hipError_t launch_quant_act(const float *x, int M, int K, int act_group, int8_t 
 hipError_t launch_hadamard_quant_act(const float *x, int M, int K, int block, float rot_scale, int8_t *xq,
                                      float *xs, float *xr, hipStream_t stream);
 
+// fp32 weights [N, K] -> nested planes hi, lo [N, K/2] and fp16 scales [N, K/128].
+hipError_t launch_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t *lo, uint16_t *scale,
+                              hipStream_t stream);
+
 // M <= kGemvMaxM. export_partials selects the integer export instead of y.
 hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream);
 
