@@ -55,12 +55,13 @@ def _load():
         lib.oracle_linear.argtypes = [I, P, P, I, P, P, P, I, I, I, P, I]
         lib.oracle_hadamard_rotate.argtypes = [P, I, I, I, P]
         lib.oracle_pack_nested.argtypes = [P, I, I, P, P, P]
+        lib.oracle_greedy_accept.argtypes = [P, I, I, P, P, P, P]
         lib.oracle_float_to_half.argtypes = [ctypes.c_float]
         lib.oracle_float_to_half.restype = ctypes.c_uint16
         lib.oracle_max_threads.argtypes = []
         for f in ("oracle_unpack_plane", "oracle_quant_act", "oracle_partials",
                   "oracle_dequant", "oracle_linear", "oracle_hadamard_rotate", "oracle_pack_nested",
-                  "oracle_max_threads"):
+                  "oracle_greedy_accept", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -219,3 +220,19 @@ def pack_nested(W: np.ndarray):
     sc = np.empty((N, K // GROUP), np.uint16)
     _check(_load().oracle_pack_nested(_ptr(W), N, K, _ptr(hi), _ptr(lo), _ptr(sc)), "pack_nested")
     return hi, lo, sc
+
+
+def greedy_accept(logits: np.ndarray, draft: np.ndarray):
+    """Greedy verification: logits fp32 [gamma + 1, V], draft int32 [gamma] ->
+    (target argmax per row int32 [gamma + 1], accepted count, next token)."""
+    logits = _c(logits, np.float32)
+    R, V = logits.shape
+    draft = _c(np.asarray(draft, np.int32).reshape(-1), np.int32)
+    if draft.shape != (R - 1,):
+        raise ValueError("draft must hold gamma = R - 1 tokens")
+    targ = np.empty(R, np.int32)
+    n = np.zeros(1, np.int32)
+    nxt = np.zeros(1, np.int32)
+    _check(_load().oracle_greedy_accept(_ptr(logits), R, V, _ptr(draft) if R > 1 else None, _ptr(targ), _ptr(n),
+                                        _ptr(nxt)), "greedy_accept")
+    return targ, int(n[0]), int(nxt[0])

@@ -63,6 +63,15 @@
  *    every division an IEEE fp32 division; s == 0 gives c_hi = c_lo = 0.
  *    Then W4 = c_hi * s and W8 = (16 c_hi + c_lo) * s / 16 per the model
  *    card's formulas, and |W8 - W| <= s / 32 wherever neither code clamps.
+ *  - Greedy verification of a speculative round: model card introduction
+ *    (every draft token is verified with the target, so the output is
+ *    exactly the W8A8 target's greedy output). Reading: the target scores
+ *    the gamma + 1 verify positions (row r: the position after the prefix
+ *    extended by the first r draft tokens); t_r = argmax_v logits[r, v],
+ *    ties to the smallest index; the accepted count n is the length of the
+ *    longest prefix with draft[r] == t_r; the round emits draft[0 .. n-1]
+ *    and then t_n (the target's own token at the first mismatch, or the
+ *    bonus token when all gamma drafts are accepted).
  *
  * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 and fp64
  * operation is the IEEE operation written.
@@ -350,6 +359,27 @@ int oracle_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t *lo, u
             }
         }
     }
+    return ORACLE_OK;
+}
+
+/* Greedy verification, the reading stated at the top. logits fp32 [R, V]
+ * (R = gamma + 1), draft int32 [R - 1]; writes targ int32 [R] (t_r), *n_acc
+ * and *next (t_n). */
+int oracle_greedy_accept(const float *logits, int R, int V, const int32_t *draft,
+                         int32_t *targ, int32_t *n_acc, int32_t *next)
+{
+    if (!logits || !targ || !n_acc || !next || R < 1 || V < 1 || (R > 1 && !draft)) return ORACLE_EINVAL;
+    for (int r = 0; r < R; ++r) {
+        const float *row = logits + (size_t)r * V;
+        int best = 0;
+        for (int v = 1; v < V; ++v)
+            if (row[v] > row[best]) best = v;          /* strict: the first maximum wins */
+        targ[r] = best;
+    }
+    int n = 0;
+    while (n < R - 1 && draft[n] == targ[n]) ++n;
+    *n_acc = n;
+    *next = targ[n];
     return ORACLE_OK;
 }
 

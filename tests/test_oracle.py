@@ -598,3 +598,47 @@ def test_pack_sign_and_power_of_two_symmetry():
     assert np.array_equal(scn, sc)
     ok = (ch > -8) & (ch < 7) & (cl > -8) & (cl < 7) & (np.abs((W / s).astype(np.float64) % 1) != 0.5)
     assert np.array_equal(chn[ok], -ch[ok])
+
+
+# --------------------------------------------------------------------------- greedy verification
+# Reading (model card introduction: the output is exactly the target's greedy
+# output): argmax per verify row, ties to the smallest index, accept the
+# longest matching prefix, emit the target's token after it.
+
+def test_accept_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "accept.json")))
+    logits = np.array(g["logits"], np.float32)
+    for case in g["cases"]:
+        targ, n, nxt = oracle.greedy_accept(logits, np.array(case["draft"], np.int32))
+        assert list(targ) == g["targ"]
+        assert (n, nxt) == (case["n"], case["next"]), case["why"]
+
+
+def test_accept_argmax_is_the_library_argmax():
+    # numpy's argmax returns the first maximum: the same tie rule
+    rng = np.random.default_rng(15)
+    for V in (1, 2, 7, 1000, 128256):
+        logits = rng.standard_normal((4, V)).astype(np.float32)
+        if V > 10:
+            logits[1, [3, V - 1]] = logits[1].max() + 1.0          # a tie at the maximum
+            logits[2] = np.round(logits[2])                          # many ties
+        targ, _, _ = oracle.greedy_accept(logits, np.zeros(3, np.int32))
+        assert np.array_equal(targ, np.argmax(logits, axis=1))
+
+
+def test_accept_emits_the_target_greedy_sequence():
+    # whatever the drafts, the emitted tokens (accepted drafts + next) are the
+    # target's argmax tokens t_0 .. t_n
+    rng = np.random.default_rng(16)
+    for _ in range(200):
+        R = int(rng.integers(1, 9))
+        logits = rng.standard_normal((R, 50)).astype(np.float32)
+        t = np.argmax(logits, axis=1)
+        draft = t[:R - 1].copy()
+        if R > 1 and rng.random() < 0.7:
+            k = int(rng.integers(0, R - 1))
+            draft[k] = (draft[k] + 1 + int(rng.integers(0, 48))) % 50
+        targ, n, nxt = oracle.greedy_accept(logits, draft.astype(np.int32))
+        emitted = list(draft[:n]) + [nxt]
+        assert emitted == list(t[:n + 1])
+        assert n == R - 1 or draft[n] != t[n]

@@ -53,6 +53,12 @@ MUTANTS = {
     "pack hi clamp -7": ("ch = rne_clamp(w[k] / s, -8, 7);", "ch = rne_clamp(w[k] / s, -7, 7);"),
     "half conversion truncates": ("float q = nearbyintf(ldexpf(m, 11));", "float q = floorf(ldexpf(m, 11));"),
     "half subnormal truncates": ("float q = nearbyintf(a * 0x1p24f);", "float q = floorf(a * 0x1p24f);"),
+    "accept argmax ties to the last": ("if (row[v] > row[best]) best = v;", "if (row[v] >= row[best]) best = v;"),
+    "accept next token off by one": ("*next = targ[n];", "*next = targ[n < R - 1 ? n + 1 : n];"),
+    "accept counts all matches": ("while (n < R - 1 && draft[n] == targ[n]) ++n;",
+                                  "for (int r = 0; r < R - 1; ++r) n += draft[r] == targ[r];"),
+    "accept compares with the next row": ("while (n < R - 1 && draft[n] == targ[n]) ++n;",
+                                          "while (n < R - 1 && draft[n] == targ[n + 1]) ++n;"),
 }
 
 
