@@ -58,6 +58,8 @@ def parse_args(argv=None):
                    help="skip the R4 (rotated down_proj input) timing")
     p.add_argument("--no-pack", dest="pack", action="store_false", default=True,
                    help="skip the offline packer timing")
+    p.add_argument("--no-accept", dest="accept", action="store_false", default=True,
+                   help="skip the greedy-verification timing")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -420,6 +422,34 @@ def pack_timing(stack, bn, reps=5):
     return out
 
 
+def accept_timing(bn, V=128256, calls=32, reps=5):
+    """Greedy verification of one round (gamma + 1 = 4 verify rows over the
+    Llama-3 vocabulary, fp32 logits, cold: a different logits buffer each
+    call) replayed from a HIP graph: us per call and GB/s of logits read."""
+    import torch
+    R = GAMMA + 1
+    g = torch.Generator(device="cuda").manual_seed(99)
+    logits = [torch.randn((R, V), generator=g, device="cuda") for _ in range(calls)]
+    draft = torch.zeros((R - 1,), dtype=torch.int32, device="cuda")
+    targ = torch.empty((R,), dtype=torch.int32, device="cuda")
+    res = torch.empty((2,), dtype=torch.int32, device="cuda")
+    graph = capture(lambda: [bn.bitnest_greedy_accept(lg, draft, targ, res) for lg in logits])
+    graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3 / calls)
+    t = sorted(ts)[len(ts) // 2]
+    out = {"rows": R, "vocab": V, "us": round(t * 1e6, 3), "GBps": round(4 * R * V / t / 1e9, 1)}
+    log("greedy accept: %.2f us per call (%d x %d fp32 logits)" % (t * 1e6, R, V))
+    return out
+
+
 def measured_traffic():
     """HBM bytes per linear launch from the committed hardware-counter
     profile (rocprofv3 FETCH_SIZE and WRITE_SIZE of the round's launches,
@@ -536,6 +566,7 @@ def main(argv=None):
     linears = per_linear(stack, bn) if args.per_linear else None
     r4 = r4_timing(stack, bn, steps=min(args.steps, 10)) if args.r4 else None
     pack = pack_timing(stack, bn) if args.pack else None
+    accept = accept_timing(bn) if args.accept else None
 
     verify = None
     batches = [int(v) for v in args.verify_batches.split(",") if v.strip()]
@@ -571,6 +602,7 @@ def main(argv=None):
         "per_linear": linears,
         "r4": r4,
         "pack": pack,
+        "accept": accept,
         "batched_verify": verify,
         "cpu_baseline": cpu,
     }

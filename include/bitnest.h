@@ -222,6 +222,23 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K,
                                    uint8_t *hi, uint8_t *lo, uint16_t *scale, void *stream);
 
 /*
+ * Greedy verification of a speculative round (model card introduction:
+ * every draft token is verified with the target, so the output is exactly
+ * the W8A8 target's greedy output). With the target's logits for the
+ * gamma + 1 verify positions (row r: the position after the prefix extended
+ * by the first r draft tokens):
+ *     targ[r] = argmax_v logits[r, v]   (ties: the smallest index)
+ *     n       = length of the longest prefix with draft[r] == targ[r]
+ *     result  = {n, targ[n]}            the round emits draft[0 .. n-1], then targ[n]
+ *
+ *   logits  fp32 [R, V], R = gamma + 1 (1 <= R <= BITNEST_MAX_M), V >= 1, finite
+ *   draft   int32 [R - 1] (may be NULL when R == 1)
+ *   targ    int32 [R], written;  result int32 [2], written
+ */
+bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft,
+                                     int32_t *targ, int32_t *result, void *stream);
+
+/*
  * The integer partials of the draft and target calls above, from the same kernels' integer
  * loop (for checking; not a fast path).
  *   p_hi  int32 [M, N, K/128] <- P_hi (always written)

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
               "bitnest_linear_partials", "bitnest_status_string", "bitnest_abi_version",
               "bitnest_quant_linear_draft", "bitnest_quant_linear_target", "bitnest_hadamard_quant_act",
               "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
-              "bitnest_pack_nested"):
+              "bitnest_pack_nested", "bitnest_greedy_accept"):
         assert n in names
 
 
@@ -79,6 +79,10 @@ def _t(xq, xs, g, hi, lo, sc, y, M, N, K):
 
 def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     return bn.lib().bitnest_linear_partials(xq, hi, lo, ph, pl, p8, M, N, K, None)
+
+
+def _ga(lg, R, V, dr, tg, res):
+    return bn.lib().bitnest_greedy_accept(lg, R, V, dr, tg, res, None)
 
 
 def _pk(W, N, K, hi, lo, sc):
@@ -185,6 +189,16 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _pk(MIS, 4, 128, B, C, D), bn.EALIGN),
     (lambda: _pk(A, 300000, 16384, B, C, D), bn.EUNSUPPORTED),
     (lambda: _pk(NUL, 0, 128, NUL, NUL, NUL), bn.OK),
+    # greedy verification
+    (lambda: _ga(A, 0, 100, B, C, D), bn.EINVAL),
+    (lambda: _ga(A, 4, 0, B, C, D), bn.EINVAL),
+    (lambda: _ga(A, 33, 100, B, C, D), bn.EUNSUPPORTED),
+    (lambda: _ga(NUL, 4, 100, B, C, D), bn.EINVAL),
+    (lambda: _ga(A, 4, 100, NUL, C, D), bn.EINVAL),
+    (lambda: _ga(A, 4, 100, B, NUL, D), bn.EINVAL),
+    (lambda: _ga(A, 4, 100, B, C, NUL), bn.EINVAL),
+    (lambda: _ga(MIS, 4, 100, B, C, D), bn.EALIGN),
+    (lambda: _ga(A, 4, 100, B, C, MIS), bn.EALIGN),
 ])
 def test_host_validation(call, status):
     assert call() == status

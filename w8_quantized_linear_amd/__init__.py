@@ -21,7 +21,7 @@ __all__ = [
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
     "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
     "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
-    "bitnest_pack_nested",
+    "bitnest_pack_nested", "bitnest_greedy_accept",
 ]
 
 GROUP = 128
@@ -67,10 +67,11 @@ def lib() -> ctypes.CDLL:
         L.bitnest_hadamard_quant_linear_draft.argtypes = [P, I, P, P, P, P, P, I, I, I, P]
         L.bitnest_hadamard_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
         L.bitnest_pack_nested.argtypes = [P, I, I, P, P, P, P]
+        L.bitnest_greedy_accept.argtypes = [P, I, I, P, P, P, P]
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
-                  "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested"):
+                  "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested", "bitnest_greedy_accept"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -320,6 +321,26 @@ def bitnest_pack_nested(W: torch.Tensor, hi: torch.Tensor | None = None, lo: tor
     return hi, lo, scale
 
 
+def bitnest_greedy_accept(logits: torch.Tensor, draft: torch.Tensor, targ: torch.Tensor | None = None,
+                          result: torch.Tensor | None = None):
+    """Greedy verification: logits fp32 [gamma + 1, V], draft int32 [gamma] ->
+    (targ int32 [gamma + 1], result int32 [2] = {accepted count, next token})."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = logits.shape
+    _need(draft, "draft", torch.int32, (R - 1,))
+    if targ is None:
+        targ = torch.empty((R,), dtype=torch.int32, device=logits.device)
+    if result is None:
+        result = torch.empty((2,), dtype=torch.int32, device=logits.device)
+    _need(targ, "targ", torch.int32, (R,))
+    _need(result, "result", torch.int32, (2,))
+    _call(lib().bitnest_greedy_accept(_p(logits), R, V, _p(draft) if R > 1 else None, _p(targ), _p(result),
+                                      _stream(logits)), "bitnest_greedy_accept")
+    return targ, result
+
+
 # Short aliases
 quant_act = bitnest_quant_act
 linear_draft = bitnest_linear_draft
@@ -331,3 +352,4 @@ hadamard_quant_act = bitnest_hadamard_quant_act
 hadamard_quant_linear_draft = bitnest_hadamard_quant_linear_draft
 hadamard_quant_linear_target = bitnest_hadamard_quant_linear_target
 pack_nested = bitnest_pack_nested
+greedy_accept = bitnest_greedy_accept

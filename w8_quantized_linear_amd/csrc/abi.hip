@@ -216,6 +216,17 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K, uint8_t *hi, ui
     return to_status(bitnest::launch_pack_nested(W, N, K, hi, lo, scale, static_cast<hipStream_t>(stream)));
 }
 
+bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
+                                     int32_t *result, void *stream) {
+    if (R < 1 || V < 1) return BITNEST_EINVAL;
+    if (R > BITNEST_MAX_M) return BITNEST_EUNSUPPORTED;
+    if (!logits || !targ || !result || (R > 1 && !draft)) return BITNEST_EINVAL;
+    if (!aligned16(logits) || !aligned16(targ) || !aligned16(result) || (draft && !aligned16(draft)))
+        return BITNEST_EALIGN;
+    return to_status(bitnest::launch_greedy_accept(logits, R, V, draft, targ, result,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo, int32_t *p_hi,
                                        int32_t *p_lo, int32_t *p8, int M, int N, int K, void *stream) {
     bitnest_status st = check_sizes(M, N, K);

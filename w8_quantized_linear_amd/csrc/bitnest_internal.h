@@ -57,6 +57,11 @@ hipError_t launch_hadamard_quant_act(const float *x, int M, int K, int block, fl
 hipError_t launch_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t *lo, uint16_t *scale,
                               hipStream_t stream);
 
+// Greedy verification: target argmax per row of logits [R, V] -> targ [R];
+// result = {accepted count, next token}.
+hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
+                                int32_t *result, hipStream_t stream);
+
 // M <= kGemvMaxM. export_partials selects the integer export instead of y.
 hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream);
 
