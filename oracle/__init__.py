@@ -56,12 +56,13 @@ def _load():
         lib.oracle_hadamard_rotate.argtypes = [P, I, I, I, P]
         lib.oracle_pack_nested.argtypes = [P, I, I, P, P, P]
         lib.oracle_greedy_accept.argtypes = [P, I, I, P, P, P, P]
+        lib.oracle_kv_attention.argtypes = [P, I, I, I, I, P, P, P, P, P, P, P, I]
         lib.oracle_float_to_half.argtypes = [ctypes.c_float]
         lib.oracle_float_to_half.restype = ctypes.c_uint16
         lib.oracle_max_threads.argtypes = []
         for f in ("oracle_unpack_plane", "oracle_quant_act", "oracle_partials",
                   "oracle_dequant", "oracle_linear", "oracle_hadamard_rotate", "oracle_pack_nested",
-                  "oracle_greedy_accept", "oracle_max_threads"):
+                  "oracle_greedy_accept", "oracle_kv_attention", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -236,3 +237,33 @@ def greedy_accept(logits: np.ndarray, draft: np.ndarray):
     _check(_load().oracle_greedy_accept(_ptr(logits), R, V, _ptr(draft) if R > 1 else None, _ptr(targ), _ptr(n),
                                         _ptr(nxt)), "greedy_accept")
     return targ, int(n[0]), int(nxt[0])
+
+
+HEAD_DIM = 128
+
+
+def kv_attention(q: np.ndarray, k_hi: np.ndarray, k_scale: np.ndarray, v_hi: np.ndarray, v_scale: np.ndarray,
+                 k_lo: np.ndarray | None = None, v_lo: np.ndarray | None = None, threads: int = 0) -> np.ndarray:
+    """Decode attention over a nested KV cache (the reading in the C file's
+    header): q fp32 [M, Hq, 128]; planes uint8 [T, Hkv, 64]; scales fp16 bits
+    uint16 [T, Hkv]; KV4 without the lo planes, KV8 with them. -> fp64 [M, Hq, 128]."""
+    q = _c(q, np.float32)
+    M, Hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dimension must be 128")
+    k_hi, v_hi = _c(k_hi, np.uint8), _c(v_hi, np.uint8)
+    k_scale, v_scale = _c(k_scale, np.uint16), _c(v_scale, np.uint16)
+    T, Hkv, half = k_hi.shape
+    if half != HEAD_DIM // 2 or v_hi.shape != k_hi.shape or k_scale.shape != (T, Hkv) or v_scale.shape != (T, Hkv):
+        raise ValueError("KV plane / scale shape mismatch")
+    if (k_lo is None) != (v_lo is None):
+        raise ValueError("give both lo planes or neither")
+    if k_lo is not None:
+        k_lo, v_lo = _c(k_lo, np.uint8), _c(v_lo, np.uint8)
+        if k_lo.shape != k_hi.shape or v_lo.shape != k_hi.shape:
+            raise ValueError("lo plane shape mismatch")
+    out = np.empty((M, Hq, HEAD_DIM), np.float64)
+    _check(_load().oracle_kv_attention(_ptr(q), M, Hq, Hkv, T, _ptr(k_hi), _ptr(k_lo), _ptr(k_scale), _ptr(v_hi),
+                                       _ptr(v_lo), _ptr(v_scale), _ptr(out), threads or max_threads()),
+           "kv_attention")
+    return out

@@ -72,6 +72,18 @@
  *    longest prefix with draft[r] == t_r; the round emits draft[0 .. n-1]
  *    and then t_n (the target's own token at the first mismatch, or the
  *    bonus token when all gamma drafts are accepted).
+ *  - Decode attention over the nested KV cache: recipe table row "KV cache"
+ *    (nested at runtime: the draft reads KV4, the target KV8) and the
+ *    abstract (the progressive-precision design extends to the KV cache).
+ *    The layout, scale granularity and rotation sit in meta.json, which is
+ *    not available. Reading: every (token, KV head) K or V vector of 128
+ *    values is packed like one 128-column group of a weight row (the packing
+ *    above): planes uint8 [T, Hkv, 64], fp16 scale [T, Hkv]; KV4 = (hi - 8)
+ *    * s and KV8 = (16 (hi - 8) + (lo - 8)) * s / 16, the weight formulas.
+ *    The M query tokens are the last M positions of the sequence (the verify
+ *    batch): token i sees positions t <= T - M + i. Query head h reads KV
+ *    head h / (Hq / Hkv) (grouped-query attention). Scores q . k / sqrt(128),
+ *    softmax over the visible positions, output sum_t p_t v_t, in fp64.
  *
  * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 and fp64
  * operation is the IEEE operation written.
@@ -380,6 +392,67 @@ int oracle_greedy_accept(const float *logits, int R, int V, const int32_t *draft
     while (n < R - 1 && draft[n] == targ[n]) ++n;
     *n_acc = n;
     *next = targ[n];
+    return ORACLE_OK;
+}
+
+#define ORACLE_HEAD_DIM 128
+
+/* One KV value (token t, KV head h, dimension j) of a nested cache:
+ * hi / lo planes [T, Hkv, 64], scale [T, Hkv]; lo == NULL reads KV4. */
+static double kv_value(const uint8_t *hi, const uint8_t *lo, const uint16_t *scale, int Hkv,
+                       int t, int h, int j)
+{
+    const size_t row = (size_t)t * Hkv + h;
+    const uint8_t *hr = hi + row * (ORACLE_HEAD_DIM / 2);
+    double s = oracle_half_to_double(scale[row]);
+    int ch = nibble_at(hr, j) - 8;
+    if (!lo) return (double)ch * s;
+    int cl = nibble_at(lo + row * (ORACLE_HEAD_DIM / 2), j) - 8;
+    return (double)(16 * ch + cl) * s / 16.0;
+}
+
+/* The attention reading stated at the top. q fp32 [M, Hq, 128]; out fp64
+ * [M, Hq, 128]. k_lo and v_lo both NULL (KV4) or both given (KV8). */
+int oracle_kv_attention(const float *q, int M, int Hq, int Hkv, int T,
+                        const uint8_t *k_hi, const uint8_t *k_lo, const uint16_t *k_scale,
+                        const uint8_t *v_hi, const uint8_t *v_lo, const uint16_t *v_scale,
+                        double *out, int nthreads)
+{
+    if (!q || !k_hi || !k_scale || !v_hi || !v_scale || !out) return ORACLE_EINVAL;
+    if (M < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || T < M) return ORACLE_EINVAL;
+    if ((k_lo == NULL) != (v_lo == NULL)) return ORACLE_EINVAL;
+    if (nthreads <= 0) nthreads = 1;
+    const int G = Hq / Hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)ORACLE_HEAD_DIM);
+#pragma omp parallel for schedule(static) num_threads(nthreads) collapse(2)
+    for (int i = 0; i < M; ++i) {
+        for (int h = 0; h < Hq; ++h) {
+            const int hk = h / G;
+            const int visible = T - M + i + 1;          /* positions 0 .. T - M + i */
+            const float *qv = q + ((size_t)i * Hq + h) * ORACLE_HEAD_DIM;
+            double *o = out + ((size_t)i * Hq + h) * ORACLE_HEAD_DIM;
+            double mx = -INFINITY;
+            for (int t = 0; t < visible; ++t) {
+                double sc = 0.0;
+                for (int j = 0; j < ORACLE_HEAD_DIM; ++j)
+                    sc += (double)qv[j] * kv_value(k_hi, k_lo, k_scale, Hkv, t, hk, j);
+                sc *= inv_sqrt_d;
+                if (sc > mx) mx = sc;
+            }
+            double den = 0.0;
+            for (int j = 0; j < ORACLE_HEAD_DIM; ++j) o[j] = 0.0;
+            for (int t = 0; t < visible; ++t) {
+                double sc = 0.0;
+                for (int j = 0; j < ORACLE_HEAD_DIM; ++j)
+                    sc += (double)qv[j] * kv_value(k_hi, k_lo, k_scale, Hkv, t, hk, j);
+                double p = exp(sc * inv_sqrt_d - mx);
+                den += p;
+                for (int j = 0; j < ORACLE_HEAD_DIM; ++j)
+                    o[j] += p * kv_value(v_hi, v_lo, v_scale, Hkv, t, hk, j);
+            }
+            for (int j = 0; j < ORACLE_HEAD_DIM; ++j) o[j] /= den;
+        }
+    }
     return ORACLE_OK;
 }
 

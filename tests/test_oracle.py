@@ -642,3 +642,122 @@ def test_accept_emits_the_target_greedy_sequence():
         emitted = list(draft[:n]) + [nxt]
         assert emitted == list(t[:n + 1])
         assert n == R - 1 or draft[n] != t[n]
+
+
+# --------------------------------------------------------------------------- nested KV cache attention
+# Reading (recipe table row "KV cache": the draft reads KV4, the target KV8):
+# every (token, KV head) vector of 128 values packed like one weight group;
+# grouped-query heads, causal visibility for the M query tokens, scores / sqrt(128).
+
+def _kv_cache(Kf, Vf):
+    """fp32 [T, Hkv, 128] K and V -> nested planes [T, Hkv, 64] and scales [T, Hkv] (the packer)."""
+    T, Hkv, d = Kf.shape
+    out = []
+    for X in (Kf, Vf):
+        hi, lo, sc = oracle.pack_nested(np.ascontiguousarray(X.reshape(T * Hkv, d)))
+        out.append((hi.reshape(T, Hkv, d // 2), lo.reshape(T, Hkv, d // 2), sc.reshape(T, Hkv)))
+    return out
+
+
+def _kv_dequant(planes, lo=True):
+    hi, lo_p, sc = planes
+    T, Hkv, half = hi.shape
+    W = oracle.dequant(hi.reshape(T * Hkv, half), sc.reshape(T * Hkv, 1), lo_p.reshape(T * Hkv, half) if lo else None)
+    return W.reshape(T, Hkv, 2 * half)
+
+
+def _attn(q, kc, vc, lo=True):
+    return oracle.kv_attention(q, kc[0], kc[2], vc[0], vc[2], kc[1] if lo else None, vc[1] if lo else None)
+
+
+def test_kv_single_visible_position_returns_its_value():
+    rng = np.random.default_rng(20)
+    Kf = rng.standard_normal((4, 2, 128)).astype(np.float32)
+    Vf = rng.standard_normal((4, 2, 128)).astype(np.float32)
+    kc, vc = _kv_cache(Kf, Vf)
+    q = rng.standard_normal((4, 4, 128)).astype(np.float32)       # M = T = 4: token 0 sees position 0 only
+    for lo in (False, True):
+        out = _attn(q, kc, vc, lo)
+        V = _kv_dequant(vc, lo)
+        for h in range(4):
+            assert np.array_equal(out[0, h], V[0, h // 2])
+
+
+def test_kv_equal_keys_average_the_values():
+    rng = np.random.default_rng(21)
+    T, Hkv = 37, 2
+    Kf = np.repeat(rng.standard_normal((1, Hkv, 128)), T, axis=0).astype(np.float32)
+    Vf = (rng.standard_normal((T, Hkv, 128)) * rng.uniform(0.1, 3, size=(T, Hkv, 1))).astype(np.float32)
+    kc, vc = _kv_cache(Kf, Vf)
+    q = rng.standard_normal((3, 8, 128)).astype(np.float32)
+    out = _attn(q, kc, vc)
+    V = _kv_dequant(vc)
+    for i in range(3):
+        vis = T - 3 + i + 1
+        for h in range(8):
+            assert np.allclose(out[i, h], V[:vis, h // 4].mean(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_kv_two_positions_closed_form_weights():
+    # softmax over two scores: weights 1 / (1 + r) and r / (1 + r) with
+    # r = exp((q.k1 - q.k0) / sqrt(128))
+    rng = np.random.default_rng(22)
+    Kf = (rng.standard_normal((2, 1, 128)) * 0.2).astype(np.float32)
+    Vf = rng.standard_normal((2, 1, 128)).astype(np.float32)
+    kc, vc = _kv_cache(Kf, Vf)
+    q = rng.standard_normal((1, 1, 128)).astype(np.float32)
+    K, V = _kv_dequant(kc), _kv_dequant(vc)
+    qd = q[0, 0].astype(np.float64)
+    r = np.exp((qd @ K[1, 0] - qd @ K[0, 0]) / np.sqrt(128.0))
+    want = (V[0, 0] + r * V[1, 0]) / (1 + r)
+    assert np.allclose(_attn(q, kc, vc)[0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_kv_peaked_score_selects_one_position():
+    rng = np.random.default_rng(23)
+    T = 50
+    Kf = np.zeros((T, 1, 128), np.float32)
+    Kf[17, 0, :] = 2.0                                  # only position 17 aligns with q
+    Vf = rng.standard_normal((T, 1, 128)).astype(np.float32)
+    kc, vc = _kv_cache(Kf, Vf)
+    q = np.full((1, 1, 128), 2.0, np.float32)           # score of 17: 512 / sqrt(128) = 45
+    out = _attn(q, kc, vc)
+    assert np.allclose(out[0, 0], _kv_dequant(vc)[17, 0], rtol=0, atol=1e-12)
+
+
+def test_kv_grouped_heads_and_causality():
+    rng = np.random.default_rng(24)
+    T, Hkv, Hq, M = 40, 2, 8, 4
+    Kf = rng.standard_normal((T, Hkv, 128)).astype(np.float32)
+    Vf = np.zeros((T, Hkv, 128), np.float32)
+    Vf[:, 0, :] = 1.5                                   # KV head 0's values all 1.5, head 1's all -0.75
+    Vf[:, 1, :] = -0.75
+    kc, vc = _kv_cache(Kf, Vf)
+    q = rng.standard_normal((M, Hq, 128)).astype(np.float32)
+    out = _attn(q, kc, vc)
+    V = _kv_dequant(vc)
+    for h in range(Hq):                                  # query heads 0-3 read KV head 0, 4-7 KV head 1
+        assert np.allclose(out[:, h], V[0, h // 4, 0], rtol=1e-12)
+    # token i of an M-token call equals a one-token call on the cache cut after position T - M + i
+    Vr = rng.standard_normal((T, Hkv, 128)).astype(np.float32)
+    kc, vc = _kv_cache(Kf, Vr)
+    out = _attn(q, kc, vc)
+    for i in range(M):
+        n = T - M + i + 1
+        cut = [tuple(a[:n] for a in kc), tuple(a[:n] for a in vc)]
+        one = _attn(q[i:i + 1], cut[0], cut[1])
+        assert np.array_equal(out[i], one[0])
+
+
+def test_kv4_equals_kv8_when_lo_is_8_and_value_scaling():
+    rng = np.random.default_rng(25)
+    Kf = rng.standard_normal((30, 2, 128)).astype(np.float32)
+    Vf = rng.standard_normal((30, 2, 128)).astype(np.float32)
+    kc, vc = _kv_cache(Kf, Vf)
+    q = rng.standard_normal((2, 4, 128)).astype(np.float32)
+    k8 = (kc[0], np.full_like(kc[1], 0x88), kc[2])
+    v8 = (vc[0], np.full_like(vc[1], 0x88), vc[2])
+    assert np.array_equal(_attn(q, k8, v8, lo=True), _attn(q, kc, vc, lo=False))
+    # doubling every value scale doubles the output exactly
+    v2 = (vc[0], vc[1], (vc[2].view(np.float16) * np.float16(2)).view(np.uint16))
+    assert np.array_equal(_attn(q, kc, v2), 2 * _attn(q, kc, vc))

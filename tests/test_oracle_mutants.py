@@ -59,6 +59,14 @@ MUTANTS = {
                                   "for (int r = 0; r < R - 1; ++r) n += draft[r] == targ[r];"),
     "accept compares with the next row": ("while (n < R - 1 && draft[n] == targ[n]) ++n;",
                                           "while (n < R - 1 && draft[n] == targ[n + 1]) ++n;"),
+    "kv grouped heads interleaved": ("const int hk = h / G;", "const int hk = h % Hkv;"),
+    "kv score scale dropped": ("double p = exp(sc * inv_sqrt_d - mx);", "double p = exp(sc - mx);"),
+    "kv causal off by one": ("const int visible = T - M + i + 1;", "const int visible = T - M + i;"),
+    "kv sees the whole cache": ("const int visible = T - M + i + 1;", "const int visible = T;"),
+    "kv8 residual offset 7": ("int cl = nibble_at(lo + row * (ORACLE_HEAD_DIM / 2), j) - 8;",
+                              "int cl = nibble_at(lo + row * (ORACLE_HEAD_DIM / 2), j) - 7;"),
+    "kv scale head-major": ("const size_t row = (size_t)t * Hkv + h;\n    const uint8_t *hr = hi + row * (ORACLE_HEAD_DIM / 2);\n    double s = oracle_half_to_double(scale[row]);",
+                            "const size_t row = (size_t)t * Hkv + h;\n    const uint8_t *hr = hi + row * (ORACLE_HEAD_DIM / 2);\n    double s = oracle_half_to_double(scale[(size_t)h * Hkv + t % Hkv]);"),
 }
 
 
