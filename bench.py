@@ -60,6 +60,8 @@ def parse_args(argv=None):
                    help="skip the offline packer timing")
     p.add_argument("--no-accept", dest="accept", action="store_false", default=True,
                    help="skip the greedy-verification timing")
+    p.add_argument("--no-kv", dest="kv", action="store_false", default=True,
+                   help="skip the nested-KV attention timing")
     p.add_argument("--unfused", action="store_true",
                    help="quantise with its own launch before each linear instead of the fused call")
     p.add_argument("--verbose", action="store_true")
@@ -450,6 +452,57 @@ def accept_timing(bn, V=128256, calls=32, reps=5):
     return out
 
 
+def kv_timing(bn, layers=32, contexts=(2048, 8192, 32768), Hq=32, Hkv=8, reps=5):
+    """Decode attention over the nested KV cache at the Llama-3-8B head layout
+    (32 query heads, 8 KV heads, head dimension 128): the draft step (M=1,
+    KV4: hi planes) and the verify pass (M=4, KV8: hi+lo planes), one call
+    per layer over `layers` distinct caches (cold) from a HIP graph. us per
+    call and GB/s of cache bytes read (planes + fp16 scales of K and V)."""
+    import torch
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(77)
+    for T in contexts:
+        caches = []
+        for _ in range(layers):
+            planes = [torch.randint(0, 256, (T, Hkv, 64), dtype=torch.uint8, device="cuda", generator=g)
+                      for _ in range(4)]                 # k_hi, k_lo, v_hi, v_lo
+            scales = [(torch.rand((T, Hkv), device="cuda", generator=g) * 0.02 + 0.005).half().view(torch.int16)
+                      for _ in range(2)]
+            caches.append((planes, scales))
+        res = {}
+        for M, kv8 in ((1, False), (GAMMA + 1, True)):
+            q = torch.randn((M, Hq, 128), device="cuda", generator=g)
+            o = torch.empty((M, Hq, 128), device="cuda")
+            work = torch.empty((bn.bitnest_kv_attention_workspace_bytes(M, Hq, T),), dtype=torch.uint8, device="cuda")
+
+            def fn(q=q, o=o, work=work, kv8=kv8):
+                for (kh, kl, vh, vl), (ks, vs) in caches:
+                    bn.bitnest_kv_attention(q, kh, ks, vh, vs, kl if kv8 else None, vl if kv8 else None,
+                                            out=o, work=work)
+            graph = capture(fn)
+            graph.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3 / layers)
+            t = sorted(ts)[len(ts) // 2]
+            nbytes = 2 * T * Hkv * (64 * (2 if kv8 else 1) + 2)
+            key = "draft_M1_KV4" if not kv8 else "verify_M4_KV8"
+            res[key] = {"us": round(t * 1e6, 2), "cache_bytes": nbytes, "GBps": round(nbytes / t / 1e9, 1),
+                        "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        out[str(T)] = res
+        del caches
+        torch.cuda.empty_cache()
+        log("nested KV attention T=%d: %s" % (T, ", ".join("%s %.2f us %.0f GB/s" % (k, v["us"], v["GBps"])
+                                                            for k, v in res.items())))
+    return out
+
+
 def measured_traffic():
     """HBM bytes per linear launch from the committed hardware-counter
     profile (rocprofv3 FETCH_SIZE and WRITE_SIZE of the round's launches,
@@ -567,6 +620,7 @@ def main(argv=None):
     r4 = r4_timing(stack, bn, steps=min(args.steps, 10)) if args.r4 else None
     pack = pack_timing(stack, bn) if args.pack else None
     accept = accept_timing(bn) if args.accept else None
+    kv = kv_timing(bn) if args.kv else None
 
     verify = None
     batches = [int(v) for v in args.verify_batches.split(",") if v.strip()]
@@ -603,6 +657,7 @@ def main(argv=None):
         "r4": r4,
         "pack": pack,
         "accept": accept,
+        "kv_attention": kv,
         "batched_verify": verify,
         "cpu_baseline": cpu,
     }

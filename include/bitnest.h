@@ -44,6 +44,7 @@
 #ifndef BITNEST_H
 #define BITNEST_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -56,6 +57,8 @@ extern "C" {
 #define BITNEST_MAX_K 16384    /* largest input width */
 #define BITNEST_MAX_PLANE_BYTES 2147483647LL  /* largest N * K / 2 (bytes of one plane) */
 #define BITNEST_MAX_ROT_BLOCK 512 /* largest rotation block of the R4 calls */
+#define BITNEST_KV_HEAD_DIM 128   /* head dimension of the nested KV cache */
+#define BITNEST_KV_MAX_ROWS 16    /* most query rows (M x Hq / Hkv) per KV head */
 
 typedef enum bitnest_status {
     BITNEST_OK = 0,
@@ -237,6 +240,44 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K,
  */
 bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft,
                                      int32_t *targ, int32_t *result, void *stream);
+
+/*
+ * Decode attention over the nested KV cache (model card, recipe table row
+ * "KV cache": nested at runtime, the draft reads KV4 and the target KV8;
+ * abstract: the progressive-precision design extends to the KV cache for
+ * long contexts). The layout and the scale granularity are in meta.json,
+ * which the pages do not reproduce; this library's reading:
+ *   - every (token t, KV head h) vector of K or V, 128 values, is packed like
+ *     one 128-column group of a weight row: planes uint8 [T, Hkv, 64] (byte
+ *     j: dimension 2j low nibble, 2j+1 high nibble) and one fp16 scale
+ *     [T, Hkv]. Writing the cache is bitnest_pack_nested with N = T Hkv rows
+ *     of K = 128 columns;
+ *   - KV4 = (hi - 8) s, KV8 = (16 (hi - 8) + (lo - 8)) s / 16, the weight
+ *     formulas;
+ *   - the M query tokens are the last M positions of the sequence (the
+ *     verify batch; M = 1 for a draft step): token i sees positions
+ *     t <= T - M + i;
+ *   - query head hq reads KV head hq / (Hq / Hkv) (grouped-query attention);
+ *   - out[i, hq] = sum_t softmax_t(q[i, hq] . k[t] / sqrt(128)) v[t].
+ * Computed in fp32 over chunks of 64 positions, merged exactly as the
+ * softmax requires; |out - out_exact| stays within a few 1e-6 of the values'
+ * magnitude.
+ *
+ *   q        fp32 [M, Hq, 128]
+ *   k_hi, v_hi  uint8 [T, Hkv, 64];  k_lo, v_lo  the same or both NULL (KV4)
+ *   k_scale, v_scale  fp16 bit patterns [T, Hkv]
+ *   out      fp32 [M, Hq, 128], written
+ *   work     caller-owned scratch of at least
+ *            bitnest_kv_attention_workspace_bytes(M, Hq, T) bytes, overwritten
+ * Limits: M >= 1, Hq a multiple of Hkv, M Hq / Hkv <= BITNEST_KV_MAX_ROWS,
+ * M <= T, T Hkv 64 < 2^31; otherwise BITNEST_EINVAL / BITNEST_EUNSUPPORTED.
+ */
+size_t bitnest_kv_attention_workspace_bytes(int M, int Hq, int T);
+
+bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int T,
+                                    const uint8_t *k_hi, const uint8_t *k_lo, const uint16_t *k_scale,
+                                    const uint8_t *v_hi, const uint8_t *v_lo, const uint16_t *v_scale,
+                                    float *out, void *work, size_t work_bytes, void *stream);
 
 /*
  * The integer partials of the draft and target calls above, from the same kernels' integer

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
               "bitnest_linear_partials", "bitnest_status_string", "bitnest_abi_version",
               "bitnest_quant_linear_draft", "bitnest_quant_linear_target", "bitnest_hadamard_quant_act",
               "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
-              "bitnest_pack_nested", "bitnest_greedy_accept"):
+              "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_kv_attention",
+              "bitnest_kv_attention_workspace_bytes"):
         assert n in names
 
 
@@ -79,6 +80,10 @@ def _t(xq, xs, g, hi, lo, sc, y, M, N, K):
 
 def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     return bn.lib().bitnest_linear_partials(xq, hi, lo, ph, pl, p8, M, N, K, None)
+
+
+def _kv(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb):
+    return bn.lib().bitnest_kv_attention(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb, None)
 
 
 def _ga(lg, R, V, dr, tg, res):
@@ -199,9 +204,26 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _ga(A, 4, 100, B, C, NUL), bn.EINVAL),
     (lambda: _ga(MIS, 4, 100, B, C, D), bn.EALIGN),
     (lambda: _ga(A, 4, 100, B, C, MIS), bn.EALIGN),
+    # nested KV attention: every case fails validation (none may launch)
+    (lambda: _kv(A, 0, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
+    (lambda: _kv(A, 4, 30, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
+    (lambda: _kv(A, 4, 32, 8, 3, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
+    (lambda: _kv(A, 8, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EUNSUPPORTED),
+    (lambda: _kv(A, 1, 32, 8, 1 << 23, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
+    (lambda: _kv(NUL, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
+    (lambda: _kv(A, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, NUL, 1 << 20), bn.EINVAL),
+    (lambda: _kv(A, 4, 32, 8, 100, B, C, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
+    (lambda: _kv(A, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1000), bn.EINVAL),
+    (lambda: _kv(MIS, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EALIGN),
+    (lambda: _kv(A, 4, 32, 8, 100, B, NUL, C, D, NUL, E, MIS, A, 1 << 20), bn.EALIGN),
 ])
 def test_host_validation(call, status):
     assert call() == status
+def test_kv_workspace_size():
+    # 64-position chunks x (M Hq) rows x (128 values + maximum + sum) floats
+    assert bn.bitnest_kv_attention_workspace_bytes(4, 32, 100) == 2 * 4 * 32 * 130 * 4
+    assert bn.bitnest_kv_attention_workspace_bytes(1, 32, 2048) == 32 * 32 * 130 * 4
+    assert bn.bitnest_kv_attention_workspace_bytes(0, 32, 10) == 0
 
 
 def test_binding_rejects_cpu_tensors():

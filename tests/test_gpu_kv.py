@@ -1,0 +1,114 @@
+"""GPU parity of decode attention over the nested KV cache (draft KV4, target
+KV8) against the CPU oracle, through the C ABI.
+
+The caches are packed on the CPU by the oracle and uploaded, so every input
+of the oracle is its own. Bar: max|out - out_oracle| <= 1e-5 * max|V| over the
+visible values (the oracle is fp64; the kernel accumulates in fp32 and merges
+64-position chunks). Invariants checked bit for bit on the GPU: KV8 with lo
+planes of 8 equals KV4; token i of an M-token call equals a one-token call on
+the cache cut after its last visible position.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w8_quantized_linear_amd as bn
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bn.lib()
+
+
+def _cache(T, Hkv, seed, spread=1.0):
+    rng = np.random.default_rng(seed)
+    out = []
+    for scale in (spread, 1.0):
+        X = (rng.standard_normal((T, Hkv, 128)) * scale * rng.uniform(0.3, 2.0, size=(T, Hkv, 1))).astype(np.float32)
+        hi, lo, sc = oracle.pack_nested(X.reshape(T * Hkv, 128))
+        out.append((hi.reshape(T, Hkv, 64), lo.reshape(T, Hkv, 64), sc.reshape(T, Hkv)))
+    return out          # (K planes, V planes)
+
+
+def _run(q, kc, vc, kv8):
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = bn.bitnest_kv_attention(d(q), d(kc[0]), d(kc[2]).view(torch.int16), d(vc[0]), d(vc[2]).view(torch.int16),
+                                  d(kc[1]) if kv8 else None, d(vc[1]) if kv8 else None)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _ref(q, kc, vc, kv8):
+    return oracle.kv_attention(q, kc[0], kc[2], vc[0], vc[2], kc[1] if kv8 else None, vc[1] if kv8 else None)
+
+
+def _vmax(vc, kv8):
+    hi, lo, sc = vc
+    T, Hkv, _ = hi.shape
+    V = oracle.dequant(hi.reshape(T * Hkv, 64), sc.reshape(T * Hkv, 1), lo.reshape(T * Hkv, 64) if kv8 else None)
+    return np.abs(V).max()
+
+
+@pytest.mark.parametrize("M,Hq,Hkv,T", [
+    (1, 32, 8, 2048), (4, 32, 8, 2048), (4, 32, 8, 100), (4, 32, 8, 4), (1, 8, 8, 1), (2, 16, 2, 300),
+    (3, 12, 4, 257), (1, 32, 8, 8192), (4, 32, 8, 64), (4, 32, 8, 65), (1, 4, 1, 129),
+])
+@pytest.mark.parametrize("kv8", [False, True])
+def test_kv_attention_matches_oracle(M, Hq, Hkv, T, kv8):
+    kc, vc = _cache(T, Hkv, seed=M * 1000 + T, spread=0.5)
+    q = np.random.default_rng(T).standard_normal((M, Hq, 128)).astype(np.float32)
+    got = _run(q, kc, vc, kv8)
+    want = _ref(q, kc, vc, kv8)
+    err = np.abs(got - want).max()
+    assert err <= TOL * _vmax(vc, kv8), (err, _vmax(vc, kv8))
+
+
+def test_kv_peaked_scores():
+    # large scores (sharp softmax) stay accurate
+    kc, vc = _cache(512, 8, seed=7, spread=3.0)
+    q = (np.random.default_rng(8).standard_normal((4, 32, 128)) * 3).astype(np.float32)
+    got = _run(q, kc, vc, True)
+    want = _ref(q, kc, vc, True)
+    assert np.abs(got - want).max() <= TOL * _vmax(vc, True)
+
+
+def test_kv8_with_lo_8_equals_kv4_on_gpu():
+    kc, vc = _cache(300, 8, seed=9)
+    q = np.random.default_rng(9).standard_normal((4, 32, 128)).astype(np.float32)
+    k8 = (kc[0], np.full_like(kc[1], 0x88), kc[2])
+    v8 = (vc[0], np.full_like(vc[1], 0x88), vc[2])
+    a = _run(q, k8, v8, True)
+    b = _run(q, kc, vc, False)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_kv_token_rows_equal_one_token_calls_on_the_cut_cache():
+    T, M = 200, 4
+    kc, vc = _cache(T, 8, seed=10)
+    q = np.random.default_rng(10).standard_normal((M, 32, 128)).astype(np.float32)
+    full = _run(q, kc, vc, True)
+    for i in range(M):
+        n = T - M + i + 1
+        cut_k = tuple(np.ascontiguousarray(a[:n]) for a in kc)
+        cut_v = tuple(np.ascontiguousarray(a[:n]) for a in vc)
+        one = _run(q[i:i + 1], cut_k, cut_v, True)
+        assert np.array_equal(full[i].view(np.uint32), one[0].view(np.uint32))
+
+
+def test_kv_pack_writes_the_oracle_planes():
+    # the cache write path (bitnest_pack_nested over T Hkv vectors)
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((33, 8, 128)).astype(np.float32)
+    hi, lo, sc = bn.kv_pack(torch.from_numpy(X).cuda())
+    torch.cuda.synchronize()
+    h_r, l_r, s_r = oracle.pack_nested(X.reshape(33 * 8, 128))
+    assert np.array_equal(hi.cpu().numpy().reshape(33 * 8, 64), h_r)
+    assert np.array_equal(lo.cpu().numpy().reshape(33 * 8, 64), l_r)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16).reshape(33 * 8, 1), s_r)

@@ -21,7 +21,8 @@ __all__ = [
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
     "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
     "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
-    "bitnest_pack_nested", "bitnest_greedy_accept",
+    "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_kv_attention",
+    "bitnest_kv_attention_workspace_bytes", "kv_pack",
 ]
 
 GROUP = 128
@@ -68,10 +69,14 @@ def lib() -> ctypes.CDLL:
         L.bitnest_hadamard_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
         L.bitnest_pack_nested.argtypes = [P, I, I, P, P, P, P]
         L.bitnest_greedy_accept.argtypes = [P, I, I, P, P, P, P]
+        L.bitnest_kv_attention_workspace_bytes.argtypes = [I, I, I]
+        L.bitnest_kv_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.bitnest_kv_attention.argtypes = [P, I, I, I, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
-                  "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested", "bitnest_greedy_accept"):
+                  "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested", "bitnest_greedy_accept",
+                  "bitnest_kv_attention"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -341,6 +346,60 @@ def bitnest_greedy_accept(logits: torch.Tensor, draft: torch.Tensor, targ: torch
     return targ, result
 
 
+KV_HEAD_DIM = 128
+
+
+def kv_pack(kv: torch.Tensor):
+    """fp32 K or V entries [T, Hkv, 128] -> nested cache planes (hi, lo uint8 [T, Hkv, 64],
+    scale int16 fp16 bits [T, Hkv]): bitnest_pack_nested over the T Hkv vectors."""
+    _need(kv, "kv", torch.float32)
+    if kv.dim() != 3 or kv.shape[2] != KV_HEAD_DIM:
+        raise ValueError("kv must be [T, Hkv, 128]")
+    T, Hkv, _ = kv.shape
+    hi, lo, sc = bitnest_pack_nested(kv.reshape(T * Hkv, KV_HEAD_DIM))
+    return hi.view(T, Hkv, KV_HEAD_DIM // 2), lo.view(T, Hkv, KV_HEAD_DIM // 2), sc.view(T, Hkv)
+
+
+def bitnest_kv_attention_workspace_bytes(M: int, Hq: int, T: int) -> int:
+    return int(lib().bitnest_kv_attention_workspace_bytes(M, Hq, T))
+
+
+def bitnest_kv_attention(q: torch.Tensor, k_hi: torch.Tensor, k_scale: torch.Tensor, v_hi: torch.Tensor,
+                         v_scale: torch.Tensor, k_lo: torch.Tensor | None = None, v_lo: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None, work: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention over the nested KV cache: q fp32 [M, Hq, 128]; planes uint8
+    [T, Hkv, 64]; scales [T, Hkv] (fp16 or their int16 bits); KV4 without the lo
+    planes, KV8 with them. Returns out fp32 [M, Hq, 128]."""
+    _need(q, "q", torch.float32)
+    if q.dim() != 3 or q.shape[2] != KV_HEAD_DIM:
+        raise ValueError("q must be [M, Hq, 128]")
+    M, Hq, _ = q.shape
+    _need(k_hi, "k_hi", torch.uint8)
+    if k_hi.dim() != 3 or k_hi.shape[2] != KV_HEAD_DIM // 2:
+        raise ValueError("k_hi must be [T, Hkv, 64]")
+    T, Hkv, _ = k_hi.shape
+    k_scale, v_scale = _scale_tensor(k_scale), _scale_tensor(v_scale)
+    _need(v_hi, "v_hi", torch.uint8, tuple(k_hi.shape))
+    _need(k_scale, "k_scale", torch.int16, (T, Hkv))
+    _need(v_scale, "v_scale", torch.int16, (T, Hkv))
+    if (k_lo is None) != (v_lo is None):
+        raise ValueError("give both lo planes or neither")
+    if k_lo is not None:
+        _need(k_lo, "k_lo", torch.uint8, tuple(k_hi.shape))
+        _need(v_lo, "v_lo", torch.uint8, tuple(k_hi.shape))
+    if out is None:
+        out = torch.empty((M, Hq, KV_HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (M, Hq, KV_HEAD_DIM))
+    need = bitnest_kv_attention_workspace_bytes(M, Hq, T)
+    if work is None:
+        work = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    _need(work, "work", work.dtype)
+    _call(lib().bitnest_kv_attention(_p(q), M, Hq, Hkv, T, _p(k_hi), _p(k_lo), _p(k_scale), _p(v_hi), _p(v_lo),
+                                     _p(v_scale), _p(out), _p(work), work.numel() * work.element_size(),
+                                     _stream(q)), "bitnest_kv_attention")
+    return out
+
+
 # Short aliases
 quant_act = bitnest_quant_act
 linear_draft = bitnest_linear_draft
@@ -353,3 +412,4 @@ hadamard_quant_linear_draft = bitnest_hadamard_quant_linear_draft
 hadamard_quant_linear_target = bitnest_hadamard_quant_linear_target
 pack_nested = bitnest_pack_nested
 greedy_accept = bitnest_greedy_accept
+kv_attention = bitnest_kv_attention

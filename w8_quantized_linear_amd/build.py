@@ -19,7 +19,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitnest.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "quant_act.hip", "gemv_planes.hip", "verify_mfma.hip", "pack_nested.hip", "accept.hip"]
+SOURCES = ["abi.hip", "quant_act.hip", "gemv_planes.hip", "verify_mfma.hip", "pack_nested.hip", "accept.hip", "kv_attention.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -62,6 +62,24 @@ hipError_t launch_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t
 hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
                                 int32_t *result, hipStream_t stream);
 
+// Decode attention over the nested KV cache.
+constexpr int kKvHeadDim = 128;
+constexpr int kKvChunk = 64;        // positions per partial
+constexpr int kKvMaxRows = 16;      // M x (Hq / Hkv) query rows per KV head
+struct KvArgs {
+    const float *q;                 // [M, Hq, 128]
+    const uint8_t *k_hi, *k_lo;     // [T, Hkv, 64] (k_lo, v_lo null: KV4)
+    const uint16_t *k_scale;        // [T, Hkv]
+    const uint8_t *v_hi, *v_lo;
+    const uint16_t *v_scale;
+    float *out;                     // [M, Hq, 128]
+    float *work;                    // kv_attention_workspace_bytes(M, Hq, T)
+    int M, Hq, Hkv, T;
+    float inv_sqrt_d;
+};
+size_t kv_attention_workspace_bytes(int M, int Hq, int T);
+hipError_t launch_kv_attention(const KvArgs &a, hipStream_t stream);
+
 // M <= kGemvMaxM. export_partials selects the integer export instead of y.
 hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t stream);
 
