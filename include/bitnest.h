@@ -259,9 +259,10 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  *     t <= T - M + i;
  *   - query head hq reads KV head hq / (Hq / Hkv) (grouped-query attention);
  *   - out[i, hq] = sum_t softmax_t(q[i, hq] . k[t] / sqrt(128)) v[t].
- * Computed in fp32 over chunks of 64 positions, merged exactly as the
- * softmax requires; |out - out_exact| stays within a few 1e-6 of the values'
- * magnitude.
+ * Computed in fp32: the sequence is cut into splits (runs of 64-position
+ * chunks, their number sized to the device), each split keeps a running
+ * softmax, and the splits are merged exactly as the softmax requires;
+ * |out - out_exact| stays within a few 1e-6 of the values' magnitude.
  *
  *   q        fp32 [M, Hq, 128]
  *   k_hi, v_hi  uint8 [T, Hkv, 64];  k_lo, v_lo  the same or both NULL (KV4)
@@ -269,6 +270,9 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  *   out      fp32 [M, Hq, 128], written
  *   work     caller-owned scratch of at least
  *            bitnest_kv_attention_workspace_bytes(M, Hq, T) bytes, overwritten
+ *            (= min(ceil(T / 64), 512) M Hq 130 floats: per split and query
+ *            row, 128 output values, the maximum and the sum; 0 for
+ *            M, Hq or T below 1)
  * Limits: M >= 1, Hq a multiple of Hkv, M Hq / Hkv <= BITNEST_KV_MAX_ROWS,
  * M <= T, T Hkv 64 < 2^31; otherwise BITNEST_EINVAL / BITNEST_EUNSUPPORTED.
  */

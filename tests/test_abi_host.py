@@ -220,9 +220,12 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
 def test_host_validation(call, status):
     assert call() == status
 def test_kv_workspace_size():
-    # 64-position chunks x (M Hq) rows x (128 values + maximum + sum) floats
+    # at most one split per 64-position chunk and at most 512 splits, each
+    # with (M Hq) rows x (128 values + maximum + sum) floats
     assert bn.bitnest_kv_attention_workspace_bytes(4, 32, 100) == 2 * 4 * 32 * 130 * 4
     assert bn.bitnest_kv_attention_workspace_bytes(1, 32, 2048) == 32 * 32 * 130 * 4
+    assert bn.bitnest_kv_attention_workspace_bytes(1, 32, 64 * 512) == 512 * 32 * 130 * 4
+    assert bn.bitnest_kv_attention_workspace_bytes(4, 32, 131072) == 512 * 4 * 32 * 130 * 4
     assert bn.bitnest_kv_attention_workspace_bytes(0, 32, 10) == 0
 
 

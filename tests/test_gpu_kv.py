@@ -3,8 +3,9 @@ KV8) against the CPU oracle, through the C ABI.
 
 The caches are packed on the CPU by the oracle and uploaded, so every input
 of the oracle is its own. Bar: max|out - out_oracle| <= 1e-5 * max|V| over the
-visible values (the oracle is fp64; the kernel accumulates in fp32 and merges
-64-position chunks). Invariants checked bit for bit on the GPU: KV8 with lo
+visible values (the oracle is fp64; the kernel accumulates in fp32 over
+splits of 64-position chunks with a running softmax, then merges the
+splits). Invariants checked bit for bit on the GPU: KV8 with lo
 planes of 8 equals KV4; token i of an M-token call equals a one-token call on
 the cache cut after its last visible position.
 """
@@ -59,6 +60,9 @@ def _vmax(vc, kv8):
 @pytest.mark.parametrize("M,Hq,Hkv,T", [
     (1, 32, 8, 2048), (4, 32, 8, 2048), (4, 32, 8, 100), (4, 32, 8, 4), (1, 8, 8, 1), (2, 16, 2, 300),
     (3, 12, 4, 257), (1, 32, 8, 8192), (4, 32, 8, 64), (4, 32, 8, 65), (1, 4, 1, 129),
+    # long contexts: several 64-position chunks per split, ragged tails, and
+    # (one KV head) hundreds of splits up to the 512 cap
+    (1, 32, 8, 32768), (4, 32, 8, 20001), (1, 4, 1, 40000), (2, 8, 1, 32768), (4, 16, 16, 12345),
 ])
 @pytest.mark.parametrize("kv8", [False, True])
 def test_kv_attention_matches_oracle(M, Hq, Hkv, T, kv8):
