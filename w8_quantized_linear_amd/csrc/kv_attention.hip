@@ -10,17 +10,14 @@
 // Split over the sequence (the draft reads only the hi planes, the target
 // both; both are HBM streams of a few bytes per position and head):
 //  - kv_attn_split_kernel: one workgroup per (split, KV head), for all M x G
-//    query rows of that head; a split is a contiguous run of 64-position
-//    chunks, and the number of splits is sized to about two workgroups per
-//    compute unit. Per chunk: its K and V rows are staged in LDS (one
-//    16-byte load per thread and plane, all in flight together, the next
-//    chunk's loads issued while the current one is scored); scores with one
-//    lane per position (unsigned nibble codes, the offset applied once per
-//    score through the row's sum of q); the running softmax per row
-//    (maximum, sum and the rescale of what is accumulated, DPP reductions);
-//    P.V with one lane per two dimensions and each wave on 16 positions.
-//    At the end the waves' outputs are summed in a fixed order and the
-//    split's (output, maximum, sum) per row go to the caller's workspace.
+//    (<= 16) query rows of that head; a split is a contiguous run of
+//    64-position chunks, their number sized to about two workgroups per
+//    compute unit. Each wave walks every fourth 16-position tile of the
+//    split on its own (the next tile's loads in flight while the current one
+//    is consumed): scores and P.V on the fp16 matrix cores, a running
+//    softmax per query row. The four waves then merge in LDS in a fixed
+//    order and the split's (output, maximum, sum) per row go to the caller's
+//    workspace.
 //  - kv_attn_combine_kernel: one workgroup per query row merges the splits:
 //    out = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m), the splits' weights
 //    staged in LDS and the partial loads spread over four thread groups.
@@ -31,257 +28,336 @@ namespace bitnest {
 namespace {
 
 constexpr int kD = kKvHeadDim;       // 128
-constexpr int kC = kKvChunk;         // 64 positions per workgroup
+constexpr int kC = kKvChunk;         // 64 positions: one step of the four waves
+constexpr int kTile = 16;            // positions per wave step
+constexpr int kRows = kKvMaxRows;    // 16 query rows: one matrix-core tile
 constexpr int kKvThreads = 256;
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-    v += dpp_f32<kDppQuadSwap1>(v);
-    v += dpp_f32<kDppQuadSwap2>(v);
-    v += dpp_f32<kDppRowRor4>(v);
-    v += dpp_f32<kDppRowRor8>(v);
-    const int b = __builtin_bit_cast(int, v);
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-    return (r0 + r1) + (r2 + r3);
-}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// byte n of x as a float (v_cvt_f32_ubyteN)
-template <int n>
-__device__ __forceinline__ float ubyte_f(unsigned x) {
-    return static_cast<float>((x >> (8 * n)) & 0xFFu);
-}
+constexpr unsigned kF16Base = 0x64006400u;      // fp16 1024.0 in both halves
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), static_cast<int>(bytes),
                                              0x00020000);
 }
 
-// RW: query rows per wave (the M x G rows padded to 4 RW). KV8: read the lo
-// planes. cps: chunks per split.
-template <int RW, bool KV8>
-__global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(const KvArgs a, int cps) {
-    constexpr int RP = 4 * RW;
-    constexpr int NPL = KV8 ? 4 : 2;
-    __shared__ float sq[RP][kD];
-    __shared__ float sqs[RP];
-    __shared__ float sp[kC][RP];
-    __shared__ float sm[RP], sl[RP], sa[RP];           // running maximum and sum, this chunk's rescale
-    __shared__ float so[4][RP][kD];
-    // the chunk's planes: [plane][position][16-byte piece] (a fifth piece of
-    // padding spreads the per-position reads over the banks), planes K hi,
-    // V hi, then K lo, V lo
-    __shared__ u32x4 sk[NPL][kC][5];
-    __shared__ float sks[kC], svs[kC];
+// Two fp16 halves 1024 + b (b a small integer) -> b - off, exact.
+__device__ __forceinline__ unsigned f16_unbias(unsigned bits, float off) {
+    const f16x2 o = {static_cast<_Float16>(-off), static_cast<_Float16>(-off)};
+    return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, bits) + o);
+}
+
+// (x0, x1) -> three fp16 pairs p1 + p2 + p3: each piece rounds toward zero
+// and the remainders are exact in fp32, so the pieces carry 33 bits of
+// |x| < 2^15 (below 2^-24 the last piece floors at the fp16 subnormals).
+__device__ __forceinline__ void split3(float x0, float x1, unsigned &p1, unsigned &p2, unsigned &p3) {
+    const auto a = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    const float r0 = x0 - static_cast<float>(a[0]), r1 = x1 - static_cast<float>(a[1]);
+    const auto b = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+    const float s0 = r0 - static_cast<float>(b[0]), s1 = r1 - static_cast<float>(b[1]);
+    const auto c = __builtin_amdgcn_cvt_pkrtz(s0, s1);
+    p1 = __builtin_bit_cast(unsigned, a);
+    p2 = __builtin_bit_cast(unsigned, b);
+    p3 = __builtin_bit_cast(unsigned, c);
+}
+
+// Maximum / sum over the four lanes c, c + 16, c + 32, c + 48 (the same in
+// all four, the sum in one fixed order).
+__device__ __forceinline__ float quad_group_max(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(r[0])), __builtin_bit_cast(float, static_cast<unsigned>(r[1])));
+    const unsigned w = __builtin_bit_cast(unsigned, v);
+    const auto t = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(t[0])), __builtin_bit_cast(float, static_cast<unsigned>(t[1])));
+}
+__device__ __forceinline__ float quad_group_sum(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, static_cast<unsigned>(r[0])) + __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, v);
+    const auto t = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return __builtin_bit_cast(float, static_cast<unsigned>(t[0])) + __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
+}
+
+// Both products on the fp16 matrix cores, every code exact in fp16 and the
+// fp32 operands (q, p v_scale) split into three fp16 pieces after a power-of-
+// two scaling, so the products are those of fp32 values to about 2^-32.
+//
+// Lanes: c = lane % 16, g = lane / 16. Per 16-position tile of a wave:
+//  - scores S^T = K Q^T (v_mfma_f32_16x16x32_f16, 4 steps of 32 dimensions):
+//    A = K codes, lane = position c, dimensions 32 g + 8 s + {j, j + 4} in
+//    pair j of step s (one 16-byte load per plane); B = q pieces, lane =
+//    query row c, the same dimensions. The accumulator gives lane (c, g) the
+//    scores of query row c at positions 4 g + i.
+//  - softmax per query row over the tile (the four lanes of a row combine
+//    with lane swaps), running maximum and sum per row.
+//  - P.V as O^T = V^T P^T (v_mfma_f32_16x16x16f16 per 16-dimension tile t):
+//    B = the score accumulator's own layout (lane = query row c, k =
+//    positions 4 g + i), A = V codes, lane = dimension 8 c + t at positions
+//    4 g + i (dword c of four position rows). The accumulator gives lane
+//    (c, g) the outputs of query row c at dimensions 32 g + 8 i + t.
+// Codes: KV4 u - 8, KV8 16 (u_hi - 8) + (u_lo - 8), both from fp16 1024 + code
+// bits and one packed subtraction. The KV8 codes with lo = 8 are 16 times the
+// KV4 codes and every scale factor differs by a power of two, so the two
+// paths then agree bit for bit.
+template <bool KV8>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void kv_attn_split_kernel(const KvArgs a, int cps) {
+    __shared__ float sO[4][kRows][kD];
+    __shared__ float sM[4][kRows], sL[4][kRows], sW[4][kRows];
+    __shared__ float4 ssc[4][2][kTile / 4];          // per wave: K and V scales of its tile
 
     const int s = blockIdx.x, h = blockIdx.y;
     const int splits = gridDim.x;
-    const int nchunks = (a.T + kC - 1) / kC;
-    const int c_begin = s * cps;
-    const int c_end = min(nchunks, c_begin + cps);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, g = lane >> 4;
     const int G = a.Hq / a.Hkv;
     const int R = a.M * G;
+    const int span0 = s * cps * kC;
+    const int span1 = min(a.T, span0 + cps * kC);
 
-    // staging: thread = (position, 16-byte piece); positions past T read as
-    // zero (an offset past the end of the buffer)
+    // query row c: token c / G, head h G + c % G; last visible position
+    const bool rv = c < R;
+    const int tok = rv ? c / G : 0;
+    const int limit = rv ? a.T - a.M + tok : -1;
+
+    // tile loads: this lane's K row (position c, bytes 16 g ..), its V dwords
+    // (dword c of positions 4 g + i) and the K / V scales of position c
     const unsigned cache_bytes = static_cast<unsigned>(a.T) * a.Hkv * (kD / 2);
-    const int spos = threadIdx.x >> 2, piece = threadIdx.x & 3;
-    const uint8_t *src[4] = {a.k_hi, a.v_hi, a.k_lo, a.v_lo};
-    u32x4 v[NPL];
-    unsigned short ks = 0, vs = 0;                     // fp16 bits: converted when stored, so that
-    auto fetch = [&](int c) {                          // nothing waits on the loads before then
-        const int t = c * kC + spos;
-        const unsigned off = t < a.T ? (static_cast<unsigned>(t) * a.Hkv + h) * (kD / 2) + 16 * piece : cache_bytes;
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl)
-            v[pl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(src[pl], cache_bytes), off, 0, 0));
-        const int ts = c * kC + threadIdx.x;
-        unsigned short k1 = 0, v1 = 0;
-        if (threadIdx.x < kC && ts < a.T) {
-            k1 = a.k_scale[static_cast<size_t>(ts) * a.Hkv + h];
-            v1 = a.v_scale[static_cast<size_t>(ts) * a.Hkv + h];
-        }
-        ks = k1;
-        vs = v1;
+    const unsigned scale_bytes = static_cast<unsigned>(a.T) * a.Hkv * 2;
+    const __amdgpu_buffer_rsrc_t rkh = rsrc(a.k_hi, cache_bytes), rvh = rsrc(a.v_hi, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rkl = rsrc(KV8 ? a.k_lo : a.k_hi, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rvl = rsrc(KV8 ? a.v_lo : a.v_hi, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rks = rsrc(a.k_scale, scale_bytes), rvs = rsrc(a.v_scale, scale_bytes);
+    struct Stage {
+        u32x4 kh, kl;
+        unsigned vh[4], vl[4];
+        unsigned short ks, vs;
     };
-    if (c_begin < c_end) fetch(c_begin);
-
-    // query rows r = i G + g (token i, query head h G + g), and their sums
-    for (int idx = threadIdx.x; idx < RP * kD; idx += kKvThreads) {
-        const int r = idx / kD, j = idx - (idx / kD) * kD;
-        float x = 0.0f;
-        if (r < R) {
-            const int i = r / G, g = r - (r / G) * G;
-            x = a.q[(static_cast<size_t>(i) * a.Hq + h * G + g) * kD + j];
+    // every load is issued (past the split: an offset past the end, which
+    // reads zero and touches no memory), so the waits count exactly
+    auto fetch = [&](Stage &st, int p0) {
+        const int tk = p0 + c;
+        const unsigned ok = tk < span1 ? (static_cast<unsigned>(tk) * a.Hkv + h) * (kD / 2) + 16 * g : cache_bytes;
+        st.kh = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkh, ok, 0, 0));
+        if (KV8) st.kl = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkl, ok, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tv = p0 + 4 * g + i;
+            const unsigned ov = tv < span1 ? (static_cast<unsigned>(tv) * a.Hkv + h) * (kD / 2) + 4 * c : cache_bytes;
+            st.vh[i] = __builtin_amdgcn_raw_buffer_load_b32(rvh, ov, 0, 0);
+            if (KV8) st.vl[i] = __builtin_amdgcn_raw_buffer_load_b32(rvl, ov, 0, 0);
         }
-        sq[r][j] = x;
+        const unsigned os = tk < span1 ? (static_cast<unsigned>(tk) * a.Hkv + h) * 2 : scale_bytes;
+        st.ks = __builtin_amdgcn_raw_buffer_load_b16(rks, os, 0, 0);
+        st.vs = __builtin_amdgcn_raw_buffer_load_b16(rvs, os, 0, 0);
+    };
+    // q row c (rows past R read row 0 and are zeroed), loaded before the
+    // tiles so that waiting for it leaves the tile loads in flight
+    float x[32];
+    {
+        const int qr = rv ? c : 0;
+        const float4 *src = reinterpret_cast<const float4 *>(
+            a.q + (static_cast<size_t>(qr / G) * a.Hq + h * G + qr % G) * kD + 32 * g);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float4 v = src[k];
+            x[4 * k] = rv ? v.x : 0.0f; x[4 * k + 1] = rv ? v.y : 0.0f;
+            x[4 * k + 2] = rv ? v.z : 0.0f; x[4 * k + 3] = rv ? v.w : 0.0f;
+        }
     }
-    if (threadIdx.x < RP) {
-        sm[threadIdx.x] = -__builtin_inff();
-        sl[threadIdx.x] = 0.0f;
+    // a ring of two tiles in flight while one is consumed
+    Stage s0, s1;
+    if (!KV8) s0.kl = s1.kl = u32x4{0, 0, 0, 0};
+    int p0 = span0 + kTile * wave;
+    fetch(s0, p0);
+    fetch(s1, p0 + kC);
+
+    // q row c scaled by 2^kq (its largest |q| in [2^14, 2^15)), three fp16
+    // pieces per step s and pair j (dimensions 32 g + 8 s + j, + j + 4)
+    unsigned qb[3][4][4];
+    float gscale;                                    // 2^-kq / sqrt(128) (/ 16: KV8 codes)
+    {
+        float mx = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) mx = fmaxf(mx, fabsf(x[k]));
+        mx = quad_group_max(mx);
+        const int kq = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                split3(__builtin_amdgcn_ldexpf(x[8 * st + j], kq), __builtin_amdgcn_ldexpf(x[8 * st + j + 4], kq),
+                       qb[0][st][j], qb[1][st][j], qb[2][st][j]);
+        gscale = __builtin_amdgcn_ldexpf(a.inv_sqrt_d, -kq) * (KV8 ? 0.0625f : 1.0f);
+    }
+
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+    int kt_run = 0;                                  // the accumulators hold O 2^kt_run
+    f32x4 o[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto consume = [&](const Stage &cur, int p0) {
+        const u32x4 ckh = cur.kh, ckl = cur.kl;
+        const unsigned *cvh = cur.vh, *cvl = cur.vl;
+        const unsigned short cks = cur.ks, cvs = cur.vs;
+
+        // scales of positions 4 g + i through the wave's LDS slot
+        reinterpret_cast<float *>(ssc[wave][0])[c] = half_bits_to_float(cks);
+        reinterpret_cast<float *>(ssc[wave][1])[c] = half_bits_to_float(cvs);
+        const float4 ksv = ssc[wave][0][g];
+        const float4 vsv = ssc[wave][1][g];
+
+        // ---- scores
+        f16x8 ka[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            unsigned pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (KV8) {
+                    // byte of each half: 16 u_hi + u_lo of dimensions j, j + 4
+                    const unsigned lo = ((ckl[st] >> (4 * j)) & 0x000F000Fu) | kF16Base;
+                    const unsigned hi = j == 0 ? (ckh[st] << 4) : (ckh[st] >> (4 * j - 4));
+                    pr[j] = f16_unbias((hi & 0x00F000F0u) | lo, 1024.0f + 136.0f);
+                } else {
+                    pr[j] = f16_unbias(((ckh[st] >> (4 * j)) & 0x000F000Fu) | kF16Base, 1024.0f + 8.0f);
+                }
+            }
+            ka[st] = __builtin_bit_cast(f16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+        }
+        f32x4 d[3];
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc) {
+            d[pc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                d[pc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    ka[st], __builtin_bit_cast(f16x8, u32x4{qb[pc][st][0], qb[pc][st][1], qb[pc][st][2], qb[pc][st][3]}),
+                    d[pc], 0, 0, 0);
+        }
+
+        // ---- running softmax of query row c over the tile
+        const float ks4[4] = {ksv.x, ksv.y, ksv.z, ksv.w};
+        const float vs4[4] = {vsv.x, vsv.y, vsv.z, vsv.w};
+        float sc[4];
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool vis = p0 + 4 * g + i <= limit;
+            const float dot = (d[2][i] + d[1][i]) + d[0][i];
+            sc[i] = vis ? dot * (ks4[i] * gscale) : -__builtin_inff();
+            tmax = fmaxf(tmax, sc[i]);
+        }
+        const float m_new = fmaxf(m_run, quad_group_max(tmax));
+        const float alpha = m_run == -__builtin_inff() ? 0.0f : expf(m_run - m_new);
+        float pv[4], psum = 0.0f, pmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = sc[i] == -__builtin_inff() ? 0.0f : expf(sc[i] - m_new);
+            psum += p;
+            pv[i] = p * vs4[i];
+            pmax = fmaxf(pmax, fabsf(pv[i]));
+        }
+        l_run = fmaf(l_run, alpha, quad_group_sum(psum));
+        m_run = m_new;
+        // p v_scale of the row scaled into [2^14, 2^15) and split into pieces;
+        // the accumulators follow the row's scale
+        pmax = quad_group_max(pmax);
+        const int kt = pmax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(pmax) : kt_run;
+        const float f = __builtin_amdgcn_ldexpf(alpha, kt - kt_run);
+        kt_run = kt;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] *= f;
+        unsigned pb[3][2];
+        split3(__builtin_amdgcn_ldexpf(pv[0], kt), __builtin_amdgcn_ldexpf(pv[1], kt), pb[0][0], pb[1][0], pb[2][0]);
+        split3(__builtin_amdgcn_ldexpf(pv[2], kt), __builtin_amdgcn_ldexpf(pv[3], kt), pb[0][1], pb[1][1], pb[2][1]);
+
+        // ---- P.V: V codes of dimension 8 c + t at positions 4 g + i
+        unsigned ve[4], vo[4];                          // codes of even / odd nibbles as bytes (KV8: full codes)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (KV8) {
+                ve[i] = ((cvh[i] & 0x0F0F0F0Fu) << 4) | (cvl[i] & 0x0F0F0F0Fu);
+                vo[i] = (cvh[i] & 0xF0F0F0F0u) | ((cvl[i] >> 4) & 0x0F0F0F0Fu);
+            } else {
+                ve[i] = cvh[i] & 0x0F0F0F0Fu;
+                vo[i] = (cvh[i] >> 4) & 0x0F0F0F0Fu;
+            }
+        }
+        f16x4 va[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            // byte t / 2 of positions (0, 1) and (2, 3) into the low bytes of the halves
+            const unsigned sel = 0x0C000C00u | ((4u + t / 2) << 16) | static_cast<unsigned>(t / 2);
+            const unsigned *src = (t & 1) ? vo : ve;
+            const unsigned b01 = __builtin_amdgcn_perm(src[1], src[0], sel) | kF16Base;
+            const unsigned b23 = __builtin_amdgcn_perm(src[3], src[2], sel) | kF16Base;
+            const float off = 1024.0f + (KV8 ? 136.0f : 8.0f);
+            va[t] = __builtin_bit_cast(f16x4, u32x2{f16_unbias(b01, off), f16_unbias(b23, off)});
+        }
+#pragma unroll
+        for (int pc = 2; pc >= 0; --pc) {
+            const f16x4 bp = __builtin_bit_cast(f16x4, u32x2{pb[pc][0], pb[pc][1]});
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[t], bp, o[t], 0, 0, 0);
+        }
+    };
+#pragma unroll 1
+    for (; p0 < span1; p0 += 2 * kC) {
+        {
+            const Stage cur = s0;
+            fetch(s0, p0 + 2 * kC);
+            consume(cur, p0);
+        }
+        if (p0 + kC >= span1) break;                 // uniform
+        {
+            const Stage cur = s1;
+            fetch(s1, p0 + 3 * kC);
+            consume(cur, p0 + kC);
+        }
+    }
+
+    // ---- the four waves' (maximum, sum, output) merged in a fixed order
+    const float unscale = __builtin_amdgcn_ldexpf(KV8 ? 0.0625f : 1.0f, -kt_run);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float4 *dst = reinterpret_cast<float4 *>(&sO[wave][c][32 * g + 8 * i]);
+        dst[0] = float4{o[0][i] * unscale, o[1][i] * unscale, o[2][i] * unscale, o[3][i] * unscale};
+        dst[1] = float4{o[4][i] * unscale, o[5][i] * unscale, o[6][i] * unscale, o[7][i] * unscale};
+    }
+    if (g == 0) {
+        sM[wave][c] = m_run;
+        sL[wave][c] = l_run;
     }
     __syncthreads();
-    if (threadIdx.x < RP) {
-        float sum = 0.0f;
-        for (int j = 0; j < kD; ++j) sum += sq[threadIdx.x][j];
-        sqs[threadIdx.x] = sum;
-    }
-
-    float o0[RP], o1[RP];
+    if (threadIdx.x < kRows) {
+        const int r = threadIdx.x;
+        float mx = sM[0][r];
 #pragma unroll
-    for (int r = 0; r < RP; ++r) o0[r] = o1[r] = 0.0f;
-
-#pragma unroll 1
-    for (int c = c_begin; c < c_end; ++c) {
-        const int t0 = c * kC;
-        __syncthreads();                               // sqs ready; the previous chunk's P.V is done
+        for (int w = 1; w < 4; ++w) mx = fmaxf(mx, sM[w][r]);
 #pragma unroll
-        for (int pl = 0; pl < NPL; ++pl) sk[pl][spos][piece] = v[pl];
-        if (threadIdx.x < kC) {
-            sks[threadIdx.x] = half_bits_to_float(ks);
-            svs[threadIdx.x] = half_bits_to_float(vs);
-        }
-        __syncthreads();
-        if (c + 1 < c_end) fetch(c + 1);               // in flight while this chunk is consumed
-
-        // ---- scores: lane = position t0 + lane, wave = rows [RW wave, RW wave + RW)
-        const int t = t0 + lane;
-        const bool tv = t < a.T;
-        const float kscale = sks[lane];
-        // acc: sum u_hi q; accl (KV8): sum u_lo q, accumulated like the row
-        // sum of q (j ascending), so that lo = 8 makes it exactly 8 sum(q)
-        float acc[RW], accl[RW];
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) acc[rr] = accl[rr] = 0.0f;
-        // 16 bytes of each plane (32 columns) per step; a rolled loop keeps
-        // the broadcast query reads of one step live at a time
-#pragma unroll 1
-        for (int cc = 0; cc < 4; ++cc) {
-            const u32x4 kh = sk[0][lane][cc];
-            const u32x4 kl = KV8 ? sk[2][lane][cc] : kh;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // dword w: columns 32 cc + 8 w + 0 .. 7 (low nibble = even column)
-                const unsigned hw = kh[w];
-                const unsigned he = hw & 0x0F0F0F0Fu, ho = (hw >> 4) & 0x0F0F0F0Fu;
-                float u[8];
-                u[0] = ubyte_f<0>(he); u[1] = ubyte_f<0>(ho);
-                u[2] = ubyte_f<1>(he); u[3] = ubyte_f<1>(ho);
-                u[4] = ubyte_f<2>(he); u[5] = ubyte_f<2>(ho);
-                u[6] = ubyte_f<3>(he); u[7] = ubyte_f<3>(ho);
-                float ul[8];
-                if (KV8) {
-                    const unsigned lw = kl[w];
-                    const unsigned le = lw & 0x0F0F0F0Fu, lo = (lw >> 4) & 0x0F0F0F0Fu;
-                    ul[0] = ubyte_f<0>(le); ul[1] = ubyte_f<0>(lo);
-                    ul[2] = ubyte_f<1>(le); ul[3] = ubyte_f<1>(lo);
-                    ul[4] = ubyte_f<2>(le); ul[5] = ubyte_f<2>(lo);
-                    ul[6] = ubyte_f<3>(le); ul[7] = ubyte_f<3>(lo);
-                }
-                const int j0 = 32 * cc + 8 * w;
-#pragma unroll
-                for (int rr = 0; rr < RW; ++rr) {
-                    const float4 qa = *reinterpret_cast<const float4 *>(&sq[wave * RW + rr][j0]);
-                    const float4 qb = *reinterpret_cast<const float4 *>(&sq[wave * RW + rr][j0 + 4]);
-                    float d = acc[rr];
-                    d = fmaf(u[0], qa.x, d); d = fmaf(u[1], qa.y, d); d = fmaf(u[2], qa.z, d); d = fmaf(u[3], qa.w, d);
-                    d = fmaf(u[4], qb.x, d); d = fmaf(u[5], qb.y, d); d = fmaf(u[6], qb.z, d); d = fmaf(u[7], qb.w, d);
-                    acc[rr] = d;
-                    if (KV8) {
-                        float e = accl[rr];
-                        e = fmaf(ul[0], qa.x, e); e = fmaf(ul[1], qa.y, e); e = fmaf(ul[2], qa.z, e); e = fmaf(ul[3], qa.w, e);
-                        e = fmaf(ul[4], qb.x, e); e = fmaf(ul[5], qb.y, e); e = fmaf(ul[6], qb.z, e); e = fmaf(ul[7], qb.w, e);
-                        accl[rr] = e;
-                    }
-                }
-            }
-        }
-        // KV4 score = (sum u_hi q - 8 sum q) * s / sqrt(128); KV8 score =
-        // (16 (sum u_hi q - 8 sum q) + (sum u_lo q - 8 sum q)) * (s / 16) / sqrt(128):
-        // with lo = 8 the second term is exactly 0 and the power-of-two
-        // factors cancel exactly, so KV8 then equals KV4 bit for bit.
-        // Running softmax: m' = max(m, chunk max), what is accumulated is
-        // rescaled by e^(m - m') (0 while nothing is seen yet).
-        const float sfac = kscale * a.inv_sqrt_d;
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) {
-            const int r = wave * RW + rr;
-            const int i = r / G;
-            const bool vis = tv && r < R && t <= a.T - a.M + i;
-            float dot = acc[rr] - 8.0f * sqs[r];
-            if (KV8) dot = 16.0f * dot + (accl[rr] - 8.0f * sqs[r]);
-            const float sc = vis ? dot * (KV8 ? sfac * 0.0625f : sfac) : -__builtin_inff();
-            const float mo = sm[r];
-            const float mn = fmaxf(mo, wave_max_dpp_f32(sc));
-            float p = 0.0f;
-            if (mn != -__builtin_inff()) p = vis ? expf(sc - mn) : 0.0f;
-            const float alpha = mo == -__builtin_inff() ? 0.0f : expf(mo - mn);
-            const float l = fmaf(sl[r], alpha, wave_sum_f32(p));
-            sp[lane][r] = p;
-            if (lane == 0) {
-                sm[r] = mn;
-                sl[r] = l;
-                sa[r] = alpha;
-            }
-        }
-        __syncthreads();
-
-        // ---- P.V: wave = positions t0 + 16 wave + k, lane = dimensions 2 lane, 2 lane + 1
-#pragma unroll
-        for (int r4 = 0; r4 < RP; r4 += 4) {
-            const float4 al = *reinterpret_cast<const float4 *>(&sa[r4]);
-            o0[r4] *= al.x; o1[r4] *= al.x;
-            o0[r4 + 1] *= al.y; o1[r4 + 1] *= al.y;
-            o0[r4 + 2] *= al.z; o1[r4 + 2] *= al.z;
-            o0[r4 + 3] *= al.w; o1[r4 + 3] *= al.w;
-        }
-        // (a rolled loop: unrolled, the compiler hoists every position's
-        // loads and runs out of registers)
-#pragma unroll 1
-        for (int k = 0; k < kC / 4; ++k) {
-            const int pl = (kC / 4) * wave + k;
-            if (t0 + pl >= a.T) break;                 // uniform
-            const float vsc = svs[pl];
-            const unsigned vb = reinterpret_cast<const uint8_t *>(&sk[1][pl][0])[lane];
-            float v0, v1;
-            if (KV8) {
-                const unsigned lb = reinterpret_cast<const uint8_t *>(&sk[3][pl][0])[lane];
-                v0 = static_cast<float>(16 * (static_cast<int>(vb & 15u) - 8) + (static_cast<int>(lb & 15u) - 8)) *
-                     (vsc * 0.0625f);
-                v1 = static_cast<float>(16 * (static_cast<int>(vb >> 4) - 8) + (static_cast<int>(lb >> 4) - 8)) *
-                     (vsc * 0.0625f);
-            } else {
-                v0 = static_cast<float>(static_cast<int>(vb & 15u) - 8) * vsc;
-                v1 = static_cast<float>(static_cast<int>(vb >> 4) - 8) * vsc;
-            }
-#pragma unroll
-            for (int r4 = 0; r4 < RP; r4 += 4) {
-                const float4 p = *reinterpret_cast<const float4 *>(&sp[pl][r4]);
-                o0[r4] = fmaf(p.x, v0, o0[r4]); o1[r4] = fmaf(p.x, v1, o1[r4]);
-                o0[r4 + 1] = fmaf(p.y, v0, o0[r4 + 1]); o1[r4 + 1] = fmaf(p.y, v1, o1[r4 + 1]);
-                o0[r4 + 2] = fmaf(p.z, v0, o0[r4 + 2]); o1[r4 + 2] = fmaf(p.z, v1, o1[r4 + 2]);
-                o0[r4 + 3] = fmaf(p.w, v0, o0[r4 + 3]); o1[r4 + 3] = fmaf(p.w, v1, o1[r4 + 3]);
-            }
-        }
-    }
-
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-        so[wave][r][2 * lane] = o0[r];
-        so[wave][r][2 * lane + 1] = o1[r];
+        for (int w = 0; w < 4; ++w) sW[w][r] = sM[w][r] == -__builtin_inff() ? 0.0f : expf(sM[w][r] - mx);
+        sM[0][r] = mx;
+        sL[0][r] = ((sL[0][r] * sW[0][r] + sL[1][r] * sW[1][r]) + sL[2][r] * sW[2][r]) + sL[3][r] * sW[3][r];
     }
     __syncthreads();
     float *part = a.work + (static_cast<size_t>(h) * splits + s) * R * (kD + 2);
     for (int idx = threadIdx.x; idx < R * kD; idx += kKvThreads) {
         const int r = idx / kD, j = idx - (idx / kD) * kD;
-        part[r * (kD + 2) + j] = ((so[0][r][j] + so[1][r][j]) + so[2][r][j]) + so[3][r][j];
+        part[r * (kD + 2) + j] = ((sO[0][r][j] * sW[0][r] + sO[1][r][j] * sW[1][r]) + sO[2][r][j] * sW[2][r]) +
+                                 sO[3][r][j] * sW[3][r];
     }
     if (threadIdx.x < R) {
-        part[threadIdx.x * (kD + 2) + kD] = sm[threadIdx.x];
-        part[threadIdx.x * (kD + 2) + kD + 1] = sl[threadIdx.x];
+        part[threadIdx.x * (kD + 2) + kD] = sM[0][threadIdx.x];
+        part[threadIdx.x * (kD + 2) + kD + 1] = sL[0][threadIdx.x];
     }
 }
 
@@ -340,11 +416,6 @@ __global__ __launch_bounds__(kD * kCombineGroups) void kv_attn_combine_kernel(co
 
 typedef void (*KvSplit)(const KvArgs, int);
 
-template <int RW>
-KvSplit pick_kv(bool kv8) {
-    return kv8 ? kv_attn_split_kernel<RW, true> : kv_attn_split_kernel<RW, false>;
-}
-
 int kv_max_splits(int T) {
     const int nchunks = (T + kC - 1) / kC;
     return nchunks < kKvMaxSplits ? nchunks : kKvMaxSplits;
@@ -357,18 +428,8 @@ size_t kv_attention_workspace_bytes(int M, int Hq, int T) {
 }
 
 hipError_t launch_kv_attention(const KvArgs &a, hipStream_t stream) {
-    const int G = a.Hq / a.Hkv;
-    const int R = a.M * G;
-    const int RW = (R + 3) / 4;
-    const bool kv8 = a.k_lo != nullptr;
-    KvSplit k;
-    switch (RW) {
-        case 1: k = pick_kv<1>(kv8); break;
-        case 2: k = pick_kv<2>(kv8); break;
-        case 3: k = pick_kv<3>(kv8); break;
-        case 4: k = pick_kv<4>(kv8); break;
-        default: return hipErrorInvalidValue;       // rejected by the ABI before this point
-    }
+    if (a.M * (a.Hq / a.Hkv) > kRows) return hipErrorInvalidValue;   // rejected by the ABI before this point
+    const KvSplit k = a.k_lo != nullptr ? kv_attn_split_kernel<true> : kv_attn_split_kernel<false>;
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
