@@ -274,7 +274,8 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  *            row, 128 output values, the maximum and the sum; 0 for
  *            M, Hq or T below 1)
  * Limits: M >= 1, Hq a multiple of Hkv, M Hq / Hkv <= BITNEST_KV_MAX_ROWS,
- * M <= T, T Hkv 64 < 2^31; otherwise BITNEST_EINVAL / BITNEST_EUNSUPPORTED.
+ * M <= T, Hkv <= 65535, T Hkv 64 < 2^31; otherwise BITNEST_EINVAL /
+ * BITNEST_EUNSUPPORTED. q and the scales are finite.
  */
 size_t bitnest_kv_attention_workspace_bytes(int M, int Hq, int T);
 

@@ -210,6 +210,7 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _kv(A, 4, 32, 8, 3, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 8, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EUNSUPPORTED),
     (lambda: _kv(A, 1, 32, 8, 1 << 23, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
+    (lambda: _kv(A, 1, 65536, 65536, 4, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
     (lambda: _kv(NUL, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, NUL, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 32, 8, 100, B, C, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),

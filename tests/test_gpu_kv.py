@@ -83,8 +83,9 @@ def test_kv_peaked_scores():
     assert np.abs(got - want).max() <= TOL * _vmax(vc, True)
 
 
-def test_kv8_with_lo_8_equals_kv4_on_gpu():
-    kc, vc = _cache(300, 8, seed=9)
+@pytest.mark.parametrize("T", [300, 20000])    # one chunk per split / runs of chunks
+def test_kv8_with_lo_8_equals_kv4_on_gpu(T):
+    kc, vc = _cache(T, 8, seed=9)
     q = np.random.default_rng(9).standard_normal((4, 32, 128)).astype(np.float32)
     k8 = (kc[0], np.full_like(kc[1], 0x88), kc[2])
     v8 = (vc[0], np.full_like(vc[1], 0x88), vc[2])
@@ -93,8 +94,9 @@ def test_kv8_with_lo_8_equals_kv4_on_gpu():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def test_kv_token_rows_equal_one_token_calls_on_the_cut_cache():
-    T, M = 200, 4
+@pytest.mark.parametrize("T", [200, 9000])
+def test_kv_token_rows_equal_one_token_calls_on_the_cut_cache(T):
+    M = 4
     kc, vc = _cache(T, 8, seed=10)
     q = np.random.default_rng(10).standard_normal((M, 32, 128)).astype(np.float32)
     full = _run(q, kc, vc, True)

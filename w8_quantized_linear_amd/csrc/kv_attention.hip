@@ -17,10 +17,11 @@
 //    is consumed): scores and P.V on the fp16 matrix cores, a running
 //    softmax per query row. The four waves then merge in LDS in a fixed
 //    order and the split's (output, maximum, sum) per row go to the caller's
-//    workspace.
+//    workspace. Scores are kept in base-2 units (log2(e) folded into the
+//    scale), so every exponential is one v_exp_f32.
 //  - kv_attn_combine_kernel: one workgroup per query row merges the splits:
-//    out = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m), the splits' weights
-//    staged in LDS and the partial loads spread over four thread groups.
+//    out = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m), as four thread
+//    groups with running maxima over interleaved splits, then merged.
 #include "bitnest_internal.h"
 #include "device_common.h"
 
@@ -40,6 +41,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr unsigned kF16Base = 0x64006400u;      // fp16 1024.0 in both halves
+constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), static_cast<int>(bytes),
@@ -85,32 +87,52 @@ __device__ __forceinline__ float quad_group_sum(float v) {
     return __builtin_bit_cast(float, static_cast<unsigned>(t[0])) + __builtin_bit_cast(float, static_cast<unsigned>(t[1]));
 }
 
-// Both products on the fp16 matrix cores, every code exact in fp16 and the
-// fp32 operands (q, p v_scale) split into three fp16 pieces after a power-of-
-// two scaling, so the products are those of fp32 values to about 2^-32.
+// (x0, x1) -> two fp16 pairs p1 + p2: 22 bits of each value (the second
+// piece floors at the fp16 subnormals, 2^-24).
+__device__ __forceinline__ void split2(float x0, float x1, unsigned &p1, unsigned &p2) {
+    const auto a = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    const float r0 = x0 - static_cast<float>(a[0]), r1 = x1 - static_cast<float>(a[1]);
+    const auto b = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+    p1 = __builtin_bit_cast(unsigned, a);
+    p2 = __builtin_bit_cast(unsigned, b);
+}
+
+// Both products on the fp16 matrix cores with every code exact in fp16; the
+// fp32 operands are scaled by a power of two and split into fp16 pieces:
+// q into three (33 bits, the scores to about 2^-32 of the row's largest
+// term), p v_scale into two (22 bits of each term).
 //
-// Lanes: c = lane % 16, g = lane / 16. Per 16-position tile of a wave:
-//  - scores S^T = K Q^T (v_mfma_f32_16x16x32_f16, 4 steps of 32 dimensions):
-//    A = K codes, lane = position c, dimensions 32 g + 8 s + {j, j + 4} in
-//    pair j of step s (one 16-byte load per plane); B = q pieces, lane =
-//    query row c, the same dimensions. The accumulator gives lane (c, g) the
-//    scores of query row c at positions 4 g + i.
-//  - softmax per query row over the tile (the four lanes of a row combine
+// Lanes: c = lane % 16, g = lane / 16. A wave step covers NT tiles of 16
+// positions (u = 0 .. NT - 1):
+//  - scores S^T = K Q^T per tile (v_mfma_f32_16x16x32_f16, 4 steps of 32
+//    dimensions): A = K codes, lane = position c, dimensions 32 g + 8 s +
+//    {j, j + 4} in pair j of step s (one 16-byte load per plane); B = q
+//    pieces, lane = query row c, the same dimensions. The accumulator gives
+//    lane (c, g) the scores of query row c at positions 16 u + 4 g + i.
+//  - softmax per query row over the step (the four lanes of a row combine
 //    with lane swaps), running maximum and sum per row.
-//  - P.V as O^T = V^T P^T (v_mfma_f32_16x16x16f16 per 16-dimension tile t):
-//    B = the score accumulator's own layout (lane = query row c, k =
-//    positions 4 g + i), A = V codes, lane = dimension 8 c + t at positions
-//    4 g + i (dword c of four position rows). The accumulator gives lane
-//    (c, g) the outputs of query row c at dimensions 32 g + 8 i + t.
+//  - P.V as O^T = V^T P^T per 16-dimension tile t (k = the step's 16 NT
+//    positions: v_mfma_f32_16x16x16f16 for NT = 1, 16x16x32 for NT = 2):
+//    B = the score accumulators' own layout (lane = query row c, k-slot
+//    4 u + i = position 16 u + 4 g + i), A = V codes, lane = dimension
+//    8 c + t at the same positions (dword c of 4 NT position rows). The
+//    accumulator gives lane (c, g) the outputs of query row c at dimensions
+//    32 g + 8 i + t.
 // Codes: KV4 u - 8, KV8 16 (u_hi - 8) + (u_lo - 8), both from fp16 1024 + code
 // bits and one packed subtraction. The KV8 codes with lo = 8 are 16 times the
 // KV4 codes and every scale factor differs by a power of two, so the two
 // paths then agree bit for bit.
-template <bool KV8>
-__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void kv_attn_split_kernel(const KvArgs a, int cps) {
+template <bool KV8, int NT>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void kv_attn_split_kernel(const KvArgs a, int cps) {
+    constexpr int STEP = kTile * NT;                 // positions per wave step
+    constexpr int WSTEP = 4 * STEP;                  // positions per workgroup step
+    constexpr int NP = 4 * NT;                       // positions per lane per step
+    typedef _Float16 f16xk __attribute__((ext_vector_type(NP)));
+    typedef unsigned u32xk __attribute__((ext_vector_type(NP / 2)));
     __shared__ float sO[4][kRows][kD];
     __shared__ float sM[4][kRows], sL[4][kRows], sW[4][kRows];
-    __shared__ float4 ssc[4][2][kTile / 4];          // per wave: K and V scales of its tile
+    __shared__ float4 ssc[4][2][STEP / 4];           // per wave: K and V scales of its step
 
     const int s = blockIdx.x, h = blockIdx.y;
     const int splits = gridDim.x;
@@ -127,39 +149,60 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const int tok = rv ? c / G : 0;
     const int limit = rv ? a.T - a.M + tok : -1;
 
-    // tile loads: this lane's K row (position c, bytes 16 g ..), its V dwords
-    // (dword c of positions 4 g + i) and the K / V scales of position c
-    const unsigned cache_bytes = static_cast<unsigned>(a.T) * a.Hkv * (kD / 2);
-    const unsigned scale_bytes = static_cast<unsigned>(a.T) * a.Hkv * 2;
+    // step loads: this lane's K rows (position 16 u + c, bytes 16 g ..), its
+    // V dwords (dword c of positions 16 u + 4 g + i) and the K / V scales of
+    // positions 16 u + c. The descriptors end at the split's last position:
+    // rows past it read zero and touch no memory (Hkv < 2^16 keeps every
+    // offset below 2^32).
+    const unsigned cache_bytes = static_cast<unsigned>(span1) * a.Hkv * (kD / 2);
+    const unsigned scale_bytes = static_cast<unsigned>(span1) * a.Hkv * 2;
     const __amdgpu_buffer_rsrc_t rkh = rsrc(a.k_hi, cache_bytes), rvh = rsrc(a.v_hi, cache_bytes);
     const __amdgpu_buffer_rsrc_t rkl = rsrc(KV8 ? a.k_lo : a.k_hi, cache_bytes);
     const __amdgpu_buffer_rsrc_t rvl = rsrc(KV8 ? a.v_lo : a.v_hi, cache_bytes);
     const __amdgpu_buffer_rsrc_t rks = rsrc(a.k_scale, scale_bytes), rvs = rsrc(a.v_scale, scale_bytes);
     struct Stage {
-        u32x4 kh, kl;
-        unsigned vh[4], vl[4];
-        unsigned short ks, vs;
+        u32x4 kh[NT], kl[NT];
+        unsigned vh[NP], vl[NP];
+        unsigned short ks[NT], vs[NT];
     };
-    // every load is issued (past the split: an offset past the end, which
-    // reads zero and touches no memory), so the waits count exactly
-    auto fetch = [&](Stage &st, int p0) {
-        const int tk = p0 + c;
-        const unsigned ok = tk < span1 ? (static_cast<unsigned>(tk) * a.Hkv + h) * (kD / 2) + 16 * g : cache_bytes;
-        st.kh = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkh, ok, 0, 0));
-        if (KV8) st.kl = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkl, ok, 0, 0));
+    // every load is issued (past the split they read zero), so the waits
+    // count exactly; the offsets advance by one workgroup step per fetch
+    const int pf = span0 + STEP * wave;              // the wave's first step
+    unsigned ok[NT], ov[NP], os[NT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tv = p0 + 4 * g + i;
-            const unsigned ov = tv < span1 ? (static_cast<unsigned>(tv) * a.Hkv + h) * (kD / 2) + 4 * c : cache_bytes;
-            st.vh[i] = __builtin_amdgcn_raw_buffer_load_b32(rvh, ov, 0, 0);
-            if (KV8) st.vl[i] = __builtin_amdgcn_raw_buffer_load_b32(rvl, ov, 0, 0);
+    for (int u = 0; u < NT; ++u) {
+        ok[u] = (static_cast<unsigned>(pf + 16 * u + c) * a.Hkv + h) * (kD / 2) + 16 * g;
+        os[u] = (static_cast<unsigned>(pf + 16 * u + c) * a.Hkv + h) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ov[4 * u + i] = (static_cast<unsigned>(pf + 16 * u + 4 * g + i) * a.Hkv + h) * (kD / 2) + 4 * c;
+    }
+    const unsigned step_planes = static_cast<unsigned>(WSTEP) * a.Hkv * (kD / 2);
+    const unsigned step_scales = static_cast<unsigned>(WSTEP) * a.Hkv * 2;
+    auto fetch = [&](Stage &st) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            st.kh[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkh, ok[u], 0, 0));
+            if (KV8) st.kl[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rkl, ok[u], 0, 0));
         }
-        const unsigned os = tk < span1 ? (static_cast<unsigned>(tk) * a.Hkv + h) * 2 : scale_bytes;
-        st.ks = __builtin_amdgcn_raw_buffer_load_b16(rks, os, 0, 0);
-        st.vs = __builtin_amdgcn_raw_buffer_load_b16(rvs, os, 0, 0);
+#pragma unroll
+        for (int e = 0; e < NP; ++e) {
+            st.vh[e] = __builtin_amdgcn_raw_buffer_load_b32(rvh, ov[e], 0, 0);
+            if (KV8) st.vl[e] = __builtin_amdgcn_raw_buffer_load_b32(rvl, ov[e], 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            st.ks[u] = __builtin_amdgcn_raw_buffer_load_b16(rks, os[u], 0, 0);
+            st.vs[u] = __builtin_amdgcn_raw_buffer_load_b16(rvs, os[u], 0, 0);
+            ok[u] += step_planes;
+            os[u] += step_scales;
+        }
+#pragma unroll
+        for (int e = 0; e < NP; ++e) ov[e] += step_planes;
     };
+
     // q row c (rows past R read row 0 and are zeroed), loaded before the
-    // tiles so that waiting for it leaves the tile loads in flight
+    // steps so that waiting for it leaves the step loads in flight
     float x[32];
     {
         const int qr = rv ? c : 0;
@@ -172,17 +215,22 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
             x[4 * k + 2] = rv ? v.z : 0.0f; x[4 * k + 3] = rv ? v.w : 0.0f;
         }
     }
-    // a ring of two tiles in flight while one is consumed
+    // a ring of RING steps in flight while one is consumed (one for the
+    // 32-position KV8 steps, which fill the registers with two)
+    constexpr int RING = (KV8 && NT == 2) ? 1 : 2;
     Stage s0, s1;
-    if (!KV8) s0.kl = s1.kl = u32x4{0, 0, 0, 0};
-    int p0 = span0 + kTile * wave;
-    fetch(s0, p0);
-    fetch(s1, p0 + kC);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) s0.kl[u] = s1.kl[u] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < NP; ++e) s0.vl[e] = s1.vl[e] = 0;
+    int p0 = pf;
+    fetch(s0);
+    if (RING == 2) fetch(s1);
 
     // q row c scaled by 2^kq (its largest |q| in [2^14, 2^15)), three fp16
     // pieces per step s and pair j (dimensions 32 g + 8 s + j, + j + 4)
     unsigned qb[3][4][4];
-    float gscale;                                    // 2^-kq / sqrt(128) (/ 16: KV8 codes)
+    float gscale;                                    // 2^-kq log2(e) / sqrt(128) (/ 16: KV8 codes)
     {
         float mx = 0.0f;
 #pragma unroll
@@ -195,7 +243,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
             for (int j = 0; j < 4; ++j)
                 split3(__builtin_amdgcn_ldexpf(x[8 * st + j], kq), __builtin_amdgcn_ldexpf(x[8 * st + j + 4], kq),
                        qb[0][st][j], qb[1][st][j], qb[2][st][j]);
-        gscale = __builtin_amdgcn_ldexpf(a.inv_sqrt_d, -kq) * (KV8 ? 0.0625f : 1.0f);
+        gscale = __builtin_amdgcn_ldexpf(a.inv_sqrt_d * kLog2e, -kq) * (KV8 ? 0.0625f : 1.0f);
     }
 
     float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -204,125 +252,158 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto consume = [&](const Stage &cur, int p0) {
-        const u32x4 ckh = cur.kh, ckl = cur.kl;
-        const unsigned *cvh = cur.vh, *cvl = cur.vl;
-        const unsigned short cks = cur.ks, cvs = cur.vs;
-
-        // scales of positions 4 g + i through the wave's LDS slot
-        reinterpret_cast<float *>(ssc[wave][0])[c] = half_bits_to_float(cks);
-        reinterpret_cast<float *>(ssc[wave][1])[c] = half_bits_to_float(cvs);
-        const float4 ksv = ssc[wave][0][g];
-        const float4 vsv = ssc[wave][1][g];
-
-        // ---- scores
-        f16x8 ka[4];
+    // consume one step from its stage: the codes and scales are converted
+    // first, so the stage can take the loads of the step RING ahead
+    auto consume = [&](Stage &cur, int p0) {
+        // scales of positions 16 u + 4 g + i through the wave's LDS slot
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            unsigned pr[4];
+        for (int u = 0; u < NT; ++u) {
+            reinterpret_cast<float *>(ssc[wave][0])[16 * u + c] = half_bits_to_float(cur.ks[u]);
+            reinterpret_cast<float *>(ssc[wave][1])[16 * u + c] = half_bits_to_float(cur.vs[u]);
+        }
+        float ks[NP], vs[NP];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (KV8) {
-                    // byte of each half: 16 u_hi + u_lo of dimensions j, j + 4
-                    const unsigned lo = ((ckl[st] >> (4 * j)) & 0x000F000Fu) | kF16Base;
-                    const unsigned hi = j == 0 ? (ckh[st] << 4) : (ckh[st] >> (4 * j - 4));
-                    pr[j] = f16_unbias((hi & 0x00F000F0u) | lo, 1024.0f + 136.0f);
-                } else {
-                    pr[j] = f16_unbias(((ckh[st] >> (4 * j)) & 0x000F000Fu) | kF16Base, 1024.0f + 8.0f);
+        for (int u = 0; u < NT; ++u) {
+            const float4 kv = ssc[wave][0][4 * u + g], vv = ssc[wave][1][4 * u + g];
+            ks[4 * u] = kv.x; ks[4 * u + 1] = kv.y; ks[4 * u + 2] = kv.z; ks[4 * u + 3] = kv.w;
+            vs[4 * u] = vv.x; vs[4 * u + 1] = vv.y; vs[4 * u + 2] = vv.z; vs[4 * u + 3] = vv.w;
+        }
+
+        // K codes (the A operands of the scores)
+        f16x8 ka[NT][4];
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const unsigned wh = cur.kh[u][st], wl = cur.kl[u][st];
+                unsigned pr[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (KV8) {
+                        // byte of each half: 16 u_hi + u_lo of dimensions j, j + 4
+                        const unsigned lo = ((wl >> (4 * j)) & 0x000F000Fu) | kF16Base;
+                        const unsigned hi = j == 0 ? (wh << 4) : (wh >> (4 * j - 4));
+                        pr[j] = f16_unbias((hi & 0x00F000F0u) | lo, 1024.0f + 136.0f);
+                    } else {
+                        pr[j] = f16_unbias(((wh >> (4 * j)) & 0x000F000Fu) | kF16Base, 1024.0f + 8.0f);
+                    }
                 }
+                ka[u][st] = __builtin_bit_cast(f16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
             }
-            ka[st] = __builtin_bit_cast(f16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
-        }
-        f32x4 d[3];
+        // V codes of dimension 8 c + t at positions 16 u + 4 g + i (the A
+        // operands of P.V, k-slot 4 u + i)
+        unsigned ve[NP], vo[NP];                     // codes of even / odd nibbles as bytes (KV8: full codes)
 #pragma unroll
-        for (int pc = 0; pc < 3; ++pc) {
-            d[pc] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                d[pc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    ka[st], __builtin_bit_cast(f16x8, u32x4{qb[pc][st][0], qb[pc][st][1], qb[pc][st][2], qb[pc][st][3]}),
-                    d[pc], 0, 0, 0);
+        for (int e = 0; e < NP; ++e) {
+            if (KV8) {
+                ve[e] = ((cur.vh[e] & 0x0F0F0F0Fu) << 4) | (cur.vl[e] & 0x0F0F0F0Fu);
+                vo[e] = (cur.vh[e] & 0xF0F0F0F0u) | ((cur.vl[e] >> 4) & 0x0F0F0F0Fu);
+            } else {
+                ve[e] = cur.vh[e] & 0x0F0F0F0Fu;
+                vo[e] = (cur.vh[e] >> 4) & 0x0F0F0F0Fu;
+            }
         }
+        f16xk va[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            // byte t / 2 of two positions into the low bytes of the halves
+            const unsigned sel = 0x0C000C00u | ((4u + t / 2) << 16) | static_cast<unsigned>(t / 2);
+            const unsigned *src = (t & 1) ? vo : ve;
+            const float off = 1024.0f + (KV8 ? 136.0f : 8.0f);
+            u32xk pk;
+#pragma unroll
+            for (int e = 0; e < NP; e += 2)
+                pk[e / 2] = f16_unbias(__builtin_amdgcn_perm(src[e + 1], src[e], sel) | kF16Base, off);
+            va[t] = __builtin_bit_cast(f16xk, pk);
+        }
+        fetch(cur);                                  // the step RING ahead
 
-        // ---- running softmax of query row c over the tile
-        const float ks4[4] = {ksv.x, ksv.y, ksv.z, ksv.w};
-        const float vs4[4] = {vsv.x, vsv.y, vsv.z, vsv.w};
-        float sc[4];
+        // ---- scores, the small pieces first
+        float sc[NP];
         float tmax = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool vis = p0 + 4 * g + i <= limit;
-            const float dot = (d[2][i] + d[1][i]) + d[0][i];
-            sc[i] = vis ? dot * (ks4[i] * gscale) : -__builtin_inff();
-            tmax = fmaxf(tmax, sc[i]);
-        }
-        const float m_new = fmaxf(m_run, quad_group_max(tmax));
-        const float alpha = m_run == -__builtin_inff() ? 0.0f : expf(m_run - m_new);
-        float pv[4], psum = 0.0f, pmax = 0.0f;
+        for (int u = 0; u < NT; ++u) {
+            f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = sc[i] == -__builtin_inff() ? 0.0f : expf(sc[i] - m_new);
+            for (int pc = 2; pc >= 0; --pc)
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        ka[u][st],
+                        __builtin_bit_cast(f16x8, u32x4{qb[pc][st][0], qb[pc][st][1], qb[pc][st][2], qb[pc][st][3]}),
+                        d, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool vis = p0 + 16 * u + 4 * g + i <= limit;
+                sc[4 * u + i] = vis ? d[i] * (ks[4 * u + i] * gscale) : -__builtin_inff();
+                tmax = fmaxf(tmax, sc[4 * u + i]);
+            }
+        }
+
+        // ---- running softmax of query row c over the step (base 2)
+        const float m_new = fmaxf(m_run, quad_group_max(tmax));
+        const bool fresh = m_run == -__builtin_inff();   // nothing accumulated yet
+        const float alpha = fresh ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        float pv[NP], psum = 0.0f, pmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NP; ++e) {
+            const float p = sc[e] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(sc[e] - m_new);
             psum += p;
-            pv[i] = p * vs4[i];
-            pmax = fmaxf(pmax, fabsf(pv[i]));
+            pv[e] = p * vs[e];
+            pmax = fmaxf(pmax, fabsf(pv[e]));
         }
         l_run = fmaf(l_run, alpha, quad_group_sum(psum));
         m_run = m_new;
-        // p v_scale of the row scaled into [2^14, 2^15) and split into pieces;
-        // the accumulators follow the row's scale
+        // p v_scale of the row times 2^kt, split into pieces: kt is kept while
+        // the step's largest value stays in [2^7, 2^15), else reset to put it
+        // in [2^14, 2^15); the accumulators hold O 2^kt and follow the row's
+        // scale and maximum
         pmax = quad_group_max(pmax);
-        const int kt = pmax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(pmax) : kt_run;
+        int kt = kt_run;
+        if (pmax > 0.0f) {
+            const int ex = __builtin_amdgcn_frexp_expf(pmax);      // pmax < 2^ex
+            if (fresh || ex + kt_run > 15 || ex + kt_run < 8) kt = 15 - ex;
+        }
         const float f = __builtin_amdgcn_ldexpf(alpha, kt - kt_run);
         kt_run = kt;
+        // (f = 1 leaves the accumulators as they are, and so does any f while
+        // nothing is accumulated)
+        if (__builtin_amdgcn_ballot_w64(!fresh && f != 1.0f) != 0) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[t] *= f;
-        unsigned pb[3][2];
-        split3(__builtin_amdgcn_ldexpf(pv[0], kt), __builtin_amdgcn_ldexpf(pv[1], kt), pb[0][0], pb[1][0], pb[2][0]);
-        split3(__builtin_amdgcn_ldexpf(pv[2], kt), __builtin_amdgcn_ldexpf(pv[3], kt), pb[0][1], pb[1][1], pb[2][1]);
+            for (int t = 0; t < 8; ++t) o[t] *= f;
+        }
+        u32xk pb[2];
+#pragma unroll
+        for (int e = 0; e < NP; e += 2) {
+            unsigned p1, p2;
+            split2(__builtin_amdgcn_ldexpf(pv[e], kt), __builtin_amdgcn_ldexpf(pv[e + 1], kt), p1, p2);
+            pb[0][e / 2] = p1;
+            pb[1][e / 2] = p2;
+        }
 
-        // ---- P.V: V codes of dimension 8 c + t at positions 4 g + i
-        unsigned ve[4], vo[4];                          // codes of even / odd nibbles as bytes (KV8: full codes)
+        // ---- P.V, the small piece first
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (KV8) {
-                ve[i] = ((cvh[i] & 0x0F0F0F0Fu) << 4) | (cvl[i] & 0x0F0F0F0Fu);
-                vo[i] = (cvh[i] & 0xF0F0F0F0u) | ((cvl[i] >> 4) & 0x0F0F0F0Fu);
-            } else {
-                ve[i] = cvh[i] & 0x0F0F0F0Fu;
-                vo[i] = (cvh[i] >> 4) & 0x0F0F0F0Fu;
+        for (int pc = 1; pc >= 0; --pc) {
+            const f16xk bp = __builtin_bit_cast(f16xk, pb[pc]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if constexpr (NT == 1)
+                    o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[t], bp, o[t], 0, 0, 0);
+                else
+                    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], bp, o[t], 0, 0, 0);
             }
         }
-        f16x4 va[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            // byte t / 2 of positions (0, 1) and (2, 3) into the low bytes of the halves
-            const unsigned sel = 0x0C000C00u | ((4u + t / 2) << 16) | static_cast<unsigned>(t / 2);
-            const unsigned *src = (t & 1) ? vo : ve;
-            const unsigned b01 = __builtin_amdgcn_perm(src[1], src[0], sel) | kF16Base;
-            const unsigned b23 = __builtin_amdgcn_perm(src[3], src[2], sel) | kF16Base;
-            const float off = 1024.0f + (KV8 ? 136.0f : 8.0f);
-            va[t] = __builtin_bit_cast(f16x4, u32x2{f16_unbias(b01, off), f16_unbias(b23, off)});
-        }
-#pragma unroll
-        for (int pc = 2; pc >= 0; --pc) {
-            const f16x4 bp = __builtin_bit_cast(f16x4, u32x2{pb[pc][0], pb[pc][1]});
-#pragma unroll
-            for (int t = 0; t < 8; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[t], bp, o[t], 0, 0, 0);
-        }
     };
+    if constexpr (RING == 2) {
 #pragma unroll 1
-    for (; p0 < span1; p0 += 2 * kC) {
-        {
-            const Stage cur = s0;
-            fetch(s0, p0 + 2 * kC);
-            consume(cur, p0);
+        for (; p0 < span1; p0 += 2 * WSTEP) {
+            consume(s0, p0);
+            if (p0 + WSTEP >= span1) break;          // uniform
+            consume(s1, p0 + WSTEP);
         }
-        if (p0 + kC >= span1) break;                 // uniform
-        {
-            const Stage cur = s1;
-            fetch(s1, p0 + 3 * kC);
-            consume(cur, p0 + kC);
-        }
+    } else {
+#pragma unroll 1
+        for (; p0 < span1; p0 += WSTEP) consume(s0, p0);
     }
 
     // ---- the four waves' (maximum, sum, output) merged in a fixed order
@@ -344,7 +425,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int w = 1; w < 4; ++w) mx = fmaxf(mx, sM[w][r]);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) sW[w][r] = sM[w][r] == -__builtin_inff() ? 0.0f : expf(sM[w][r] - mx);
+        for (int w = 0; w < 4; ++w)
+            sW[w][r] = sM[w][r] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(sM[w][r] - mx);
         sM[0][r] = mx;
         sL[0][r] = ((sL[0][r] * sW[0][r] + sL[1][r] * sW[1][r]) + sL[2][r] * sW[2][r]) + sL[3][r] * sW[3][r];
     }
@@ -365,11 +447,12 @@ constexpr int kCombineGroups = 4;
 constexpr int kKvMaxSplits = 512;
 
 // One workgroup (4 groups of 128 threads, one thread per dimension) per
-// output row (token i, query head hq), merging the splits of its KV head.
+// output row (token i, query head hq), merging the splits of its KV head:
+// group q takes the splits s = q, q + 4, .. in ascending order with a
+// running maximum (the loads of a split do not wait on the previous one),
+// then the four groups merge in LDS in a fixed order.
 __global__ __launch_bounds__(kD * kCombineGroups) void kv_attn_combine_kernel(const KvArgs a, int splits) {
-    __shared__ float cm[kKvMaxSplits], cl[kKvMaxSplits], cw[kKvMaxSplits];
-    __shared__ float cmax[kCombineGroups * kD / 64];
-    __shared__ float cnum[kCombineGroups][kD], cden[kCombineGroups];
+    __shared__ float cnum[kCombineGroups][kD], cden[kCombineGroups], cmx[kCombineGroups];
     const int row = blockIdx.x;                       // i Hq + hq
     const int i = row / a.Hq, hq = row - (row / a.Hq) * a.Hq;
     const int G = a.Hq / a.Hkv;
@@ -378,38 +461,38 @@ __global__ __launch_bounds__(kD * kCombineGroups) void kv_attn_combine_kernel(co
     const int r = i * G + g;
     const float *base = a.work + static_cast<size_t>(h) * splits * R * (kD + 2) + static_cast<size_t>(r) * (kD + 2);
     const size_t stride = static_cast<size_t>(R) * (kD + 2);
-    constexpr int nthreads = kD * kCombineGroups;
-
-    float mx = -__builtin_inff();
-    for (int s = threadIdx.x; s < splits; s += nthreads) {
-        const float m = base[s * stride + kD];
-        cm[s] = m;
-        cl[s] = base[s * stride + kD + 1];
-        mx = fmaxf(mx, m);
-    }
-    mx = wave_max_dpp_f32(mx);
-    if ((threadIdx.x & 63) == 0) cmax[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = cmax[0];
-#pragma unroll
-    for (int w = 1; w < nthreads / 64; ++w) mx = fmaxf(mx, cmax[w]);
-    for (int s = threadIdx.x; s < splits; s += nthreads) cw[s] = cl[s] > 0.0f ? expf(cm[s] - mx) : 0.0f;
-    __syncthreads();
-
     const int grp = threadIdx.x / kD, j = threadIdx.x - grp * kD;
-    float num = 0.0f, den = 0.0f;
-#pragma unroll 8
+
+    float mx = -__builtin_inff(), num = 0.0f, den = 0.0f;
+#pragma unroll 4
     for (int s = grp; s < splits; s += kCombineGroups) {
-        const float w = cw[s];
-        num = fmaf(base[s * stride + j], w, num);
-        den = fmaf(cl[s], w, den);
+        const float *p = base + s * stride;
+        const float m = p[kD], l = p[kD + 1], o = p[j];
+        const bool seen = l > 0.0f;                   // a split that saw a visible position
+        const float mn = seen ? fmaxf(mx, m) : mx;
+        const float wa = seen ? __builtin_amdgcn_exp2f(mx - mn) : 1.0f;
+        const float wb = seen ? __builtin_amdgcn_exp2f(m - mn) : 0.0f;
+        num = fmaf(num, wa, o * wb);
+        den = fmaf(den, wa, l * wb);
+        mx = mn;
     }
     cnum[grp][j] = num;
-    if (j == 0) cden[grp] = den;
+    if (j == 0) {
+        cden[grp] = den;
+        cmx[grp] = mx;
+    }
     __syncthreads();
     if (grp == 0) {
-        const float n = ((cnum[0][j] + cnum[1][j]) + cnum[2][j]) + cnum[3][j];
-        const float d = ((cden[0] + cden[1]) + cden[2]) + cden[3];
+        float m = cmx[0];
+#pragma unroll
+        for (int q = 1; q < kCombineGroups; ++q) m = fmaxf(m, cmx[q]);
+        float n = 0.0f, d = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kCombineGroups; ++q) {
+            const float w = cden[q] > 0.0f ? __builtin_amdgcn_exp2f(cmx[q] - m) : 0.0f;
+            n = fmaf(cnum[q][j], w, n);
+            d = fmaf(cden[q], w, d);
+        }
         a.out[static_cast<size_t>(row) * kD + j] = n / d;
     }
 }
@@ -429,18 +512,22 @@ size_t kv_attention_workspace_bytes(int M, int Hq, int T) {
 
 hipError_t launch_kv_attention(const KvArgs &a, hipStream_t stream) {
     if (a.M * (a.Hq / a.Hkv) > kRows) return hipErrorInvalidValue;   // rejected by the ABI before this point
-    const KvSplit k = a.k_lo != nullptr ? kv_attn_split_kernel<true> : kv_attn_split_kernel<false>;
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
     // about two workgroups per compute unit over the KV heads, each split a
-    // run of cps chunks (no split empty)
+    // run of cps chunks (no split empty); runs of several chunks take
+    // 32-position wave steps (cps made even: whole workgroup steps)
     const int nchunks = (a.T + kC - 1) / kC;
     int want = (2 * dev.cus + a.Hkv - 1) / a.Hkv;
     if (want > kv_max_splits(a.T)) want = kv_max_splits(a.T);
     if (want < 1) want = 1;
-    const int cps = (nchunks + want - 1) / want;
+    int cps = (nchunks + want - 1) / want;
+    if (cps > 1) cps += cps & 1;
     const int splits = (nchunks + cps - 1) / cps;
+    const bool kv8 = a.k_lo != nullptr;
+    const KvSplit k = cps > 1 ? (kv8 ? kv_attn_split_kernel<true, 2> : kv_attn_split_kernel<false, 2>)
+                              : (kv8 ? kv_attn_split_kernel<true, 1> : kv_attn_split_kernel<false, 1>);
     hipLaunchKernelGGL(k, dim3(splits, a.Hkv), dim3(kKvThreads), 0, stream, a, cps);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
