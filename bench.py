@@ -435,7 +435,8 @@ def accept_timing(bn, V=128256, calls=32, reps=5):
     draft = torch.zeros((R - 1,), dtype=torch.int32, device="cuda")
     targ = torch.empty((R,), dtype=torch.int32, device="cuda")
     res = torch.empty((2,), dtype=torch.int32, device="cuda")
-    graph = capture(lambda: [bn.bitnest_greedy_accept(lg, draft, targ, res) for lg in logits])
+    work = torch.empty((bn.bitnest_greedy_accept_workspace_bytes(R, V),), dtype=torch.uint8, device="cuda")
+    graph = capture(lambda: [bn.bitnest_greedy_accept(lg, draft, targ, res, work) for lg in logits])
     graph.replay()
     torch.cuda.synchronize()
     ts = []

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 2
+#define BITNEST_ABI_VERSION 3
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
@@ -237,9 +237,16 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K,
  *   logits  fp32 [R, V], R = gamma + 1 (1 <= R <= BITNEST_MAX_M), V >= 1, finite
  *   draft   int32 [R - 1] (may be NULL when R == 1)
  *   targ    int32 [R], written;  result int32 [2], written
+ *   work    caller-owned scratch of at least
+ *           bitnest_greedy_accept_workspace_bytes(R, V) bytes (per-slice partials:
+ *           8 bytes per row and slice of about 4096 logits, at most 64 slices),
+ *           overwritten; 16-byte aligned
  */
+size_t bitnest_greedy_accept_workspace_bytes(int R, int V);
+
 bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft,
-                                     int32_t *targ, int32_t *result, void *stream);
+                                     int32_t *targ, int32_t *result, void *work, size_t work_bytes,
+                                     void *stream);
 
 /*
  * Decode attention over the nested KV cache (model card, recipe table row

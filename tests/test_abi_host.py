@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
               "bitnest_quant_linear_draft", "bitnest_quant_linear_target", "bitnest_hadamard_quant_act",
               "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
               "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_kv_attention",
-              "bitnest_kv_attention_workspace_bytes"):
+              "bitnest_kv_attention_workspace_bytes", "bitnest_greedy_accept_workspace_bytes"):
         assert n in names
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bn.bitnest_abi_version() == 2
+    assert bn.bitnest_abi_version() == 3
     seen = set()
     for s in range(5):
         txt = bn.bitnest_status_string(s)
@@ -86,8 +86,11 @@ def _kv(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb):
     return bn.lib().bitnest_kv_attention(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb, None)
 
 
-def _ga(lg, R, V, dr, tg, res):
-    return bn.lib().bitnest_greedy_accept(lg, R, V, dr, tg, res, None)
+_DEFAULT = object()
+
+
+def _ga(lg, R, V, dr, tg, res, w=_DEFAULT, wb=1 << 20):
+    return bn.lib().bitnest_greedy_accept(lg, R, V, dr, tg, res, A if w is _DEFAULT else w, wb, None)
 
 
 def _pk(W, N, K, hi, lo, sc):
@@ -204,6 +207,9 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _ga(A, 4, 100, B, C, NUL), bn.EINVAL),
     (lambda: _ga(MIS, 4, 100, B, C, D), bn.EALIGN),
     (lambda: _ga(A, 4, 100, B, C, MIS), bn.EALIGN),
+    (lambda: _ga(A, 4, 100, B, C, D, NUL), bn.EINVAL),
+    (lambda: _ga(A, 4, 100, B, C, D, A, 31), bn.EINVAL),
+    (lambda: _ga(A, 4, 100, B, C, D, MIS), bn.EALIGN),
     # nested KV attention: every case fails validation (none may launch)
     (lambda: _kv(A, 0, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 30, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
@@ -228,6 +234,16 @@ def test_kv_workspace_size():
     assert bn.bitnest_kv_attention_workspace_bytes(1, 32, 64 * 512) == 512 * 32 * 130 * 4
     assert bn.bitnest_kv_attention_workspace_bytes(4, 32, 131072) == 512 * 4 * 32 * 130 * 4
     assert bn.bitnest_kv_attention_workspace_bytes(0, 32, 10) == 0
+
+
+def test_accept_workspace_size():
+    # one (value, index) pair of 8 bytes per row and slice of about 4096
+    # logits, from 1 to 64 slices
+    assert bn.bitnest_greedy_accept_workspace_bytes(4, 128256) == 4 * 32 * 8
+    assert bn.bitnest_greedy_accept_workspace_bytes(1, 1) == 8
+    assert bn.bitnest_greedy_accept_workspace_bytes(32, 4097) == 32 * 2 * 8
+    assert bn.bitnest_greedy_accept_workspace_bytes(2, 10 ** 6) == 2 * 64 * 8
+    assert bn.bitnest_greedy_accept_workspace_bytes(0, 100) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -39,7 +39,7 @@ def _case(R, V, seed, ties):
 
 
 @pytest.mark.parametrize("R", [1, 2, 4, 8, 32])
-@pytest.mark.parametrize("V", [1, 3, 1000, 4096, 128256, 32001])
+@pytest.mark.parametrize("V", [1, 3, 1000, 4096, 4097, 128256, 32001, 262147, 300000])
 @pytest.mark.parametrize("ties", ["none", "top", "flat", "negative"])
 def test_greedy_accept_exact(R, V, ties):
     logits, draft = _case(R, V, seed=R * 131 + V, ties=ties)

@@ -21,7 +21,7 @@ __all__ = [
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
     "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
     "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
-    "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_kv_attention",
+    "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_greedy_accept_workspace_bytes", "bitnest_kv_attention",
     "bitnest_kv_attention_workspace_bytes", "kv_pack",
 ]
 
@@ -68,7 +68,9 @@ def lib() -> ctypes.CDLL:
         L.bitnest_hadamard_quant_linear_draft.argtypes = [P, I, P, P, P, P, P, I, I, I, P]
         L.bitnest_hadamard_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
         L.bitnest_pack_nested.argtypes = [P, I, I, P, P, P, P]
-        L.bitnest_greedy_accept.argtypes = [P, I, I, P, P, P, P]
+        L.bitnest_greedy_accept.argtypes = [P, I, I, P, P, P, P, ctypes.c_size_t, P]
+        L.bitnest_greedy_accept_workspace_bytes.argtypes = [I, I]
+        L.bitnest_greedy_accept_workspace_bytes.restype = ctypes.c_size_t
         L.bitnest_kv_attention_workspace_bytes.argtypes = [I, I, I]
         L.bitnest_kv_attention_workspace_bytes.restype = ctypes.c_size_t
         L.bitnest_kv_attention.argtypes = [P, I, I, I, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -326,10 +328,16 @@ def bitnest_pack_nested(W: torch.Tensor, hi: torch.Tensor | None = None, lo: tor
     return hi, lo, scale
 
 
+def bitnest_greedy_accept_workspace_bytes(R: int, V: int) -> int:
+    return int(lib().bitnest_greedy_accept_workspace_bytes(R, V))
+
+
 def bitnest_greedy_accept(logits: torch.Tensor, draft: torch.Tensor, targ: torch.Tensor | None = None,
-                          result: torch.Tensor | None = None):
+                          result: torch.Tensor | None = None, work: torch.Tensor | None = None):
     """Greedy verification: logits fp32 [gamma + 1, V], draft int32 [gamma] ->
-    (targ int32 [gamma + 1], result int32 [2] = {accepted count, next token})."""
+    (targ int32 [gamma + 1], result int32 [2] = {accepted count, next token}).
+    work: device scratch of bitnest_greedy_accept_workspace_bytes(R, V) bytes
+    (allocated here when not given)."""
     _need(logits, "logits", torch.float32)
     if logits.dim() != 2:
         raise ValueError("logits must be [R, V]")
@@ -341,8 +349,13 @@ def bitnest_greedy_accept(logits: torch.Tensor, draft: torch.Tensor, targ: torch
         result = torch.empty((2,), dtype=torch.int32, device=logits.device)
     _need(targ, "targ", torch.int32, (R,))
     _need(result, "result", torch.int32, (2,))
+    need = bitnest_greedy_accept_workspace_bytes(R, V)
+    if work is None:
+        work = torch.empty((max(need, 16),), dtype=torch.uint8, device=logits.device)
+    _need(work, "work", work.dtype)
     _call(lib().bitnest_greedy_accept(_p(logits), R, V, _p(draft) if R > 1 else None, _p(targ), _p(result),
-                                      _stream(logits)), "bitnest_greedy_accept")
+                                      _p(work), work.numel() * work.element_size(), _stream(logits)),
+          "bitnest_greedy_accept")
     return targ, result
 
 

@@ -216,14 +216,21 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K, uint8_t *hi, ui
     return to_status(bitnest::launch_pack_nested(W, N, K, hi, lo, scale, static_cast<hipStream_t>(stream)));
 }
 
+size_t bitnest_greedy_accept_workspace_bytes(int R, int V) {
+    if (R < 1 || V < 1) return 0;
+    return bitnest::accept_workspace_bytes(R, V);
+}
+
 bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
-                                     int32_t *result, void *stream) {
+                                     int32_t *result, void *work, size_t work_bytes, void *stream) {
     if (R < 1 || V < 1) return BITNEST_EINVAL;
     if (R > BITNEST_MAX_M) return BITNEST_EUNSUPPORTED;
-    if (!logits || !targ || !result || (R > 1 && !draft)) return BITNEST_EINVAL;
-    if (!aligned16(logits) || !aligned16(targ) || !aligned16(result) || (draft && !aligned16(draft)))
+    if (!logits || !targ || !result || !work || (R > 1 && !draft)) return BITNEST_EINVAL;
+    if (work_bytes < bitnest::accept_workspace_bytes(R, V)) return BITNEST_EINVAL;
+    if (!aligned16(logits) || !aligned16(targ) || !aligned16(result) || !aligned16(work) ||
+        (draft && !aligned16(draft)))
         return BITNEST_EALIGN;
-    return to_status(bitnest::launch_greedy_accept(logits, R, V, draft, targ, result,
+    return to_status(bitnest::launch_greedy_accept(logits, R, V, draft, targ, result, work,
                                                    static_cast<hipStream_t>(stream)));
 }
 

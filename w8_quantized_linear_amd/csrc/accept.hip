@@ -5,17 +5,23 @@
 // index), the longest prefix of draft tokens equal to it, and the target's
 // token after that prefix.
 //
-// Two launches: one workgroup per row scans the row (16-byte loads when the
-// rows are 16-byte aligned) and reduces (value, index) pairs, whose order
-// (larger value, then smaller index) makes the result independent of the
-// reduction order; then one thread walks the at most 31 draft tokens.
+// Two launches: every row is cut into S slices of about 4K logits, one
+// 256-thread workgroup per (slice, row) scans its slice (16-byte loads when
+// the rows are 16-byte aligned, all in flight together) and writes its
+// (value, index) pair to the caller's workspace; then one wave per row
+// reduces the row's S pairs, and one thread walks the at most 31 draft
+// tokens. The pair order
+// (larger value, then smaller index) makes every result independent of the
+// order of the reductions.
 #include "bitnest_internal.h"
 #include "device_common.h"
 
 namespace bitnest {
 namespace {
 
-constexpr int kArgThreads = 1024;
+constexpr int kSliceThreads = 256;
+constexpr int kSliceLogits = 4096;     // about this many logits per slice
+constexpr int kMaxSlices = 64;         // one per lane of the final wave
 
 // (v, i) replaces (bv, bi) when larger, or equal with a smaller index
 __device__ __forceinline__ void take(float &bv, int &bi, float v, int i) {
@@ -25,37 +31,55 @@ __device__ __forceinline__ void take(float &bv, int &bi, float v, int i) {
     }
 }
 
+// wave-wide (value, index) reduction; every lane ends with the result
+__device__ __forceinline__ void wave_take(float &bv, int &bi) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        take(bv, bi, ov, oi);
+    }
+}
+
+int accept_slices(int V) {
+    const int s = (V + kSliceLogits - 1) / kSliceLogits;
+    return s < 1 ? 1 : (s > kMaxSlices ? kMaxSlices : s);
+}
+
+// slice length: ceil(V / S) rounded up to a multiple of 4 (whole float4s)
+int accept_slice_len(int V, int S) { return (((V + S - 1) / S) + 3) & ~3; }
+
+// part[r S + s] = {bits of the slice's largest logit, its smallest column}
 template <bool VEC>
-__global__ __launch_bounds__(kArgThreads) void row_argmax_kernel(const float *__restrict__ logits, int V,
-                                                                  int32_t *__restrict__ targ) {
-    __shared__ float sv[kArgThreads / 64];
-    __shared__ int si[kArgThreads / 64];
-    const float *row = logits + static_cast<size_t>(blockIdx.x) * V;
+__global__ __launch_bounds__(kSliceThreads) void slice_argmax_kernel(const float *__restrict__ logits, int V, int L,
+                                                                     uint2 *__restrict__ part) {
+    __shared__ float sv[kSliceThreads / 64];
+    __shared__ int si[kSliceThreads / 64];
+    const int s = blockIdx.x, r = blockIdx.y;
+    const float *row = logits + static_cast<size_t>(r) * V;
+    const int c0 = s * L;
+    const int c1 = c0 + L < V ? c0 + L : V;
     float bv = -__builtin_inff();
     int bi = 0x7FFFFFFF;
     if (VEC) {
-        // columns 4 j .. 4 j + 3 per float4 j; a thread visits j = tid, tid + T, ...
-        // in increasing order and its four columns in order, so the first
-        // maximum it sees is its smallest index. A chunk of U float4 per
-        // thread (half the row of a 128K vocabulary; as many as the register
-        // budget of 1024 threads holds) is requested at once; a float4 whose
-        // maximum is below the running best cannot change it, so the exact
-        // pairwise update runs only when it can.
+        // float4 j holds columns 4 j .. 4 j + 3; U float4 per thread are
+        // requested together (a 4096-logit slice is one round); a float4 whose
+        // maximum is below the running best cannot change it
         const float4 *r4 = reinterpret_cast<const float4 *>(row);
-        const int n4 = V >> 2;
-        constexpr int U = 16;
-        for (int base = 0; base < n4; base += U * kArgThreads) {
+        const int j1 = c1 >> 2;
+        constexpr int U = 4;
+        for (int base = c0 >> 2; base < j1; base += U * kSliceThreads) {
             float4 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = base + u * kArgThreads + threadIdx.x;
-                v[u] = r4[j < n4 ? j : 0];
+                const int j = base + u * kSliceThreads + threadIdx.x;
+                v[u] = r4[j < j1 ? j : 0];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = base + u * kArgThreads + threadIdx.x;
+                const int j = base + u * kSliceThreads + threadIdx.x;
                 const float m4 = fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w));
-                if (j < n4 && m4 >= bv) {
+                if (j < j1 && m4 >= bv) {
                     take(bv, bi, v[u].x, 4 * j);
                     take(bv, bi, v[u].y, 4 * j + 1);
                     take(bv, bi, v[u].z, 4 * j + 2);
@@ -64,16 +88,9 @@ __global__ __launch_bounds__(kArgThreads) void row_argmax_kernel(const float *__
             }
         }
     } else {
-        for (int j = threadIdx.x; j < V; j += kArgThreads) take(bv, bi, row[j], j);
+        for (int j = c0 + threadIdx.x; j < c1; j += kSliceThreads) take(bv, bi, row[j], j);
     }
-    // wave, then workgroup: the pair order makes the result independent of
-    // the reduction order
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        take(bv, bi, ov, oi);
-    }
+    wave_take(bv, bi);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         sv[wave] = bv;
@@ -81,32 +98,62 @@ __global__ __launch_bounds__(kArgThreads) void row_argmax_kernel(const float *__
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kArgThreads / 64; ++w) take(bv, bi, sv[w], si[w]);
-        targ[blockIdx.x] = bi;
+        for (int w = 1; w < kSliceThreads / 64; ++w) take(bv, bi, sv[w], si[w]);
+        part[static_cast<size_t>(r) * gridDim.x + s] = make_uint2(__builtin_bit_cast(unsigned, bv), static_cast<unsigned>(bi));
     }
 }
 
-__global__ void accept_kernel(int R, const int32_t *__restrict__ draft, const int32_t *__restrict__ targ,
-                              int32_t *__restrict__ result) {
-    if (threadIdx.x != 0) return;
-    int n = 0;
-    while (n < R - 1 && draft[n] == targ[n]) ++n;
-    result[0] = n;
-    result[1] = targ[n];
+// One wave per row (up to 16 rows at a time): lane l holds slice l, the
+// wave reduces them; then thread 0 walks the draft tokens.
+constexpr int kAcceptWaves = 16;
+__global__ __launch_bounds__(64 * kAcceptWaves) void accept_kernel(int R, int S, const uint2 *__restrict__ part,
+                                                                   const int32_t *__restrict__ draft,
+                                                                   int32_t *__restrict__ targ,
+                                                                   int32_t *__restrict__ result) {
+    __shared__ int st[kMaxM];                    // R <= kMaxM (checked by the ABI)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int r = wave; r < R; r += blockDim.x >> 6) {
+        float bv = -__builtin_inff();
+        int bi = 0x7FFFFFFF;
+        if (lane < S) {
+            const uint2 p = part[static_cast<size_t>(r) * S + lane];
+            bv = __builtin_bit_cast(float, p.x);
+            bi = static_cast<int>(p.y);
+        }
+        wave_take(bv, bi);
+        if (lane == 0) {
+            st[r] = bi;
+            targ[r] = bi;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0;
+        while (n < R - 1 && draft[n] == st[n]) ++n;
+        result[0] = n;
+        result[1] = st[n];
+    }
 }
 
 }  // namespace
 
+size_t accept_workspace_bytes(int R, int V) {
+    return static_cast<size_t>(R) * accept_slices(V) * sizeof(uint2);
+}
+
 hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
-                                int32_t *result, hipStream_t stream) {
-    const bool vec = (V % 4) == 0;   // rows then stay 16-byte aligned
-    if (vec)
-        hipLaunchKernelGGL(row_argmax_kernel<true>, dim3(R), dim3(kArgThreads), 0, stream, logits, V, targ);
+                                int32_t *result, void *work, hipStream_t stream) {
+    const int S = accept_slices(V);
+    const int L = accept_slice_len(V, S);
+    uint2 *part = static_cast<uint2 *>(work);
+    if ((V % 4) == 0)      // rows then stay 16-byte aligned
+        hipLaunchKernelGGL(slice_argmax_kernel<true>, dim3(S, R), dim3(kSliceThreads), 0, stream, logits, V, L, part);
     else
-        hipLaunchKernelGGL(row_argmax_kernel<false>, dim3(R), dim3(kArgThreads), 0, stream, logits, V, targ);
+        hipLaunchKernelGGL(slice_argmax_kernel<false>, dim3(S, R), dim3(kSliceThreads), 0, stream, logits, V, L, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, stream, R, draft, targ, result);
+    const int waves = R < kAcceptWaves ? R : kAcceptWaves;
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64 * waves), 0, stream, R, S, part, draft, targ, result);
     return hipGetLastError();
 }
 

@@ -59,8 +59,10 @@ hipError_t launch_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t
 
 // Greedy verification: target argmax per row of logits [R, V] -> targ [R];
 // result = {accepted count, next token}.
+// work: accept_workspace_bytes(R, V) bytes of per-slice partials.
+size_t accept_workspace_bytes(int R, int V);
 hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
-                                int32_t *result, hipStream_t stream);
+                                int32_t *result, void *work, hipStream_t stream);
 
 // Decode attention over the nested KV cache.
 constexpr int kKvHeadDim = 128;
