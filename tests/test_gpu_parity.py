@@ -141,6 +141,22 @@ def test_linear_matches_oracle(M, N, K, act_group, target):
     _check_y(y, y64, "M=%d N=%d K=%d g=%d t=%s" % (M, N, K, act_group, target))
 
 
+@pytest.mark.parametrize("N", [16390, 32770])   # 2 and 4 row tiles per workgroup on 256 CUs, ragged last tile
+@pytest.mark.parametrize("M", [8, 17, 32])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_batched_verify_several_row_tiles(M, N, act_group, target):
+    # the batched-verify kernel gives a workgroup several 16-row tiles when N
+    # is large (shared activation loads); every row is checked
+    w, x = _problem(M, N, 256, seed=3)
+    xq, xs, y = _run(w, x, act_group, target)
+    hi, lo, sc = w.numpy()
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    y64 = oracle.linear(q, s, hi, sc, lo if target else None, act_group)
+    _check_y(y, y64, "M=%d N=%d g=%d t=%s" % (M, N, act_group, target))
+
+
 @pytest.mark.parametrize("M", [1, 4, 8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 def test_target_equals_draft_when_lo_is_8(M, act_group):

@@ -72,29 +72,34 @@ constexpr int kAuxStream = 2;   // non-temporal: plane bytes are read once
 constexpr int kOOB = 0x7FFFFFF0;
 
 
-// One item = one 128-column group of the wave's 16-row tile: 16 plane bytes
-// per lane per plane, the group's scale bits for the lane's row, and the 32
-// activation bytes of the lane's token (per 16-token tile) in the same
-// columns.
-template <int PLANES, int T>
+// One item = one 128-column group of the workgroup's RT 16-row tiles: 16
+// plane bytes per lane per plane and tile, the group's scale bits for the
+// lane's row in each tile, and the 32 activation bytes of the lane's token
+// (per 16-token tile) in the same columns, shared by the RT row tiles.
+template <int PLANES, int T, int RT>
 struct VItem {
-    u32x4 h, l;
-    unsigned sbits;
+    u32x4 h[RT], l[RT];
+    unsigned sbits[RT];
     u32x4 x[T][2];
 };
 
-// T: 16-token tiles (1 for M <= 16, 2 for M <= 32). SPLIT: waves per tile
-// (each streams a contiguous range of the K groups). D: items in flight.
+// T: 16-token tiles (1 for M <= 16, 2 for M <= 32). SPLIT: waves per
+// workgroup (each streams a contiguous range of the K groups). D: items in
+// flight. RT: 16-row tiles per workgroup.
 //
-// A workgroup owns one 16-row tile. Lane l works on weight row l % 16 and
-// token l % 16 (+16 t) in quarter l / 16 of each group, so every load has a
-// lane-constant vector offset and a wave-uniform scalar offset; rows past N
-// and tokens past M fall outside the buffer descriptors and read as zero.
-template <int PLANES, int T, bool GA, bool EXPORT, int SPLIT, int D>
+// A workgroup owns RT consecutive 16-row tiles. Lane l works on weight row
+// l % 16 of each tile and token l % 16 (+16 t) in quarter l / 16 of each
+// group, so every load has a lane-constant vector offset and a wave-uniform
+// scalar offset; rows past N and tokens past M fall outside the buffer
+// descriptors and read as zero. Each activation load feeds the MFMAs of all
+// RT row tiles, so the activation bytes a workgroup reads from L2 per plane
+// byte fall by RT.
+template <int PLANES, int T, bool GA, bool EXPORT, int SPLIT, int D, int RT>
 __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArgs a) {
+    static_assert(RT <= SPLIT, "one wave per row tile writes the outputs");
     extern __shared__ __align__(16) unsigned char smem[];
-    float *red = reinterpret_cast<float *>(smem);                       // [SPLIT][T][4][64]
-    float *sact = red + SPLIT * T * 4 * 64;                              // [G][16 T] (GA)
+    float *red = reinterpret_cast<float *>(smem);                       // [SPLIT][RT][T][4][64]
+    float *sact = red + SPLIT * RT * T * 4 * 64;                         // [G][16 T] (GA)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -103,8 +108,8 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     const int row_bytes = K >> 1;
     const int col = lane & 15;          // weight row within the tile; token within an A tile
     const int kq = lane >> 4;           // quarter of the group; token quad of a D tile
-    const int row0 = blockIdx.x * kRowsPerBlock;
-    const int rows = N - row0 < kRowsPerBlock ? N - row0 : kRowsPerBlock;
+    const int row0 = blockIdx.x * kRowsPerBlock * RT;
+    const int rows = N - row0 < kRowsPerBlock * RT ? N - row0 : kRowsPerBlock * RT;   // of the RT tiles
     // draft: (16 P_hi) * scale / 16; target: 16 (16 P_hi + P_lo) * scale / 256
     const float fscale = PLANES == 2 ? 0.00390625f : 0.0625f;
 
@@ -115,8 +120,12 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + static_cast<size_t>(row0) * G,
                                                 static_cast<unsigned>(rows) * G * 2u);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, static_cast<unsigned>(M) * K);
-    const int voff_w = col * row_bytes + kq * 16;
-    const int voff_s = col * G * 2;
+    int voff_w[RT], voff_s[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        voff_w[rt] = (16 * rt + col) * row_bytes + kq * 16;
+        voff_s[rt] = (16 * rt + col) * G * 2;
+    }
     int voff_x[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) voff_x[t] = (16 * t + col) * K + kq * 32;
@@ -136,14 +145,18 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     const int n_items = g_end - g_begin;
 
     int iseq = 0;
-    auto issue = [&](VItem<PLANES, T> &x) {
+    auto issue = [&](VItem<PLANES, T, RT> &x) {
         const int g = g_begin + iseq;
         const bool live = iseq < n_items;
         const int sw = live ? g * 64 : kOOB;
-        x.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, voff_w, sw, kAuxStream));
-        if (PLANES == 2)
-            x.l = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, voff_w, sw, kAuxStream));
-        if (!EXPORT) x.sbits = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, live ? g * 2 : kOOB, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            x.h[rt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, voff_w[rt], sw, kAuxStream));
+            if (PLANES == 2)
+                x.l[rt] =
+                    __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, voff_w[rt], sw, kAuxStream));
+            if (!EXPORT) x.sbits[rt] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s[rt], live ? g * 2 : kOOB, 0);
+        }
         const int sx = live ? g * kGroup : kOOB;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -153,65 +166,76 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
         ++iseq;
     };
 
-    float yacc[T][4];
+    float yacc[RT][T][4];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[t][r] = 0.0f;
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[rt][t][r] = 0.0f;
 
     int cseq = 0;
-    auto consume = [&](const VItem<PLANES, T> &x) {
+    auto consume = [&](const VItem<PLANES, T, RT> &x) {
         const int g = g_begin + cseq;
         ++cseq;
-        i32x4 bhe, bho, ble, blo;
-        signed16(x.h, bhe, bho);
-        if (PLANES == 2) signed16(x.l, ble, blo);
-        const float sc = half_bits_to_float(static_cast<uint16_t>(x.sbits)) * fscale;
+        i32x4 ae[T], ao[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) split_act(x.x[t][0], x.x[t][1], ae[t], ao[t]);
+        float sa[T][4];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            i32x4 ae, ao;
-            split_act(x.x[t][0], x.x[t][1], ae, ao);
-            const i32x4 zero = {0, 0, 0, 0};
-            i32x4 dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, bhe, zero, 0, 0, 0);
-            dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao, bho, dh, 0, 0, 0);
-            i32x4 dl = zero;
-            if (PLANES == 2) {
-                dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, ble, zero, 0, 0, 0);
-                dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao, blo, dl, 0, 0, 0);
+            sa[t][0] = sa[t][1] = sa[t][2] = sa[t][3] = 1.0f;
+            if (GA && !EXPORT) {
+                const float4 v = *reinterpret_cast<const float4 *>(sact + g * 16 * T + 16 * t + 4 * kq);
+                sa[t][0] = v.x; sa[t][1] = v.y; sa[t][2] = v.z; sa[t][3] = v.w;
             }
-            if (EXPORT) {
+        }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = 16 * t + 4 * kq + r;
-                    if (tok < M && col < rows) {
-                        const size_t o = (static_cast<size_t>(tok) * N + row0 + col) * G + g;
-                        const int ph = dh[r] >> 4;
-                        a.p_hi[o] = ph;
-                        if (PLANES == 2) {
-                            const int pl = dl[r] >> 4;
-                            a.p_lo[o] = pl;
-                            a.p8[o] = 16 * ph + pl;
+        for (int rt = 0; rt < RT; ++rt) {
+            i32x4 bhe, bho, ble, blo;
+            signed16(x.h[rt], bhe, bho);
+            if (PLANES == 2) signed16(x.l[rt], ble, blo);
+            const float sc = half_bits_to_float(static_cast<uint16_t>(x.sbits[rt])) * fscale;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const i32x4 zero = {0, 0, 0, 0};
+                i32x4 dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae[t], bhe, zero, 0, 0, 0);
+                dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao[t], bho, dh, 0, 0, 0);
+                i32x4 dl = zero;
+                if (PLANES == 2) {
+                    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae[t], ble, zero, 0, 0, 0);
+                    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao[t], blo, dl, 0, 0, 0);
+                }
+                if (EXPORT) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = 16 * t + 4 * kq + r;
+                        const int row = 16 * rt + col;
+                        if (tok < M && row < rows) {
+                            const size_t o = (static_cast<size_t>(tok) * N + row0 + row) * G + g;
+                            const int ph = dh[r] >> 4;
+                            a.p_hi[o] = ph;
+                            if (PLANES == 2) {
+                                const int pl = dl[r] >> 4;
+                                a.p_lo[o] = pl;
+                                a.p8[o] = 16 * ph + pl;
+                            }
                         }
                     }
-                }
-            } else {
-                float sa[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-                if (GA) {
-                    const float4 v = *reinterpret_cast<const float4 *>(sact + g * 16 * T + 16 * t + 4 * kq);
-                    sa[0] = v.x; sa[1] = v.y; sa[2] = v.z; sa[3] = v.w;
-                }
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // draft: 16 P_hi; target: 16 (16 P_hi) + 16 P_lo = 16 P8
-                    const int p = PLANES == 2 ? 16 * dh[r] + dl[r] : dh[r];
-                    const float w = GA ? sc * sa[r] : sc;
-                    yacc[t][r] += static_cast<float>(p) * w;
+                    for (int r = 0; r < 4; ++r) {
+                        // draft: 16 P_hi; target: 16 (16 P_hi) + 16 P_lo = 16 P8
+                        const int p = PLANES == 2 ? 16 * dh[r] + dl[r] : dh[r];
+                        const float w = GA ? sc * sa[t][r] : sc;
+                        yacc[rt][t][r] += static_cast<float>(p) * w;
+                    }
                 }
             }
         }
     };
 
-    VItem<PLANES, T> ring[D];
+    VItem<PLANES, T, RT> ring[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(ring[d]);
     for (int base = 0; base < n_items; base += D) {
@@ -223,12 +247,18 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     }
 
     if (!EXPORT) {
+        // the waves' partial sums meet in LDS; wave rt sums them in wave
+        // order for row tile rt and writes its outputs
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[((wave * T + t) * 4 + r) * 64 + lane] = yacc[t][r];
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[(((wave * RT + rt) * T + t) * 4 + r) * 64 + lane] = yacc[rt][t][r];
         __syncthreads();
-        if (wave == 0) {
+        if (wave < RT) {
+            const int rt = wave;
+            const int row = 16 * rt + col;
             float tok_scale[T][4];
             if (!GA) {
 #pragma unroll
@@ -243,12 +273,12 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
             for (int t = 0; t < T; ++t) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = red[((0 * T + t) * 4 + r) * 64 + lane];
+                    float v = red[(((0 * RT + rt) * T + t) * 4 + r) * 64 + lane];
 #pragma unroll
-                    for (int w = 1; w < SPLIT; ++w) v += red[((w * T + t) * 4 + r) * 64 + lane];
+                    for (int w = 1; w < SPLIT; ++w) v += red[(((w * RT + rt) * T + t) * 4 + r) * 64 + lane];
                     const int tok = 16 * t + 4 * kq + r;
-                    if (tok < M && col < rows)
-                        a.y[static_cast<size_t>(tok) * N + row0 + col] = GA ? v : v * tok_scale[t][r];
+                    if (tok < M && row < rows)
+                        a.y[static_cast<size_t>(tok) * N + row0 + row] = GA ? v : v * tok_scale[t][r];
                 }
             }
         }
@@ -257,14 +287,29 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
 
 typedef void (*VerifyKernel)(const LinearArgs);
 
-constexpr int kSplit = 8;     // waves per 16-row tile
+constexpr int kSplit = 8;     // waves per workgroup
 constexpr int kVerifyItems = 2;
 
-template <int PLANES, int T>
+template <int PLANES, int T, int RT>
 VerifyKernel pick_mode(bool grouped, bool exporting) {
-    if (exporting) return verify_mfma_kernel<PLANES, T, false, true, kSplit, kVerifyItems>;
-    return grouped ? verify_mfma_kernel<PLANES, T, true, false, kSplit, kVerifyItems>
-                   : verify_mfma_kernel<PLANES, T, false, false, kSplit, kVerifyItems>;
+    if (exporting) return verify_mfma_kernel<PLANES, T, false, true, kSplit, kVerifyItems, 1>;
+    return grouped ? verify_mfma_kernel<PLANES, T, true, false, kSplit, kVerifyItems, RT>
+                   : verify_mfma_kernel<PLANES, T, false, false, kSplit, kVerifyItems, RT>;
+}
+
+template <int PLANES, int T>
+VerifyKernel pick_rt(int rt, bool grouped, bool exporting) {
+    return rt == 4 ? pick_mode<PLANES, T, 4>(grouped, exporting)
+                   : rt == 2 ? pick_mode<PLANES, T, 2>(grouped, exporting) : pick_mode<PLANES, T, 1>(grouped, exporting);
+}
+
+// Row tiles per workgroup: as many (up to 4) as keep at least two
+// workgroups per compute unit.
+int verify_row_tiles(int N, int cus) {
+    const int tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
+    int rt = 4;
+    while (rt > 1 && (tiles + rt - 1) / rt < 2 * cus) rt >>= 1;
+    return rt;
 }
 
 }  // namespace
@@ -274,25 +319,26 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
     const int T = a.M <= 16 ? 1 : 2;
     const bool target = a.lo != nullptr;
     const bool grouped = a.act_group == kGroup && !export_partials;
-    VerifyKernel k;
-    if (target)
-        k = T == 1 ? pick_mode<2, 1>(grouped, export_partials) : pick_mode<2, 2>(grouped, export_partials);
-    else
-        k = T == 1 ? pick_mode<1, 1>(grouped, export_partials) : pick_mode<1, 2>(grouped, export_partials);
-    // the partial-sum exchange [kSplit][T][4][64] and the grouped
-    // activation-scale table [G][16 T]
-    const size_t G = a.K / kGroup;
-    const size_t lds = static_cast<size_t>(kSplit) * T * 4 * 64 * 4 + (grouped ? G * 16 * T * 4 : 0);
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
+    const int RT = export_partials ? 1 : verify_row_tiles(a.N, dev.cus);   // the export is for checking
+    VerifyKernel k;
+    if (target)
+        k = T == 1 ? pick_rt<2, 1>(RT, grouped, export_partials) : pick_rt<2, 2>(RT, grouped, export_partials);
+    else
+        k = T == 1 ? pick_rt<1, 1>(RT, grouped, export_partials) : pick_rt<1, 2>(RT, grouped, export_partials);
+    // the partial-sum exchange [kSplit][RT][T][4][64] and the grouped
+    // activation-scale table [G][16 T]
+    const size_t G = a.K / kGroup;
+    const size_t lds = static_cast<size_t>(kSplit) * RT * T * 4 * 64 * 4 + (grouped ? G * 16 * T * 4 : 0);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
     if (lds > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    const int blocks = (a.N + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int blocks = (a.N + kRowsPerBlock * RT - 1) / (kRowsPerBlock * RT);
     hipLaunchKernelGGL(k, dim3(blocks), dim3(64 * kSplit), lds, stream, a);
     return hipGetLastError();
 }
