@@ -66,7 +66,7 @@ hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t
 
 // Decode attention over the nested KV cache.
 constexpr int kKvHeadDim = 128;
-constexpr int kKvChunk = 64;        // positions per partial
+constexpr int kKvChunk = 64;        // positions per chunk; a split (one partial) is a run of chunks
 constexpr int kKvMaxRows = 16;      // M x (Hq / Hkv) query rows per KV head
 struct KvArgs {
     const float *q;                 // [M, Hq, 128]

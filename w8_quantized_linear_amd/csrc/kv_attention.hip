@@ -12,11 +12,12 @@
 //  - kv_attn_split_kernel: one workgroup per (split, KV head), for all M x G
 //    (<= 16) query rows of that head; a split is a contiguous run of
 //    64-position chunks, their number sized to about two workgroups per
-//    compute unit. Each wave walks every fourth 16-position tile of the
-//    split on its own (the next tile's loads in flight while the current one
-//    is consumed): scores and P.V on the fp16 matrix cores, a running
-//    softmax per query row. The four waves then merge in LDS in a fixed
-//    order and the split's (output, maximum, sum) per row go to the caller's
+//    compute unit. Each wave walks every fourth step of the split on its own
+//    (a step is 16 positions, or 32 when a split holds several chunks; the
+//    loads of the next one or two steps are in flight while one is
+//    consumed): scores and P.V on the fp16 matrix cores, a running softmax
+//    per query row. The four waves then merge in LDS in a fixed order and
+//    the split's (output, maximum, sum) per row go to the caller's
 //    workspace. Scores are kept in base-2 units (log2(e) folded into the
 //    scale), so every exponential is one v_exp_f32.
 //  - kv_attn_combine_kernel: one workgroup per query row merges the splits:
@@ -29,16 +30,14 @@ namespace bitnest {
 namespace {
 
 constexpr int kD = kKvHeadDim;       // 128
-constexpr int kC = kKvChunk;         // 64 positions: one step of the four waves
-constexpr int kTile = 16;            // positions per wave step
+constexpr int kC = kKvChunk;         // 64 positions: the unit a split is made of
+constexpr int kTile = 16;            // positions per score tile (a wave step is NT tiles)
 constexpr int kRows = kKvMaxRows;    // 16 query rows: one matrix-core tile
 constexpr int kKvThreads = 256;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr unsigned kF16Base = 0x64006400u;      // fp16 1024.0 in both halves
 constexpr float kLog2e = 1.44269504088896340736f;
