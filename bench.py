@@ -558,7 +558,7 @@ def cpu_baseline(stack, budget_s):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
     import torch
