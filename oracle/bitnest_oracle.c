@@ -23,7 +23,7 @@
  *        q    = 0 if s == 0, else clamp(round_half_even(x / s), -127, 127)
  *    with x / s an IEEE fp32 division. Both sides take this integer decision
  *    in fp32.
- *  - The linear itself is the plain definition "dequantise, then multiply":
+ *  - The linear itself is the plain definition: dequantise, then multiply,
  *        y[m, n] = sum_k (q[m, k] * s_a) * W[n, k]
  *    in fp64, k ascending, with s_a the token's (or the token-group's) scale
  *    and W the draft or target weight above.
