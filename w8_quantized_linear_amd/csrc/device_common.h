@@ -82,9 +82,19 @@ __device__ __forceinline__ void quant_codes(const float (&x)[n], float s, float 
         dist = fmaxf(dist, fabsf(__builtin_fmaf(x[i], r, -(v - kRoundMagic))));
         y[i] = __builtin_bit_cast(unsigned, v);
     }
-    if (!(dist <= 0.49997f) || !(r <= 3.0e38f)) {
+    // The redo is rare: the test is made wave-wide first, so that the
+    // divisions are branched over (not computed for every lane and
+    // discarded) when no lane of the wave needs them. The empty asm passes
+    // the scale through a register the compiler cannot see into, so that the
+    // divisions stay inside the branch instead of being hoisted above it.
+    const bool redo = !(dist <= 0.49997f) || !(r <= 3.0e38f);
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        float sv = s;
+        asm volatile("" : "+v"(sv));
+        if (redo) {
 #pragma unroll
-        for (int i = 0; i < n; ++i) y[i] = __builtin_bit_cast(unsigned, rintf(x[i] / s) + kRoundMagic);
+            for (int i = 0; i < n; ++i) y[i] = __builtin_bit_cast(unsigned, rintf(x[i] / sv) + kRoundMagic);
+        }
     }
 }
 
