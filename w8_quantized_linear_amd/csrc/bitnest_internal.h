@@ -41,6 +41,10 @@ struct LinearArgs {
     // only): block size (0 = none) and the fp32 value nearest 1/sqrt(block)
     int rot_block;
     float rot_scale;
+    // set by the plane-streaming GEMV's launcher: N = rows_q * waves + rows_r
+    // over the launch's waves
+    int rows_q;
+    int rows_r;
 };
 
 constexpr int kMaxRotBlock = 512;   // a rotation block stays inside one wave (64 lanes x 8)

@@ -197,13 +197,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
     const int voff_plane = lane * 16;          // lane's 16 bytes within a chunk
     const int voff_scale = (lane >> 2) * 2;    // its group's scale within the chunk's 16 groups
 
-    // this wave's rows [row_begin, row_end): whole rows, so that exactly one
-    // wave owns each output; its items are the C chunks of each row, in order
-    const long long gw = static_cast<long long>(blockIdx.x) * WAVES + wave;
-    const long long W = static_cast<long long>(gridDim.x) * WAVES;
-    const int row_begin = static_cast<int>(N * gw / W);
-    const int row_end = static_cast<int>(N * (gw + 1) / W);
-    const int n_items = (row_end - row_begin) * C;
+    // this wave's rows [row_begin, row_begin + rows): whole rows, so that
+    // exactly one wave owns each output; its items are the C chunks of each
+    // row, in order. Of the grid's waves, the first rows_r take rows_q + 1
+    // rows and the rest rows_q (the launcher's quotient and remainder of N by
+    // the wave count, so no division is made here).
+    const int gw = static_cast<int>(blockIdx.x) * WAVES + wave;
+    const int row_begin = gw * a.rows_q + min(gw, a.rows_r);
+    const int n_items = (a.rows_q + (gw < a.rows_r ? 1 : 0)) * C;
 
     // Issue the loads of the next item in order. Items past this wave's run
     // are given an offset beyond the plane, which the buffer unit answers
@@ -298,21 +299,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
     } else {
         static_assert(M == 1, "the fused prologue quantises one token");
         // 1) the fp32 row in 8-column units u = tid + k * threads (k < XU),
-        //    two 16-byte loads each; waves wholly past the row skip them and
-        //    lanes past it read zeros; then the ring
+        //    two 16-byte loads each; lanes past the row read zeros (the
+        //    descriptor ends with the row, and such loads make no memory
+        //    traffic). The loads are unconditional (under a branch, the
+        //    compiler adds register copies at its join). The row arrives
+        //    before the ring is issued: every code needs the row's maximum, so
+        //    the row's loads are the critical path, and issued together with
+        //    the ring's (a far larger batch over the whole chip) they return
+        //    later, while the ring's data is not needed before the codes are
+        //    in LDS anyway (measured: 0.3 to 0.5 us less per launch).
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, static_cast<unsigned>(K) * 4u);
         const int nunit = K >> 3;
         u32x4 xr[XU][2];
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
-            xr[k][0] = u32x4{0u, 0u, 0u, 0u};
-            xr[k][1] = xr[k][0];
-            if (k * kThreads + wave * 64 < nunit) {      // wave-uniform
-                const int off = (threadIdx.x + k * kThreads) * 32;
-                xr[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-                xr[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
-            }
+            const int off = (threadIdx.x + k * kThreads) * 32;
+            xr[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            xr[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(ring[d]);
 
@@ -368,9 +373,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
             am = wave_max_dpp_f32(am);
             if (lane == 0) part[wave] = am;
             __syncthreads();
-            am = part[0];
+            // the per-wave maxima as 16-byte reads, all in flight together
+            static_assert(WAVES % 4 == 0, "per-wave maxima are read four at a time");
+            float4 pm[WAVES / 4];
 #pragma unroll
-            for (int w = 1; w < WAVES; ++w) am = fmaxf(am, part[w]);
+            for (int w = 0; w < WAVES / 4; ++w) pm[w] = reinterpret_cast<const float4 *>(part)[w];
+            am = fmaxf(fmaxf(pm[0].x, pm[0].y), fmaxf(pm[0].z, pm[0].w));
+#pragma unroll
+            for (int w = 1; w < WAVES / 4; ++w)
+                am = fmaxf(am, fmaxf(fmaxf(pm[w].x, pm[w].y), fmaxf(pm[w].z, pm[w].w)));
             tok_scale[0] = am / 127.0f;
             const float r = quant_recip(tok_scale[0]);
             if (blockIdx.x == 0 && threadIdx.x == 0) a.xs_out[0] = tok_scale[0];
@@ -597,7 +608,10 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
     const int rows_blocks = (a.N + waves - 1) / waves;
     const int full = dev.cus * occ;
     const int blocks = rows_blocks < full ? rows_blocks : full;
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), lds, stream, a);
+    LinearArgs b = a;
+    b.rows_q = a.N / (blocks * waves);
+    b.rows_r = a.N % (blocks * waves);
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), lds, stream, b);
     return hipGetLastError();
 }
 
