@@ -138,18 +138,18 @@ __device__ __forceinline__ float wave_max_dpp_f32(float v) {
 
 // One cross-lane stage of fwht_unit: lanes with bit m clear hold a = z[i],
 // their partners (lane ^ m) hold c = z[i + 8 m]; the lower lane keeps
-// a + c, the upper one a - c, computed as partner + (+-own) (an IEEE
-// subtraction is the addition of the negated operand, so the bits are those
-// of a - c). The partner's value comes without LDS traffic where the
-// hardware allows: DPP quad permutes (m = 1, 2), DPP row rotate by 8 (m = 8),
-// a swizzle (m = 4); for m = 16 and 32 the gfx950 row / half-wave swaps
+// a + c, the upper one a - c, computed as fma(own, +-1, partner): the product
+// by +-1 is exact and the fma rounds once, so the bits are those of a + c and
+// a - c. The partner's value comes without LDS traffic where the hardware
+// allows: DPP quad permutes (m = 1, 2), DPP row rotate by 8 (m = 8), a
+// swizzle (m = 4); for m = 16 and 32 the gfx950 row / half-wave swaps
 // exchange the two halves of (v, v), after which the first result holds the
 // lower lane's value and the second the upper lane's, in both lanes of a
 // pair.
 template <int m>
 __device__ __forceinline__ void fwht_cross_stage(float (&v)[8], int lane) {
     static_assert(m == 1 || m == 2 || m == 4 || m == 8 || m == 16 || m == 32, "lane masks 1..32");
-    const unsigned neg = (lane & m) ? 0x80000000u : 0u;          // upper lanes subtract their own value
+    const float sgn = (lane & m) ? -1.0f : 1.0f;          // upper lanes subtract their own value
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const unsigned u = __builtin_bit_cast(unsigned, v[i]);
@@ -164,15 +164,26 @@ __device__ __forceinline__ void fwht_cross_stage(float (&v)[8], int lane) {
                 lo = r[0];
                 hi = r[1];
             }
-            v[i] = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi ^ neg);
+            v[i] = __builtin_fmaf(__builtin_bit_cast(float, hi), sgn, __builtin_bit_cast(float, lo));
         } else {
             float p;
             if constexpr (m == 1) p = dpp_f32<kDppQuadSwap1>(v[i]);
             else if constexpr (m == 2) p = dpp_f32<kDppQuadSwap2>(v[i]);
             else if constexpr (m == 8) p = dpp_f32<kDppRowRor8>(v[i]);
             else p = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(static_cast<int>(u), 0x1F | (4 << 10)));
-            v[i] = p + __builtin_bit_cast(float, u ^ neg);
+            v[i] = __builtin_fmaf(v[i], sgn, p);
         }
+    }
+}
+
+// The stages of fwht_unit inside one lane, h = 1, 2, 4 while h < b.
+__device__ __forceinline__ void fwht_lane_stage(float (&v)[8], int h) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i & h) continue;
+        const float a = v[i], c = v[i + h];
+        v[i] = a + c;
+        v[i + h] = a - c;
     }
 }
 
@@ -187,23 +198,31 @@ __device__ __forceinline__ void fwht_cross_stage(float (&v)[8], int lane) {
 // partner lane lane ^ (h / 8). The caller then scales by r_b.
 __device__ __forceinline__ void fwht_unit(float (&v)[8], int lane, int b) {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-        if (h < b) {                                   // uniform
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i & h) continue;
-                const float a = v[i], c = v[i + h];
-                v[i] = a + c;
-                v[i + h] = a - c;
-            }
-        }
-    }
+    for (int h = 1; h < 8; h <<= 1)
+        if (h < b) fwht_lane_stage(v, h);               // uniform
     if (b > 8) fwht_cross_stage<1>(v, lane);            // uniform conditions
     if (b > 16) fwht_cross_stage<2>(v, lane);
     if (b > 32) fwht_cross_stage<4>(v, lane);
     if (b > 64) fwht_cross_stage<8>(v, lane);
     if (b > 128) fwht_cross_stage<16>(v, lane);
     if (b > 256) fwht_cross_stage<32>(v, lane);
+}
+
+// fwht_unit with the block size B fixed when compiling: the same stages as
+// straight-line code (with a run-time size, the compiler places each stage
+// behind a branch, away from the rest).
+template <int B>
+__device__ __forceinline__ void fwht_unit_fixed(float (&v)[8], int lane) {
+    static_assert(B >= 2 && B <= 512 && (B & (B - 1)) == 0, "a power of two in [2, 512]");
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+        if (h < B) fwht_lane_stage(v, h);
+    if constexpr (B > 8) fwht_cross_stage<1>(v, lane);
+    if constexpr (B > 16) fwht_cross_stage<2>(v, lane);
+    if constexpr (B > 32) fwht_cross_stage<4>(v, lane);
+    if constexpr (B > 64) fwht_cross_stage<8>(v, lane);
+    if constexpr (B > 128) fwht_cross_stage<16>(v, lane);
+    if constexpr (B > 256) fwht_cross_stage<32>(v, lane);
 }
 
 __device__ __forceinline__ float absmax4(const float4 &v) {

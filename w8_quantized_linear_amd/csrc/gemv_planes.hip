@@ -161,8 +161,10 @@ struct Item {
 // scales. EXPORT: write the integer partials instead of y. D: items in flight
 // per wave. WAVES: waves per workgroup. XU: 0, or (one token only) quantise
 // the fp32 input in the prologue, XU 8-column units per thread. ROT (with XU):
-// apply the R4 rotation (fwht_unit, blocks of a.rot_block columns, times
-// a.rot_scale) to the fp32 input before quantising it.
+// 0, or apply the R4 rotation (blocks of a.rot_block columns, times
+// a.rot_scale) to the fp32 input before quantising it: ROT = 1 takes the
+// block size from a.rot_block, any other value is that block size fixed when
+// compiling (which the launcher picks only when a.rot_block equals it).
 //
 // A row of K columns is C = ceil(K / 2048) chunks; the (row, chunk) items of
 // the whole call are split into contiguous runs, one per wave, and each wave
@@ -171,7 +173,7 @@ struct Item {
 // (scalar registers) plus a fixed lane offset, so address arithmetic stays
 // off the vector ALU; loads past the end of a plane return 0. The workgroup
 // stages the codes once into LDS while its first D items are in flight.
-template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, int XU, bool ROT>
+template <int PLANES, int M, bool GA, bool EXPORT, int D, int WAVES, int XU, int ROT>
 __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArgs a) {
     constexpr bool FUSED = XU > 0;
     constexpr int kThreads = 64 * WAVES;
@@ -332,13 +334,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
                 xf[k][i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][0][i]));
                 xf[k][4 + i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][1][i]));
             }
-        if (ROT) {
+        if constexpr (ROT != 0) {
             // unit u = tid + k * threads: one wave's units at one k are 512
             // consecutive columns, so every rotation block is inside a wave
 #pragma unroll
             for (int k = 0; k < XU; ++k) {
-                if (k * kThreads + wave * 64 < nunit) {  // wave-uniform: units past the row stay zero
-                    fwht_unit(xf[k], lane, a.rot_block);
+                // wave-uniform: units past the row stay zero (marked as the
+                // rare case, so that the transform is laid out in line)
+                if (__builtin_expect(k * kThreads + wave * 64 < nunit, 1)) {
+                    if constexpr (ROT == 1) fwht_unit(xf[k], lane, a.rot_block);
+                    else fwht_unit_fixed<ROT>(xf[k], lane);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) xf[k][i] = xf[k][i] * a.rot_scale;
                 }
@@ -524,9 +529,9 @@ template <int PLANES, int M>
 GemvKernel pick_mode(bool grouped, bool exporting) {
     constexpr int D = items_in_flight<PLANES>();
     constexpr int W = kGemvWaves;
-    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, 0, false>;
-    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, 0, false>
-                   : gemv_planes_kernel<PLANES, M, false, false, D, W, 0, false>;
+    if (exporting) return gemv_planes_kernel<PLANES, M, false, true, D, W, 0, 0>;
+    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, W, 0, 0>
+                   : gemv_planes_kernel<PLANES, M, false, false, D, W, 0, 0>;
 }
 
 template <int PLANES>
@@ -547,19 +552,26 @@ GemvKernel pick_m(int M, bool grouped, bool exporting) {
 constexpr int fused_units(int K) { return (K / 8 + 64 * kFusedWaves - 1) / (64 * kFusedWaves); }
 static_assert(fused_units(kFusedMaxMK) <= 4, "pick_fused covers up to four units per thread");
 
+// The rotation block the fused kernel has a straight-line instantiation for
+// (the R4 recipe's block here); other block sizes take it from the arguments.
+constexpr int kRotFixedBlock = 512;
+static_assert(kRotFixedBlock <= kMaxRotBlock, "a rotation block stays inside one wave");
+
 template <int PLANES, int XU>
-GemvKernel pick_fused_xu(bool grouped, bool rot) {
+GemvKernel pick_fused_xu(bool grouped, int rot_block) {
     constexpr int D = items_in_flight<PLANES>();
-    if (rot) return gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, true>;
-    return grouped ? gemv_planes_kernel<PLANES, 1, true, false, D, kFusedWaves, XU, false>
-                   : gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, false>;
+    if (rot_block == kRotFixedBlock) return gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, kRotFixedBlock>;
+    if (rot_block > 0) return gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, 1>;
+    return grouped ? gemv_planes_kernel<PLANES, 1, true, false, D, kFusedWaves, XU, 0>
+                   : gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, 0>;
 }
 
 template <int PLANES>
-GemvKernel pick_fused(int K, bool grouped, bool rot) {
+GemvKernel pick_fused(int K, bool grouped, int rot_block) {
     const int xu = fused_units(K);
-    return xu <= 1 ? pick_fused_xu<PLANES, 1>(grouped, rot)
-                   : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped, rot) : pick_fused_xu<PLANES, 4>(grouped, rot);
+    return xu <= 1 ? pick_fused_xu<PLANES, 1>(grouped, rot_block)
+                   : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped, rot_block)
+                             : pick_fused_xu<PLANES, 4>(grouped, rot_block);
 }
 
 size_t gemv_lds_bytes(int M, int K, bool grouped, bool fused, int waves, bool sums) {
@@ -580,7 +592,7 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
     const bool grouped = a.act_group == kGroup && !exporting;
     GemvKernel k;
     if (fused)
-        k = target ? pick_fused<2>(a.K, grouped, a.rot_block > 0) : pick_fused<1>(a.K, grouped, a.rot_block > 0);
+        k = target ? pick_fused<2>(a.K, grouped, a.rot_block) : pick_fused<1>(a.K, grouped, a.rot_block);
     else
         k = target ? pick_m<2>(a.M, grouped, exporting) : pick_m<1>(a.M, grouped, exporting);
     if (!k) return hipErrorInvalidValue;

@@ -90,8 +90,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
 // ALU-bound on its one compute unit, so it runs 16 waves, where the plain
 // quantisation is latency-bound and runs 8.)
 constexpr int kRotThreads = 1024;
+// the block size with a straight-line transform (RB below); others take the
+// block from the arguments (RB = 0)
+constexpr int kRotFixedBlock = 512;
 
-template <int NU>
+template <int NU, int RB>
 __global__ __launch_bounds__(kRotThreads) void hadamard_quant_kernel(
     const float *__restrict__ x, int K, int block, float rot_scale, int8_t *__restrict__ q, float *__restrict__ s,
     float *__restrict__ xr) {
@@ -120,7 +123,8 @@ __global__ __launch_bounds__(kRotThreads) void hadamard_quant_kernel(
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
         if (k * TH + (threadIdx.x & ~63) < nunit) {    // wave-uniform: units past K stay zero
-            fwht_unit(v[k], lane, block);
+            if constexpr (RB == 0) fwht_unit(v[k], lane, block);
+            else fwht_unit_fixed<RB>(v[k], lane);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 v[k][i] = v[k][i] * rot_scale;
@@ -160,9 +164,10 @@ hipError_t launch_hadamard_quant_act(const float *x, int M, int K, int block, fl
                                      float *xs, float *xr, hipStream_t stream) {
     const int nu = (K / 8 + kRotThreads - 1) / kRotThreads;
     void (*k)(const float *, int, int, float, int8_t *, float *, float *);
+    const bool fixed = block == kRotFixedBlock;
     switch (nu) {
-        case 1: k = hadamard_quant_kernel<1>; break;
-        case 2: k = hadamard_quant_kernel<2>; break;
+        case 1: k = fixed ? hadamard_quant_kernel<1, kRotFixedBlock> : hadamard_quant_kernel<1, 0>; break;
+        case 2: k = fixed ? hadamard_quant_kernel<2, kRotFixedBlock> : hadamard_quant_kernel<2, 0>; break;
         default: return hipErrorInvalidValue;   // K > kMaxK: rejected by the ABI before this point
     }
     hipLaunchKernelGGL(k, dim3(M), dim3(kRotThreads), 0, stream, x, K, block, rot_scale, xq, xs, xr);
