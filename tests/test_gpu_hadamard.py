@@ -57,7 +57,8 @@ def test_rotation_without_rotated_output_gives_same_codes():
     assert torch.equal(xq1, xq2) and torch.equal(xs1, xs2)
 
 
-FUSED = [(64, 14336, 512), (37, 512, 512), (129, 4096, 512), (33, 1024, 8), (17, 16384, 512)]
+FUSED = [(64, 14336, 512), (37, 512, 512), (129, 4096, 512), (33, 1024, 8), (17, 16384, 512),
+         (65, 2048, 256), (9, 1024, 64)]
 
 
 @pytest.mark.parametrize("N,K,block", FUSED)
