@@ -38,13 +38,14 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
-# (pattern on the demangled kernel name, labels in launch order)
+# (pattern on the demangled kernel name, labels in launch order; the last
+# template argument of gemv_planes_kernel is the rotation block, 0 = none)
 LABELS = [
-    (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 1, false>", ["draft qkv", "draft gate_up"]),
-    (r"^gemv_planes_kernel<1, 1, true, false, \d+, \d+, 1, false>", ["draft o_proj"]),
-    (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 4, false>", ["draft down"]),
-    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 0, false>", ["verify qkv", "verify gate_up", "verify down"]),
-    (r"^gemv_planes_kernel<2, 4, true, false, \d+, \d+, 0, false>", ["verify o_proj"]),
+    (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 1, 0>", ["draft qkv", "draft gate_up"]),
+    (r"^gemv_planes_kernel<1, 1, true, false, \d+, \d+, 1, 0>", ["draft o_proj"]),
+    (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 4, 0>", ["draft down"]),
+    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 0, 0>", ["verify qkv", "verify gate_up", "verify down"]),
+    (r"^gemv_planes_kernel<2, 4, true, false, \d+, \d+, 0, 0>", ["verify o_proj"]),
     (r"^quant_token_kernel<2>", ["quant qkv", "quant gate_up"]),
     (r"^quant_token_kernel<7>", ["quant down"]),
     (r"^quant_group_kernel", ["quant o_proj"]),
