@@ -217,6 +217,8 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _kv(A, 8, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EUNSUPPORTED),
     (lambda: _kv(A, 1, 32, 8, 1 << 23, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
     (lambda: _kv(A, 1, 65536, 65536, 4, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
+    # M * (Hq / Hkv) = 2^32: beyond the row limit (not wrapped to 0)
+    (lambda: _kv(A, 1 << 20, 1 << 12, 1, 1 << 20, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EUNSUPPORTED),
     (lambda: _kv(NUL, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, NUL, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 32, 8, 100, B, C, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
@@ -234,6 +236,8 @@ def test_kv_workspace_size():
     assert bn.bitnest_kv_attention_workspace_bytes(1, 32, 64 * 512) == 512 * 32 * 130 * 4
     assert bn.bitnest_kv_attention_workspace_bytes(4, 32, 131072) == 512 * 4 * 32 * 130 * 4
     assert bn.bitnest_kv_attention_workspace_bytes(0, 32, 10) == 0
+    # the largest T: still 512 splits (no overflow in the chunk count)
+    assert bn.bitnest_kv_attention_workspace_bytes(1, 32, 2 ** 31 - 1) == 512 * 32 * 130 * 4
 
 
 def test_accept_workspace_size():
@@ -244,6 +248,8 @@ def test_accept_workspace_size():
     assert bn.bitnest_greedy_accept_workspace_bytes(32, 4097) == 32 * 2 * 8
     assert bn.bitnest_greedy_accept_workspace_bytes(2, 10 ** 6) == 2 * 64 * 8
     assert bn.bitnest_greedy_accept_workspace_bytes(0, 100) == 0
+    # the largest V: still 64 slices (no overflow in the slice count)
+    assert bn.bitnest_greedy_accept_workspace_bytes(2, 2 ** 31 - 1) == 2 * 64 * 8
 
 
 def test_binding_rejects_cpu_tensors():

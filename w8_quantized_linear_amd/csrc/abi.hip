@@ -244,7 +244,7 @@ bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int 
                                     const uint8_t *v_lo, const uint16_t *v_scale, float *out, void *work,
                                     size_t work_bytes, void *stream) {
     if (M < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || T < M) return BITNEST_EINVAL;
-    if (M * (Hq / Hkv) > BITNEST_KV_MAX_ROWS || Hkv > 65535) return BITNEST_EUNSUPPORTED;
+    if (static_cast<long long>(M) * (Hq / Hkv) > BITNEST_KV_MAX_ROWS || Hkv > 65535) return BITNEST_EUNSUPPORTED;
     if (static_cast<long long>(T) * Hkv * (BITNEST_KV_HEAD_DIM / 2) > 0x7FFFFFFFLL) return BITNEST_EUNSUPPORTED;
     if (!q || !k_hi || !k_scale || !v_hi || !v_scale || !out || !work) return BITNEST_EINVAL;
     if ((k_lo == nullptr) != (v_lo == nullptr)) return BITNEST_EINVAL;

@@ -42,12 +42,14 @@ __device__ __forceinline__ void wave_take(float &bv, int &bi) {
 }
 
 int accept_slices(int V) {
-    const int s = (V + kSliceLogits - 1) / kSliceLogits;
-    return s < 1 ? 1 : (s > kMaxSlices ? kMaxSlices : s);
+    const long long s = (static_cast<long long>(V) + kSliceLogits - 1) / kSliceLogits;   // any V >= 1
+    return s < 1 ? 1 : (s > kMaxSlices ? kMaxSlices : static_cast<int>(s));
 }
 
 // slice length: ceil(V / S) rounded up to a multiple of 4 (whole float4s)
-int accept_slice_len(int V, int S) { return (((V + S - 1) / S) + 3) & ~3; }
+int accept_slice_len(int V, int S) {
+    return static_cast<int>((((static_cast<long long>(V) + S - 1) / S) + 3) & ~3LL);
+}
 
 // part[r S + s] = {bits of the slice's largest logit, its smallest column}
 template <bool VEC>

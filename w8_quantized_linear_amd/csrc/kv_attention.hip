@@ -499,8 +499,8 @@ __global__ __launch_bounds__(kD * kCombineGroups) void kv_attn_combine_kernel(co
 typedef void (*KvSplit)(const KvArgs, int);
 
 int kv_max_splits(int T) {
-    const int nchunks = (T + kC - 1) / kC;
-    return nchunks < kKvMaxSplits ? nchunks : kKvMaxSplits;
+    const long long nchunks = (static_cast<long long>(T) + kC - 1) / kC;   // any T >= 1
+    return nchunks < kKvMaxSplits ? static_cast<int>(nchunks) : kKvMaxSplits;
 }
 
 }  // namespace
@@ -510,7 +510,7 @@ size_t kv_attention_workspace_bytes(int M, int Hq, int T) {
 }
 
 hipError_t launch_kv_attention(const KvArgs &a, hipStream_t stream) {
-    if (a.M * (a.Hq / a.Hkv) > kRows) return hipErrorInvalidValue;   // rejected by the ABI before this point
+    if (static_cast<long long>(a.M) * (a.Hq / a.Hkv) > kRows) return hipErrorInvalidValue;   // rejected by the ABI before this point
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
