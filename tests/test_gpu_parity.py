@@ -157,6 +157,25 @@ def test_batched_verify_several_row_tiles(M, N, act_group, target):
     _check_y(y, y64, "M=%d N=%d g=%d t=%s" % (M, N, act_group, target))
 
 
+# rows per workgroup on 256 CUs: 8 (tiles half empty), 24 with a ragged last
+# workgroup, 24 (the qkv shape), 40 (three tiles, the last with 8 rows), 64
+@pytest.mark.parametrize("N", [1000, 5001, 6144, 10000, 16000])
+@pytest.mark.parametrize("M", [8, 32])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_batched_verify_rows_per_workgroup(M, N, act_group, target):
+    # where N spread over one workgroup per CU fits four 16-row tiles, a
+    # workgroup owns ceil(N / CUs) rows rounded up to 8, and the rows past it
+    # in its last tile read as zero; every row is checked
+    w, x = _problem(M, N, 256, seed=4)
+    xq, xs, y = _run(w, x, act_group, target)
+    hi, lo, sc = w.numpy()
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    y64 = oracle.linear(q, s, hi, sc, lo if target else None, act_group)
+    _check_y(y, y64, "M=%d N=%d g=%d t=%s" % (M, N, act_group, target))
+
+
 @pytest.mark.parametrize("M", [1, 4, 8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 def test_target_equals_draft_when_lo_is_8(M, act_group):

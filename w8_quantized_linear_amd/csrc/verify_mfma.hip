@@ -87,15 +87,16 @@ struct VItem {
 // workgroup (each streams a contiguous range of the K groups). D: items in
 // flight. RT: 16-row tiles per workgroup.
 //
-// A workgroup owns RT consecutive 16-row tiles. Lane l works on weight row
-// l % 16 of each tile and token l % 16 (+16 t) in quarter l / 16 of each
-// group, so every load has a lane-constant vector offset and a wave-uniform
-// scalar offset; rows past N and tokens past M fall outside the buffer
-// descriptors and read as zero. Each activation load feeds the MFMAs of all
+// A workgroup owns R consecutive rows (R <= 16 RT, a multiple of 8), held in
+// RT 16-row tiles. Lane l works on weight row l % 16 of each tile and token
+// l % 16 (+16 t) in quarter l / 16 of each group, so every load has a
+// lane-constant vector offset and a wave-uniform scalar offset; rows past the
+// workgroup's R (or past N) and tokens past M fall outside the buffer
+// descriptors and read as zero, with no memory traffic. Each activation load feeds the MFMAs of all
 // RT row tiles, so the activation bytes a workgroup reads from L2 per plane
 // byte fall by RT.
 template <int PLANES, int T, bool GA, bool EXPORT, int SPLIT, int D, int RT>
-__global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArgs a) {
+__global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArgs a, int R) {
     static_assert(RT <= SPLIT, "one wave per row tile writes the outputs");
     extern __shared__ __align__(16) unsigned char smem[];
     float *red = reinterpret_cast<float *>(smem);                       // [SPLIT][RT][T][4][64]
@@ -108,8 +109,8 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     const int row_bytes = K >> 1;
     const int col = lane & 15;          // weight row within the tile; token within an A tile
     const int kq = lane >> 4;           // quarter of the group; token quad of a D tile
-    const int row0 = blockIdx.x * kRowsPerBlock * RT;
-    const int rows = N - row0 < kRowsPerBlock * RT ? N - row0 : kRowsPerBlock * RT;   // of the RT tiles
+    const int row0 = blockIdx.x * R;
+    const int rows = N - row0 < R ? N - row0 : R;   // of the RT tiles (R <= 16 RT)
     // draft: (16 P_hi) * scale / 16; target: 16 (16 P_hi + P_lo) * scale / 256
     const float fscale = PLANES == 2 ? 0.00390625f : 0.0625f;
 
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     }
 }
 
-typedef void (*VerifyKernel)(const LinearArgs);
+typedef void (*VerifyKernel)(const LinearArgs, int);
 
 constexpr int kSplit = 8;     // waves per workgroup
 constexpr int kVerifyItems = 2;
@@ -299,17 +300,34 @@ VerifyKernel pick_mode(bool grouped, bool exporting) {
 
 template <int PLANES, int T>
 VerifyKernel pick_rt(int rt, bool grouped, bool exporting) {
-    return rt == 4 ? pick_mode<PLANES, T, 4>(grouped, exporting)
-                   : rt == 2 ? pick_mode<PLANES, T, 2>(grouped, exporting) : pick_mode<PLANES, T, 1>(grouped, exporting);
+    switch (rt) {
+        case 4: return pick_mode<PLANES, T, 4>(grouped, exporting);
+        case 3: return pick_mode<PLANES, T, 3>(grouped, exporting);
+        case 2: return pick_mode<PLANES, T, 2>(grouped, exporting);
+        default: return pick_mode<PLANES, T, 1>(grouped, exporting);
+    }
 }
 
-// Row tiles per workgroup: as many (up to 4) as keep at least two
-// workgroups per compute unit.
-int verify_row_tiles(int N, int cus) {
+constexpr int kMaxRowTiles = 4;
+
+// Rows per workgroup (R) and its 16-row tiles (RT). Where N spread over one
+// workgroup per compute unit gives at most kMaxRowTiles tiles, every CU gets
+// one workgroup of R = ceil(N / CUs) rows rounded up to 8 (N = 6144: 24 rows
+// on each of 256 CUs, where whole 16-row tiles would leave half of the CUs
+// with two tiles and half with one). Otherwise whole tiles, as many (up to
+// kMaxRowTiles, a power of two) as keep at least two workgroups per CU.
+void verify_rows(int N, int cus, int *R, int *RT) {
+    const int even = ((N + cus - 1) / cus + 7) & ~7;
+    if (even <= kMaxRowTiles * kRowsPerBlock) {
+        *R = even;
+        *RT = (even + kRowsPerBlock - 1) / kRowsPerBlock;
+        return;
+    }
     const int tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
-    int rt = 4;
+    int rt = kMaxRowTiles;
     while (rt > 1 && (tiles + rt - 1) / rt < 2 * cus) rt >>= 1;
-    return rt;
+    *R = rt * kRowsPerBlock;
+    *RT = rt;
 }
 
 }  // namespace
@@ -322,7 +340,8 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
     DeviceInfo dev;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
-    const int RT = export_partials ? 1 : verify_row_tiles(a.N, dev.cus);   // the export is for checking
+    int R = kRowsPerBlock, RT = 1;                     // the export is for checking: one tile
+    if (!export_partials) verify_rows(a.N, dev.cus, &R, &RT);
     VerifyKernel k;
     if (target)
         k = T == 1 ? pick_rt<2, 1>(RT, grouped, export_partials) : pick_rt<2, 2>(RT, grouped, export_partials);
@@ -338,8 +357,8 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    const int blocks = (a.N + kRowsPerBlock * RT - 1) / (kRowsPerBlock * RT);
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(64 * kSplit), lds, stream, a);
+    const int blocks = (a.N + R - 1) / R;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(64 * kSplit), lds, stream, a, R);
     return hipGetLastError();
 }
 
