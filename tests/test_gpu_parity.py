@@ -158,13 +158,15 @@ def test_batched_verify_several_row_tiles(M, N, act_group, target):
 
 
 # rows per workgroup on 256 CUs: 8 (tiles half empty), 24 with a ragged last
-# workgroup, 24 (the qkv shape), 40 (three tiles, the last with 8 rows), 64
-@pytest.mark.parametrize("N", [1000, 5001, 6144, 10000, 16000])
+# workgroup, 24 (the qkv shape), 40 (three tiles, the last with 8 rows), 64,
+# 80, 112 (the gate_up shape, seven tiles) and 120 (eight tiles); with 17-32
+# tokens the last three take whole tiles instead (at most six per workgroup)
+@pytest.mark.parametrize("N", [1000, 5001, 6144, 10000, 16000, 20000, 28672, 30000])
 @pytest.mark.parametrize("M", [8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 @pytest.mark.parametrize("target", [False, True])
 def test_batched_verify_rows_per_workgroup(M, N, act_group, target):
-    # where N spread over one workgroup per CU fits four 16-row tiles, a
+    # where N spread over one workgroup per CU fits the tile limit, a
     # workgroup owns ceil(N / CUs) rows rounded up to 8, and the rows past it
     # in its last tile read as zero; every row is checked
     w, x = _problem(M, N, 256, seed=4)

@@ -298,33 +298,44 @@ VerifyKernel pick_mode(bool grouped, bool exporting) {
                    : verify_mfma_kernel<PLANES, T, false, false, kSplit, kVerifyItems, RT>;
 }
 
-template <int PLANES, int T>
-VerifyKernel pick_rt(int rt, bool grouped, bool exporting) {
-    switch (rt) {
-        case 4: return pick_mode<PLANES, T, 4>(grouped, exporting);
-        case 3: return pick_mode<PLANES, T, 3>(grouped, exporting);
-        case 2: return pick_mode<PLANES, T, 2>(grouped, exporting);
-        default: return pick_mode<PLANES, T, 1>(grouped, exporting);
+// Most 16-row tiles per workgroup without register spills: 8 for one token
+// tile, 6 for two (checked in the ISA: the 7- and 8-tile two-token-tile
+// instantiations spill).
+constexpr int max_row_tiles(int T) { return T == 1 ? 8 : 6; }
+
+template <int PLANES, int T, int RT>
+VerifyKernel pick_rt_from(int rt, bool grouped, bool exporting) {
+    if constexpr (RT > 1) {
+        if (rt >= RT) return pick_mode<PLANES, T, RT>(grouped, exporting);
+        return pick_rt_from<PLANES, T, RT - 1>(rt, grouped, exporting);
+    } else {
+        return pick_mode<PLANES, T, 1>(grouped, exporting);
     }
 }
 
-constexpr int kMaxRowTiles = 4;
+template <int PLANES, int T>
+VerifyKernel pick_rt(int rt, bool grouped, bool exporting) {
+    return pick_rt_from<PLANES, T, max_row_tiles(T)>(rt, grouped, exporting);
+}
+
+constexpr int kMaxTileRule = 4;   // the whole-tile rule's largest tile count (a power of two)
 
 // Rows per workgroup (R) and its 16-row tiles (RT). Where N spread over one
-// workgroup per compute unit gives at most kMaxRowTiles tiles, every CU gets
-// one workgroup of R = ceil(N / CUs) rows rounded up to 8 (N = 6144: 24 rows
-// on each of 256 CUs, where whole 16-row tiles would leave half of the CUs
-// with two tiles and half with one). Otherwise whole tiles, as many (up to
-// kMaxRowTiles, a power of two) as keep at least two workgroups per CU.
-void verify_rows(int N, int cus, int *R, int *RT) {
+// workgroup per compute unit needs at most max_row_tiles(T) tiles, every CU
+// gets one workgroup of R = ceil(N / CUs) rows rounded up to 8 (N = 6144: 24
+// rows on each of 256 CUs, where whole 16-row tiles would leave half of the
+// CUs with two tiles and half with one; N = 28672: 112 rows, where whole
+// tiles would take two rounds of residency). Otherwise whole tiles, as many
+// (up to kMaxTileRule) as keep at least two workgroups per CU.
+void verify_rows(int N, int T, int cus, int *R, int *RT) {
     const int even = ((N + cus - 1) / cus + 7) & ~7;
-    if (even <= kMaxRowTiles * kRowsPerBlock) {
+    if (even <= max_row_tiles(T) * kRowsPerBlock) {
         *R = even;
         *RT = (even + kRowsPerBlock - 1) / kRowsPerBlock;
         return;
     }
     const int tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
-    int rt = kMaxRowTiles;
+    int rt = kMaxTileRule;
     while (rt > 1 && (tiles + rt - 1) / rt < 2 * cus) rt >>= 1;
     *R = rt * kRowsPerBlock;
     *RT = rt;
@@ -341,7 +352,7 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
     int R = kRowsPerBlock, RT = 1;                     // the export is for checking: one tile
-    if (!export_partials) verify_rows(a.N, dev.cus, &R, &RT);
+    if (!export_partials) verify_rows(a.N, T, dev.cus, &R, &RT);
     VerifyKernel k;
     if (target)
         k = T == 1 ? pick_rt<2, 1>(RT, grouped, export_partials) : pick_rt<2, 2>(RT, grouped, export_partials);
