@@ -160,7 +160,8 @@ def test_batched_verify_several_row_tiles(M, N, act_group, target):
 # rows per workgroup on 256 CUs: 8 (tiles half empty), 24 with a ragged last
 # workgroup, 24 (the qkv shape), 40 (three tiles, the last with 8 rows), 64,
 # 80, 112 (the gate_up shape, seven tiles) and 120 (eight tiles); with 17-32
-# tokens the last three take whole tiles instead (at most six per workgroup)
+# tokens a workgroup holds at most 7 tiles (6 with grouped activation
+# scales), so 120 rows (and 112 with grouped scales) take whole tiles instead
 @pytest.mark.parametrize("N", [1000, 5001, 6144, 10000, 16000, 20000, 28672, 30000])
 @pytest.mark.parametrize("M", [8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])

@@ -291,45 +291,42 @@ typedef void (*VerifyKernel)(const LinearArgs, int);
 constexpr int kSplit = 8;     // waves per workgroup
 constexpr int kVerifyItems = 2;
 
-template <int PLANES, int T, int RT>
-VerifyKernel pick_mode(bool grouped, bool exporting) {
-    if (exporting) return verify_mfma_kernel<PLANES, T, false, true, kSplit, kVerifyItems, 1>;
-    return grouped ? verify_mfma_kernel<PLANES, T, true, false, kSplit, kVerifyItems, RT>
-                   : verify_mfma_kernel<PLANES, T, false, false, kSplit, kVerifyItems, RT>;
-}
+// Most 16-row tiles per workgroup without register spills (checked in the
+// ISA): 8 for one token tile; for two, 7 with per-token activation scales
+// and 6 with grouped ones (the 8-tile two-token-tile instantiations and the
+// grouped 7-tile one spill, so they are not instantiated).
+constexpr int max_row_tiles(int T, bool grouped) { return T == 1 ? 8 : (grouped ? 6 : 7); }
 
-// Most 16-row tiles per workgroup without register spills: 8 for one token
-// tile, 6 for two (checked in the ISA: the 7- and 8-tile two-token-tile
-// instantiations spill).
-constexpr int max_row_tiles(int T) { return T == 1 ? 8 : 6; }
-
-template <int PLANES, int T, int RT>
-VerifyKernel pick_rt_from(int rt, bool grouped, bool exporting) {
+// the largest instantiation with at most rt tiles, down from RT
+template <int PLANES, int T, bool GA, int RT>
+VerifyKernel pick_rt_from(int rt) {
     if constexpr (RT > 1) {
-        if (rt >= RT) return pick_mode<PLANES, T, RT>(grouped, exporting);
-        return pick_rt_from<PLANES, T, RT - 1>(rt, grouped, exporting);
+        if (rt >= RT) return verify_mfma_kernel<PLANES, T, GA, false, kSplit, kVerifyItems, RT>;
+        return pick_rt_from<PLANES, T, GA, RT - 1>(rt);
     } else {
-        return pick_mode<PLANES, T, 1>(grouped, exporting);
+        return verify_mfma_kernel<PLANES, T, GA, false, kSplit, kVerifyItems, 1>;
     }
 }
 
 template <int PLANES, int T>
 VerifyKernel pick_rt(int rt, bool grouped, bool exporting) {
-    return pick_rt_from<PLANES, T, max_row_tiles(T)>(rt, grouped, exporting);
+    if (exporting) return verify_mfma_kernel<PLANES, T, false, true, kSplit, kVerifyItems, 1>;
+    if (grouped) return pick_rt_from<PLANES, T, true, max_row_tiles(T, true)>(rt);
+    return pick_rt_from<PLANES, T, false, max_row_tiles(T, false)>(rt);
 }
 
 constexpr int kMaxTileRule = 4;   // the whole-tile rule's largest tile count (a power of two)
 
 // Rows per workgroup (R) and its 16-row tiles (RT). Where N spread over one
-// workgroup per compute unit needs at most max_row_tiles(T) tiles, every CU
+// workgroup per compute unit needs at most max_row_tiles tiles, every CU
 // gets one workgroup of R = ceil(N / CUs) rows rounded up to 8 (N = 6144: 24
 // rows on each of 256 CUs, where whole 16-row tiles would leave half of the
 // CUs with two tiles and half with one; N = 28672: 112 rows, where whole
 // tiles would take two rounds of residency). Otherwise whole tiles, as many
 // (up to kMaxTileRule) as keep at least two workgroups per CU.
-void verify_rows(int N, int T, int cus, int *R, int *RT) {
+void verify_rows(int N, int T, bool grouped, int cus, int *R, int *RT) {
     const int even = ((N + cus - 1) / cus + 7) & ~7;
-    if (even <= max_row_tiles(T) * kRowsPerBlock) {
+    if (even <= max_row_tiles(T, grouped) * kRowsPerBlock) {
         *R = even;
         *RT = (even + kRowsPerBlock - 1) / kRowsPerBlock;
         return;
@@ -352,7 +349,7 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
     int R = kRowsPerBlock, RT = 1;                     // the export is for checking: one tile
-    if (!export_partials) verify_rows(a.N, T, dev.cus, &R, &RT);
+    if (!export_partials) verify_rows(a.N, T, grouped, dev.cus, &R, &RT);
     VerifyKernel k;
     if (target)
         k = T == 1 ? pick_rt<2, 1>(RT, grouped, export_partials) : pick_rt<2, 2>(RT, grouped, export_partials);
