@@ -17,6 +17,14 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       measures, and writes the JSON that bench.py reads (traffic per launch of
       the round's linear kernel, with the hash of the kernel sources).
 
+  python bench_profile.py mfma DIR
+      DIR holds the output of
+        rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_VALU_MFMA_BUSY_CYCLES
+                  SQ_INSTS_VALU_MFMA_I8 GRBM_GUI_ACTIVE --output-format csv -d DIR -o run -- python -u bench.py ...
+      Prints, per batched-verify instantiation, the int8 matrix-core work per
+      dispatch and the share of the kernel's duration the matrix cores were
+      busy.
+
 Shapes are told apart by the round's fixed launch order: each draft pass
 launches qkv, o_proj, gate_up, down per layer, the verify pass a quantisation
 launch and a linear launch per linear, so every kernel instantiation sees its
@@ -189,6 +197,40 @@ def cmd_traffic(fetch_dir: str, write_dir: str, json_path: str | None, copy_mib:
         print("\nwrote %s" % json_path)
 
 
+# MI355X: 256 CUs x 4 SIMDs, each with its own matrix core; the engine clock
+# the busy share is taken against (the part's peak clock, so the share can
+# only be understated)
+SIMDS = 1024
+CLOCK_GHZ = 2.4
+
+
+def cmd_mfma(directory: str):
+    rows = [r for r in read_csv(directory, "counter_collection.csv") if "verify_mfma_kernel" in r["Kernel_Name"]]
+    if not rows:
+        sys.exit("no verify_mfma_kernel dispatches in %s" % directory)
+    per = {}
+    for r in rows:
+        d = per.setdefault((short(r["Kernel_Name"]), r["Dispatch_Id"]),
+                           {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                            "grid": int(r["Grid_Size"]) // int(r["Workgroup_Size"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), d in per.items():
+        by_kernel.setdefault(name, []).append(d)
+    print("| kernel | dispatches | workgroups | mean us | int8 MFMA ops per dispatch | MFMA instructions | "
+          "busy cycles per SIMD | busy share of the duration |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    for name in sorted(by_kernel):
+        ds = by_kernel[name]
+        n = len(ds)
+        mean = lambda key: sum(d[key] for d in ds) / n
+        dur = mean("dur_ns")
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / SIMDS
+        print("| %s | %d | %d | %.2f | %.4g | %.0f | %.0f | %.2f %% |" % (
+            name, n, ds[0]["grid"], dur / 1e3, mean("SQ_INSTS_VALU_MFMA_MOPS_I8") * 512,
+            mean("SQ_INSTS_VALU_MFMA_I8"), busy, 100.0 * busy / (dur * CLOCK_GHZ)))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -199,9 +241,13 @@ def main(argv=None):
     c.add_argument("write_dir")
     c.add_argument("--json", default=None)
     c.add_argument("--copy-mib", type=int, default=256)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         cmd_trace(a.dir)
+    elif a.cmd == "mfma":
+        cmd_mfma(a.dir)
     else:
         cmd_traffic(a.fetch_dir, a.write_dir, a.json, a.copy_mib)
 
