@@ -30,9 +30,10 @@
 // for o_proj; both factors are powers of two, so the draft and the target
 // round alike.
 //
-// Work split: a workgroup owns 16 weight rows; its 8 waves split the groups
-// of K into contiguous ranges (one read of every plane byte), and the
-// partial sums meet in LDS in a fixed order.
+// Work split: a workgroup owns R consecutive weight rows, held in 16-row
+// tiles (verify_rows picks R); its 8 waves split the groups of K into
+// contiguous ranges (one read of every plane byte), and the partial sums
+// meet in LDS in a fixed order.
 #include "bitnest_internal.h"
 #include "device_common.h"
 
