@@ -305,7 +305,27 @@ def _rows_sample(N, n=384):
     return idx
 
 
-@pytest.mark.parametrize("M,target", [(1, False), (1, True), (4, True), (8, True), (16, True), (32, True)])
+@pytest.mark.parametrize("N", [6144, 10000])     # 24 and 40 rows per workgroup on 256 CUs
+@pytest.mark.parametrize("M", [8, 32])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_batched_verify_tile_major_full_k(M, N, act_group, target):
+    # several row tiles per workgroup and K = 4096 (four groups per wave):
+    # the batched-verify kernel streams whole tiles, the wave's activations
+    # held in registers; sampled rows against the oracle
+    K = 4096
+    w, x = _problem(M, N, K, seed=5)
+    xq, xs, y = _run(w, x, act_group, target)
+    hi, lo, sc = w.numpy()
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    rows = _rows_sample(N)
+    y64 = oracle.linear(q, s, np.ascontiguousarray(hi[rows]), np.ascontiguousarray(sc[rows]),
+                        np.ascontiguousarray(lo[rows]) if target else None, act_group)
+    _check_y(y[:, torch.from_numpy(rows).cuda()], y64, "M=%d N=%d g=%d t=%s" % (M, N, act_group, target))
+
+
+@pytest.mark.parametrize("M,target", [(1, False), (1, True), (4, True), (8, False), (8, True), (16, True), (32, True)])
 def test_llama_layer_full_size(llama_layer, M, target):
     for li, (name, N, K, g, w, wd) in enumerate(llama_layer):
         x = synth.make_activations(M, K, seed=0, layer=0, linear=li)
