@@ -179,6 +179,25 @@ def test_batched_verify_rows_per_workgroup(M, N, act_group, target):
     _check_y(y, y64, "M=%d N=%d g=%d t=%s" % (M, N, act_group, target))
 
 
+# one 16-row tile per workgroup (at most 16 rows per CU on 256 CUs): the
+# row-contiguous order, 1 KiB chunks of each row staged through LDS. N = 4090
+# leaves 10 rows in the last workgroup, N = 2000 gives 8-row workgroups; K =
+# 6016 ends in a partial chunk (15 of 16 groups), K = 14336 has an odd number
+# of chunks
+@pytest.mark.parametrize("N,K", [(4090, 6016), (2000, 14336), (4096, 1152)])
+@pytest.mark.parametrize("M", [8, 17])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_batched_verify_row_contiguous(M, N, K, act_group, target):
+    w, x = _problem(M, N, K, seed=6)
+    xq, xs, y = _run(w, x, act_group, target)
+    hi, lo, sc = w.numpy()
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    assert np.array_equal(xq.cpu().numpy(), q)
+    y64 = oracle.linear(q, s, hi, sc, lo if target else None, act_group)
+    _check_y(y, y64, "M=%d N=%d K=%d g=%d t=%s" % (M, N, K, act_group, target))
+
+
 @pytest.mark.parametrize("M", [1, 4, 8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 def test_target_equals_draft_when_lo_is_8(M, act_group):

@@ -31,9 +31,11 @@
 // round alike.
 //
 // Work split: a workgroup owns R consecutive weight rows, held in 16-row
-// tiles (verify_rows picks R); its 8 waves split the groups of K into
-// contiguous ranges (one read of every plane byte), and the partial sums
-// meet in LDS in a fixed order.
+// tiles (verify_rows picks R); its 8 waves split the groups of K (one read
+// of every plane byte), and the partial sums meet in LDS in a fixed order.
+// With one tile per workgroup the plane bytes are read a row at a time and
+// staged through LDS (verify_rowload_kernel); with several, straight into
+// the operand registers (verify_mfma_kernel).
 #include "bitnest_internal.h"
 #include "device_common.h"
 
@@ -369,6 +371,213 @@ __global__ __launch_bounds__(64 * SPLIT) void verify_mfma_kernel(const LinearArg
     }
 }
 
+// Row-contiguous order for one 16-row tile per workgroup (N spread at most
+// 16 rows per CU, e.g. N = 4096). A B operand needs 16 rows per load, so the
+// kernel above reads a 64-byte slice of 16 rows per instruction; here every
+// plane load is 1 KiB of one row (a probe reading down_proj's planes: 5.9
+// TB/s in this order against 4.0 TB/s in slices), and the chunk of the tile
+// is turned into the matrix-core layout through LDS.
+//
+// Chunk c = plane bytes [c kChunk, (c + 1) kChunk) of the 16 rows (16
+// groups). Wave w loads rows 2w and 2w + 1 of each plane into registers,
+// kChunkLead chunks ahead, writes them to LDS buffer c % 2 and, after a
+// barrier, takes groups w and w + 8 of the chunk: B from LDS (the row pitch
+// puts the 16 rows of an operand in distinct banks), A from its own
+// activation loads, issued together with the chunk's plane loads so that
+// the in-order load counter never waits for a later chunk. The epilogue is
+// the kernel above's with one tile.
+constexpr int kChunk = 1024;                    // plane bytes per row per chunk
+constexpr int kChunkGroups = kChunk / 64;       // 16
+constexpr int kRowPitch = kChunk + 16;          // LDS bytes per row of a chunk
+constexpr int kChunkLead = 2;                   // chunks in flight (and LDS buffers)
+
+template <int PLANES>
+constexpr size_t chunk_lds_bytes() { return static_cast<size_t>(PLANES) * kRowsPerBlock * kRowPitch; }
+
+template <int PLANES, int T, bool GA>
+__global__ __launch_bounds__(64 * 8) void verify_rowload_kernel(const LinearArgs a, int R) {
+    constexpr int SPLIT = 8;
+    constexpr int NL = 2 * PLANES;                // plane loads per wave per chunk
+    static_assert(kChunkGroups == 2 * SPLIT, "two groups of a chunk per wave");
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char *lbuf = smem;                                             // [kChunkLead][PLANES][16][kRowPitch]
+    float *sact = reinterpret_cast<float *>(smem + kChunkLead * chunk_lds_bytes<PLANES>());   // [G][16 T] (GA)
+    float *red = reinterpret_cast<float *>(smem);                          // [SPLIT][T][4][64], after the stream
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = a.K, N = a.N, M = a.M;
+    const int G = K >> 7;
+    const int row_bytes = K >> 1;
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int row0 = blockIdx.x * R;
+    const int rows = N - row0 < R ? N - row0 : R;
+    const float fscale = PLANES == 2 ? 0.00390625f : 0.0625f;
+    const int nchunks = (row_bytes + kChunk - 1) / kChunk;
+
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hi + static_cast<size_t>(row0) * row_bytes,
+                                                static_cast<unsigned>(rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc((PLANES == 2 ? a.lo : a.hi) + static_cast<size_t>(row0) * row_bytes,
+                                                static_cast<unsigned>(rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scale + static_cast<size_t>(row0) * G,
+                                                static_cast<unsigned>(rows) * G * 2u);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, static_cast<unsigned>(M) * K);
+    const int voff_s = col * G * 2;
+    int voff_x[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) voff_x[t] = (16 * t + col) * K + kq * 32;
+
+    if (GA) {
+        for (int i = threadIdx.x; i < G * 16 * T; i += 64 * SPLIT) {
+            const int g = i / (16 * T);
+            const int t = i - g * 16 * T;
+            sact[i] = t < M ? a.xs[static_cast<size_t>(t) * G + g] : 0.0f;
+        }
+        // made visible by the first chunk's barrier
+    }
+
+    struct Chunk {
+        u32x4 p[NL];                 // load j: plane j / 2, row 2 wave + j % 2
+        u32x4 x[2][T][2];            // activation bytes of groups wave, wave + 8
+        uint16_t sbits[2];
+    };
+    auto issue = [&](Chunk &ck, int c) {
+        const bool live = c < nchunks;
+        // lanes past the row's end (a last, partial chunk) read nothing: an
+        // offset of at least kOOB is outside the descriptor (whose size is
+        // below 2^31), and the sums stay below 2^32
+        const int left = row_bytes - c * kChunk;
+        const unsigned lane_off = lane * 16 < left ? static_cast<unsigned>(lane * 16) : static_cast<unsigned>(kOOB);
+        const int sc = live ? c * kChunk : kOOB;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const unsigned vo = static_cast<unsigned>((2 * wave + (j & 1)) * row_bytes) + lane_off;
+            ck.p[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    (j >> 1) ? rl : rh, static_cast<int>(vo), sc, kAuxStream));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int g = c * kChunkGroups + wave + SPLIT * i;
+            const bool gl = live && g < G;
+            const int sx = gl ? g * kGroup : kOOB;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                ck.x[i][t][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[t], sx, 0));
+                ck.x[i][t][1] = __builtin_bit_cast(u32x4,
+                                                   __builtin_amdgcn_raw_buffer_load_b128(rx, voff_x[t] + 16, sx, 0));
+            }
+            ck.sbits[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_s, gl ? g * 2 : kOOB, 0);
+        }
+    };
+
+    float yacc[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[t][r] = 0.0f;
+
+    auto consume = [&](const Chunk &ck, int c, unsigned char *buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int gl = wave + SPLIT * i;
+            const int g = c * kChunkGroups + gl;
+            if (g >= G) continue;                          // uniform
+            const unsigned char *src = buf + col * kRowPitch + gl * 64 + kq * 16;
+            i32x4 bhe, bho, ble, blo;
+            signed16(*reinterpret_cast<const u32x4 *>(src), bhe, bho);
+            if (PLANES == 2) signed16(*reinterpret_cast<const u32x4 *>(src + kRowsPerBlock * kRowPitch), ble, blo);
+            const float sc = half_bits_to_float(ck.sbits[i]) * fscale;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                i32x4 ae, ao;
+                split_act(ck.x[i][t][0], ck.x[i][t][1], ae, ao);
+                float sa[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if (GA) {
+                    const float4 v = *reinterpret_cast<const float4 *>(sact + g * 16 * T + 16 * t + 4 * kq);
+                    sa[0] = v.x; sa[1] = v.y; sa[2] = v.z; sa[3] = v.w;
+                }
+                const i32x4 zero = {0, 0, 0, 0};
+                i32x4 dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, bhe, zero, 0, 0, 0);
+                dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao, bho, dh, 0, 0, 0);
+                i32x4 dl = zero;
+                if (PLANES == 2) {
+                    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, ble, zero, 0, 0, 0);
+                    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ao, blo, dl, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // draft: 16 P_hi; target: 16 (16 P_hi) + 16 P_lo = 16 P8
+                    const int pv = PLANES == 2 ? 16 * dh[r] + dl[r] : dh[r];
+                    const float w = GA ? sc * sa[r] : sc;
+                    yacc[t][r] += static_cast<float>(pv) * w;
+                }
+            }
+        }
+    };
+
+    // the chunks' loads are issued in chunk order (no scheduling across an
+    // issue), so waiting for one chunk never waits for a later one
+    Chunk ring[kChunkLead];
+#pragma unroll
+    for (int d = 0; d < kChunkLead; ++d) {
+        issue(ring[d], d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // every pass of the loop takes kChunkLead chunks with no early exit (a
+    // chunk past the end writes zeros, has no groups and loads nothing), so
+    // the load counter waits are the same on every path
+    for (int base = 0; base < nchunks; base += kChunkLead) {
+#pragma unroll
+        for (int d = 0; d < kChunkLead; ++d) {
+            const int c = base + d;
+            unsigned char *buf = lbuf + d * chunk_lds_bytes<PLANES>();
+            // buffer d was last read for chunk c - kChunkLead, before the
+            // previous chunk's barrier
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                *reinterpret_cast<u32x4 *>(buf + ((j >> 1) * kRowsPerBlock + 2 * wave + (j & 1)) * kRowPitch +
+                                           lane * 16) = ring[d].p[j];
+            __syncthreads();
+            consume(ring[d], c, buf);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(ring[d], c + kChunkLead);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    __syncthreads();                                       // the chunk buffers become the exchange
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[((wave * T + t) * 4 + r) * 64 + lane] = yacc[t][r];
+    __syncthreads();
+    if (wave == 0) {
+        float tok_scale[T][4];
+        if (!GA) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = 16 * t + 4 * kq + r;
+                    tok_scale[t][r] = tok < M ? a.xs[tok] : 0.0f;
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = red[((0 * T + t) * 4 + r) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < SPLIT; ++w) v += red[((w * T + t) * 4 + r) * 64 + lane];
+                const int tok = 16 * t + 4 * kq + r;
+                if (tok < M && col < rows)
+                    a.y[static_cast<size_t>(tok) * N + row0 + col] = GA ? v : v * tok_scale[t][r];
+            }
+        }
+    }
+}
+
 typedef void (*VerifyKernel)(const LinearArgs, int);
 
 constexpr int kSplit = 8;     // waves per workgroup
@@ -380,15 +589,15 @@ constexpr int kVerifyItems = 2;
 // grouped 7-tile one spill, so they are not instantiated).
 constexpr int max_row_tiles(int T, bool grouped) { return T == 1 ? 8 : (grouped ? 6 : 7); }
 
-// the largest instantiation with at most rt tiles, down from RT (one tile:
-// the two orders are the same, so the group-major one)
+// the largest instantiation with at most rt tiles, down from RT (rt >= 2:
+// one tile per workgroup takes verify_rowload_kernel)
 template <int PLANES, int T, bool GA, bool TM, int RT>
 VerifyKernel pick_rt_from(int rt) {
-    if constexpr (RT > 1) {
+    if constexpr (RT > 2) {
         if (rt >= RT) return verify_mfma_kernel<PLANES, T, GA, false, kSplit, kVerifyItems, RT, TM>;
         return pick_rt_from<PLANES, T, GA, TM, RT - 1>(rt);
     } else {
-        return verify_mfma_kernel<PLANES, T, GA, false, kSplit, kVerifyItems, 1, false>;
+        return verify_mfma_kernel<PLANES, T, GA, false, kSplit, kVerifyItems, 2, TM>;
     }
 }
 
@@ -402,6 +611,15 @@ template <int PLANES, int T>
 VerifyKernel pick_rt(int rt, bool grouped, bool exporting, bool tile_major) {
     if (exporting) return verify_mfma_kernel<PLANES, T, false, true, kSplit, kVerifyItems, 1, false>;
     return tile_major ? pick_rt_order<PLANES, T, true>(rt, grouped) : pick_rt_order<PLANES, T, false>(rt, grouped);
+}
+
+VerifyKernel pick_rowload(int planes, int T, bool grouped) {
+    if (planes == 2) {
+        if (T == 1) return grouped ? verify_rowload_kernel<2, 1, true> : verify_rowload_kernel<2, 1, false>;
+        return grouped ? verify_rowload_kernel<2, 2, true> : verify_rowload_kernel<2, 2, false>;
+    }
+    if (T == 1) return grouped ? verify_rowload_kernel<1, 1, true> : verify_rowload_kernel<1, 1, false>;
+    return grouped ? verify_rowload_kernel<1, 2, true> : verify_rowload_kernel<1, 2, false>;
 }
 
 constexpr int kMaxTileRule = 4;   // the whole-tile rule's largest tile count (a power of two)
@@ -443,15 +661,22 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
     // K range fits the registers it keeps the activations in
     const int G_ = a.K / kGroup;
     const bool tm = !export_partials && RT >= 2 && (G_ + kSplit - 1) / kSplit <= kTmGroups;
+    // one tile per workgroup: the row-contiguous order
+    const bool rowload = !export_partials && RT == 1;
     VerifyKernel k;
-    if (target)
+    if (rowload)
+        k = pick_rowload(target ? 2 : 1, T, grouped);
+    else if (target)
         k = T == 1 ? pick_rt<2, 1>(RT, grouped, export_partials, tm) : pick_rt<2, 2>(RT, grouped, export_partials, tm);
     else
         k = T == 1 ? pick_rt<1, 1>(RT, grouped, export_partials, tm) : pick_rt<1, 2>(RT, grouped, export_partials, tm);
-    // the partial-sum exchange [kSplit][RT][T][4][64] and the grouped
-    // activation-scale table [G][16 T]
+    // the partial-sum exchange [kSplit][RT][T][4][64] (for the row-contiguous
+    // kernel: the chunk buffers, which it reuses for the exchange) and the
+    // grouped activation-scale table [G][16 T]
     const size_t G = a.K / kGroup;
-    const size_t lds = static_cast<size_t>(kSplit) * RT * T * 4 * 64 * 4 + (grouped ? G * 16 * T * 4 : 0);
+    const size_t exchange = static_cast<size_t>(kSplit) * RT * T * 4 * 64 * 4;
+    const size_t stream_lds = rowload ? kChunkLead * (target ? chunk_lds_bytes<2>() : chunk_lds_bytes<1>()) : 0;
+    const size_t lds = (stream_lds > exchange ? stream_lds : exchange) + (grouped ? G * 16 * T * 4 : 0);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
     if (lds > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
