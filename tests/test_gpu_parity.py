@@ -147,7 +147,7 @@ def test_linear_matches_oracle(M, N, K, act_group, target):
 @pytest.mark.parametrize("target", [False, True])
 def test_batched_verify_several_row_tiles(M, N, act_group, target):
     # the batched-verify kernel gives a workgroup several 16-row tiles when N
-    # is large (shared activation loads); every row is checked
+    # is large (activation loads shared by the tiles); every row is checked
     w, x = _problem(M, N, 256, seed=3)
     xq, xs, y = _run(w, x, act_group, target)
     hi, lo, sc = w.numpy()
@@ -159,9 +159,8 @@ def test_batched_verify_several_row_tiles(M, N, act_group, target):
 
 # rows per workgroup on 256 CUs: 8 (tiles half empty), 24 with a ragged last
 # workgroup, 24 (the qkv shape), 40 (three tiles, the last with 8 rows), 64,
-# 80, 112 (the gate_up shape, seven tiles) and 120 (eight tiles); with 17-32
-# tokens a workgroup holds at most 7 tiles (6 with grouped activation
-# scales), so 120 rows (and 112 with grouped scales) take whole tiles instead
+# 80, 112 (the gate_up shape, seven tiles) and 120 (eight tiles, the most a
+# workgroup holds, with one or two token tiles)
 @pytest.mark.parametrize("N", [1000, 5001, 6144, 10000, 16000, 20000, 28672, 30000])
 @pytest.mark.parametrize("M", [8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
@@ -325,14 +324,15 @@ def _rows_sample(N, n=384):
 
 
 @pytest.mark.parametrize("N", [6144, 10000])     # 24 and 40 rows per workgroup on 256 CUs
+@pytest.mark.parametrize("K", [4096, 14336])     # 2 and 7 chunks of 16 groups
 @pytest.mark.parametrize("M", [8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 @pytest.mark.parametrize("target", [False, True])
-def test_batched_verify_tile_major_full_k(M, N, act_group, target):
-    # several row tiles per workgroup and K = 4096 (four groups per wave):
-    # the batched-verify kernel streams whole tiles, the wave's activations
-    # held in registers; sampled rows against the oracle
-    K = 4096
+def test_batched_verify_several_tiles_full_k(M, K, N, act_group, target):
+    # several row tiles per workgroup at full width: the batched-verify
+    # kernel takes each chunk of K for all its tiles in turn, the chunk's
+    # activations loaded once (an odd chunk count ends in an empty chunk);
+    # sampled rows against the oracle
     w, x = _problem(M, N, K, seed=5)
     xq, xs, y = _run(w, x, act_group, target)
     hi, lo, sc = w.numpy()
