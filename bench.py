@@ -457,17 +457,18 @@ def kv_timing(bn, layers=32, contexts=(2048, 8192, 32768), Hq=32, Hkv=8, reps=5)
     """Decode attention over the nested KV cache at the Llama-3-8B head layout
     (32 query heads, 8 KV heads, head dimension 128): the draft step (M=1,
     KV4: hi planes) and the verify pass (M=4, KV8: hi+lo planes), one call
-    per layer over `layers` distinct caches (cold) from a HIP graph. us per
-    call and GB/s of cache bytes read (planes + fp16 scales of K and V)."""
+    per layer over `layers` distinct caches (cold) from a HIP graph; each
+    cache is head-major, exactly T positions per head. us per call and GB/s
+    of cache bytes read (planes + fp16 scales of K and V)."""
     import torch
     out = {}
     g = torch.Generator(device="cuda").manual_seed(77)
     for T in contexts:
         caches = []
         for _ in range(layers):
-            planes = [torch.randint(0, 256, (T, Hkv, 64), dtype=torch.uint8, device="cuda", generator=g)
+            planes = [torch.randint(0, 256, (Hkv, T, 64), dtype=torch.uint8, device="cuda", generator=g)
                       for _ in range(4)]                 # k_hi, k_lo, v_hi, v_lo
-            scales = [(torch.rand((T, Hkv), device="cuda", generator=g) * 0.02 + 0.005).half().view(torch.int16)
+            scales = [(torch.rand((Hkv, T), device="cuda", generator=g) * 0.02 + 0.005).half().view(torch.int16)
                       for _ in range(2)]
             caches.append((planes, scales))
         res = {}

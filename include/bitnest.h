@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 3
+#define BITNEST_ABI_VERSION 4
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
@@ -255,10 +255,14 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  * long contexts). The layout and the scale granularity are in meta.json,
  * which the pages do not reproduce; this library's reading:
  *   - every (token t, KV head h) vector of K or V, 128 values, is packed like
- *     one 128-column group of a weight row: planes uint8 [T, Hkv, 64] (byte
- *     j: dimension 2j low nibble, 2j+1 high nibble) and one fp16 scale
- *     [T, Hkv]. Writing the cache is bitnest_pack_nested with N = T Hkv rows
- *     of K = 128 columns;
+ *     one 128-column group of a weight row (byte j: dimension 2j low nibble,
+ *     2j+1 high nibble) with one fp16 scale. The cache is head-major: planes
+ *     uint8 [Hkv, t_cap, 64] and scales [Hkv, t_cap], where t_cap >= T is
+ *     the number of positions allocated per head and positions t < T are
+ *     read, so a head's positions are contiguous bytes (the layout this
+ *     library's loads stream fastest). Writing positions [t0, t1) of head h
+ *     is bitnest_pack_nested with N = t1 - t0 rows of K = 128 columns at row
+ *     h t_cap + t0;
  *   - KV4 = (hi - 8) s, KV8 = (16 (hi - 8) + (lo - 8)) s / 16, the weight
  *     formulas;
  *   - the M query tokens are the last M positions of the sequence (the
@@ -272,8 +276,9 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  * |out - out_exact| stays within a few 1e-6 of the values' magnitude.
  *
  *   q        fp32 [M, Hq, 128]
- *   k_hi, v_hi  uint8 [T, Hkv, 64];  k_lo, v_lo  the same or both NULL (KV4)
- *   k_scale, v_scale  fp16 bit patterns [T, Hkv]
+ *   T        positions in the sequence; t_cap  positions per head in the cache
+ *   k_hi, v_hi  uint8 [Hkv, t_cap, 64];  k_lo, v_lo  the same or both NULL (KV4)
+ *   k_scale, v_scale  fp16 bit patterns [Hkv, t_cap]
  *   out      fp32 [M, Hq, 128], written
  *   work     caller-owned scratch of at least
  *            bitnest_kv_attention_workspace_bytes(M, Hq, T) bytes, overwritten
@@ -281,12 +286,12 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  *            row, 128 output values, the maximum and the sum; 0 for
  *            M, Hq or T below 1)
  * Limits: M >= 1, Hq a multiple of Hkv, M Hq / Hkv <= BITNEST_KV_MAX_ROWS,
- * M <= T, Hkv <= 65535, T Hkv 64 < 2^31; otherwise BITNEST_EINVAL /
+ * M <= T <= t_cap, Hkv <= 65535, T 64 < 2^31; otherwise BITNEST_EINVAL /
  * BITNEST_EUNSUPPORTED. q and the scales are finite.
  */
 size_t bitnest_kv_attention_workspace_bytes(int M, int Hq, int T);
 
-bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int T,
+bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int T, int t_cap,
                                     const uint8_t *k_hi, const uint8_t *k_lo, const uint16_t *k_scale,
                                     const uint8_t *v_hi, const uint8_t *v_lo, const uint16_t *v_scale,
                                     float *out, void *work, size_t work_bytes, void *stream);

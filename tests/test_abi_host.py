@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bn.bitnest_abi_version() == 3
+    assert bn.bitnest_abi_version() == 4
     seen = set()
     for s in range(5):
         txt = bn.bitnest_status_string(s)
@@ -82,8 +82,9 @@ def _p(xq, hi, lo, ph, pl, p8, M, N, K):
     return bn.lib().bitnest_linear_partials(xq, hi, lo, ph, pl, p8, M, N, K, None)
 
 
-def _kv(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb):
-    return bn.lib().bitnest_kv_attention(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb, None)
+def _kv(q, M, Hq, Hkv, T, kh, kl, ks, vh, vl, vs, out, w, wb, t_cap=None):
+    return bn.lib().bitnest_kv_attention(q, M, Hq, Hkv, T, T if t_cap is None else t_cap, kh, kl, ks, vh, vl, vs,
+                                         out, w, wb, None)
 
 
 _DEFAULT = object()
@@ -215,7 +216,10 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _kv(A, 4, 30, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 32, 8, 3, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 8, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EUNSUPPORTED),
-    (lambda: _kv(A, 1, 32, 8, 1 << 23, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
+    # T 64 = 2^31 bytes of one head: beyond the offset range
+    (lambda: _kv(A, 1, 32, 8, 1 << 25, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
+    # fewer positions allocated per head than the sequence holds
+    (lambda: _kv(A, 4, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20, 99), bn.EINVAL),
     (lambda: _kv(A, 1, 65536, 65536, 4, B, NUL, C, D, NUL, E, F, A, 1 << 40), bn.EUNSUPPORTED),
     # M * (Hq / Hkv) = 2^32: beyond the row limit (not wrapped to 0)
     (lambda: _kv(A, 1 << 20, 1 << 12, 1, 1 << 20, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EUNSUPPORTED),

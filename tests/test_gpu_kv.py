@@ -1,8 +1,9 @@
 """GPU parity of decode attention over the nested KV cache (draft KV4, target
 KV8) against the CPU oracle, through the C ABI.
 
-The caches are packed on the CPU by the oracle and uploaded, so every input
-of the oracle is its own. Bar: max|out - out_oracle| <= 1e-5 * max|V| over the
+The caches are packed on the CPU by the oracle (in its [T, Hkv] order) and
+uploaded in the library's head-major layout, so every input of the oracle is
+its own. Bar: max|out - out_oracle| <= 1e-5 * max|V| over the
 visible values (the oracle is fp64; the kernel accumulates in fp32 over
 splits of 64-position chunks with a running softmax, then merges the
 splits). Invariants checked bit for bit on the GPU: KV8 with lo
@@ -38,10 +39,26 @@ def _cache(T, Hkv, seed, spread=1.0):
     return out          # (K planes, V planes)
 
 
-def _run(q, kc, vc, kv8):
-    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    out = bn.bitnest_kv_attention(d(q), d(kc[0]), d(kc[2]).view(torch.int16), d(vc[0]), d(vc[2]).view(torch.int16),
-                                  d(kc[1]) if kv8 else None, d(vc[1]) if kv8 else None)
+def _head_major(a, t_cap, fill):
+    # [T, Hkv, ...] (the oracle's layout) -> the cache's [Hkv, t_cap, ...]:
+    # positions past T hold `fill`, which the kernel must not read
+    T = a.shape[0]
+    out = np.full((a.shape[1], t_cap) + a.shape[2:], fill, dtype=a.dtype)
+    out[:, :T] = np.swapaxes(a, 0, 1)
+    return out
+
+
+def _run(q, kc, vc, kv8, t_cap=None):
+    T = kc[0].shape[0]
+    t_cap = T if t_cap is None else t_cap
+    # past T: codes 0xFF and a huge scale (fp16 60000), so a read past the
+    # sequence would show
+    d = lambda a, fill: torch.from_numpy(np.ascontiguousarray(_head_major(a, t_cap, fill))).cuda()
+    big = np.uint16(0x7B53)
+    out = bn.bitnest_kv_attention(torch.from_numpy(np.ascontiguousarray(q)).cuda(),
+                                  d(kc[0], 0xFF), d(kc[2], big).view(torch.int16), d(vc[0], 0xFF),
+                                  d(vc[2], big).view(torch.int16),
+                                  d(kc[1], 0xFF) if kv8 else None, d(vc[1], 0xFF) if kv8 else None, T=T)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -72,6 +89,18 @@ def test_kv_attention_matches_oracle(M, Hq, Hkv, T, kv8):
     want = _ref(q, kc, vc, kv8)
     err = np.abs(got - want).max()
     assert err <= TOL * _vmax(vc, kv8), (err, _vmax(vc, kv8))
+
+
+@pytest.mark.parametrize("M,T,t_cap", [(1, 2048, 2049), (4, 1000, 4096), (4, 20001, 20480)])
+@pytest.mark.parametrize("kv8", [False, True])
+def test_kv_attention_reads_only_the_first_t_positions_of_each_head(M, T, t_cap, kv8):
+    # the cache holds t_cap positions per head; those past T are filled with
+    # codes and scales that would dominate the result if they were read
+    kc, vc = _cache(T, 8, seed=T + t_cap)
+    q = np.random.default_rng(T).standard_normal((M, 32, 128)).astype(np.float32)
+    got = _run(q, kc, vc, kv8, t_cap=t_cap)
+    want = _ref(q, kc, vc, kv8)
+    assert np.abs(got - want).max() <= TOL * _vmax(vc, kv8)
 
 
 def test_kv_peaked_scores():
@@ -109,12 +138,14 @@ def test_kv_token_rows_equal_one_token_calls_on_the_cut_cache(T):
 
 
 def test_kv_pack_writes_the_oracle_planes():
-    # the cache write path (bitnest_pack_nested over T Hkv vectors)
+    # the cache write path (bitnest_pack_nested over the Hkv T vectors of a
+    # head-major cache)
     rng = np.random.default_rng(11)
-    X = rng.standard_normal((33, 8, 128)).astype(np.float32)
+    X = rng.standard_normal((8, 33, 128)).astype(np.float32)
     hi, lo, sc = bn.kv_pack(torch.from_numpy(X).cuda())
     torch.cuda.synchronize()
-    h_r, l_r, s_r = oracle.pack_nested(X.reshape(33 * 8, 128))
-    assert np.array_equal(hi.cpu().numpy().reshape(33 * 8, 64), h_r)
-    assert np.array_equal(lo.cpu().numpy().reshape(33 * 8, 64), l_r)
-    assert np.array_equal(sc.cpu().numpy().view(np.uint16).reshape(33 * 8, 1), s_r)
+    h_r, l_r, s_r = oracle.pack_nested(X.reshape(8 * 33, 128))
+    assert hi.shape == (8, 33, 64) and sc.shape == (8, 33)
+    assert np.array_equal(hi.cpu().numpy().reshape(8 * 33, 64), h_r)
+    assert np.array_equal(lo.cpu().numpy().reshape(8 * 33, 64), l_r)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16).reshape(8 * 33, 1), s_r)

@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
         L.bitnest_greedy_accept_workspace_bytes.restype = ctypes.c_size_t
         L.bitnest_kv_attention_workspace_bytes.argtypes = [I, I, I]
         L.bitnest_kv_attention_workspace_bytes.restype = ctypes.c_size_t
-        L.bitnest_kv_attention.argtypes = [P, I, I, I, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.bitnest_kv_attention.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
@@ -363,14 +363,15 @@ KV_HEAD_DIM = 128
 
 
 def kv_pack(kv: torch.Tensor):
-    """fp32 K or V entries [T, Hkv, 128] -> nested cache planes (hi, lo uint8 [T, Hkv, 64],
-    scale int16 fp16 bits [T, Hkv]): bitnest_pack_nested over the T Hkv vectors."""
+    """fp32 K or V entries [Hkv, T, 128] (head-major) -> nested cache planes (hi, lo
+    uint8 [Hkv, T, 64], scale int16 fp16 bits [Hkv, T]): bitnest_pack_nested over
+    the Hkv T vectors."""
     _need(kv, "kv", torch.float32)
     if kv.dim() != 3 or kv.shape[2] != KV_HEAD_DIM:
-        raise ValueError("kv must be [T, Hkv, 128]")
-    T, Hkv, _ = kv.shape
-    hi, lo, sc = bitnest_pack_nested(kv.reshape(T * Hkv, KV_HEAD_DIM))
-    return hi.view(T, Hkv, KV_HEAD_DIM // 2), lo.view(T, Hkv, KV_HEAD_DIM // 2), sc.view(T, Hkv)
+        raise ValueError("kv must be [Hkv, T, 128]")
+    Hkv, T, _ = kv.shape
+    hi, lo, sc = bitnest_pack_nested(kv.reshape(Hkv * T, KV_HEAD_DIM))
+    return hi.view(Hkv, T, KV_HEAD_DIM // 2), lo.view(Hkv, T, KV_HEAD_DIM // 2), sc.view(Hkv, T)
 
 
 def bitnest_kv_attention_workspace_bytes(M: int, Hq: int, T: int) -> int:
@@ -379,22 +380,26 @@ def bitnest_kv_attention_workspace_bytes(M: int, Hq: int, T: int) -> int:
 
 def bitnest_kv_attention(q: torch.Tensor, k_hi: torch.Tensor, k_scale: torch.Tensor, v_hi: torch.Tensor,
                          v_scale: torch.Tensor, k_lo: torch.Tensor | None = None, v_lo: torch.Tensor | None = None,
-                         out: torch.Tensor | None = None, work: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode attention over the nested KV cache: q fp32 [M, Hq, 128]; planes uint8
-    [T, Hkv, 64]; scales [T, Hkv] (fp16 or their int16 bits); KV4 without the lo
-    planes, KV8 with them. Returns out fp32 [M, Hq, 128]."""
+                         out: torch.Tensor | None = None, work: torch.Tensor | None = None,
+                         T: int | None = None) -> torch.Tensor:
+    """Decode attention over the nested KV cache: q fp32 [M, Hq, 128]; head-major
+    planes uint8 [Hkv, t_cap, 64]; scales [Hkv, t_cap] (fp16 or their int16 bits);
+    the first T positions of each head are read (T defaults to t_cap); KV4
+    without the lo planes, KV8 with them. Returns out fp32 [M, Hq, 128]."""
     _need(q, "q", torch.float32)
     if q.dim() != 3 or q.shape[2] != KV_HEAD_DIM:
         raise ValueError("q must be [M, Hq, 128]")
     M, Hq, _ = q.shape
     _need(k_hi, "k_hi", torch.uint8)
     if k_hi.dim() != 3 or k_hi.shape[2] != KV_HEAD_DIM // 2:
-        raise ValueError("k_hi must be [T, Hkv, 64]")
-    T, Hkv, _ = k_hi.shape
+        raise ValueError("k_hi must be [Hkv, t_cap, 64]")
+    Hkv, t_cap, _ = k_hi.shape
+    if T is None:
+        T = t_cap
     k_scale, v_scale = _scale_tensor(k_scale), _scale_tensor(v_scale)
     _need(v_hi, "v_hi", torch.uint8, tuple(k_hi.shape))
-    _need(k_scale, "k_scale", torch.int16, (T, Hkv))
-    _need(v_scale, "v_scale", torch.int16, (T, Hkv))
+    _need(k_scale, "k_scale", torch.int16, (Hkv, t_cap))
+    _need(v_scale, "v_scale", torch.int16, (Hkv, t_cap))
     if (k_lo is None) != (v_lo is None):
         raise ValueError("give both lo planes or neither")
     if k_lo is not None:
@@ -407,8 +412,8 @@ def bitnest_kv_attention(q: torch.Tensor, k_hi: torch.Tensor, k_scale: torch.Ten
     if work is None:
         work = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
     _need(work, "work", work.dtype)
-    _call(lib().bitnest_kv_attention(_p(q), M, Hq, Hkv, T, _p(k_hi), _p(k_lo), _p(k_scale), _p(v_hi), _p(v_lo),
-                                     _p(v_scale), _p(out), _p(work), work.numel() * work.element_size(),
+    _call(lib().bitnest_kv_attention(_p(q), M, Hq, Hkv, T, t_cap, _p(k_hi), _p(k_lo), _p(k_scale), _p(v_hi),
+                                     _p(v_lo), _p(v_scale), _p(out), _p(work), work.numel() * work.element_size(),
                                      _stream(q)), "bitnest_kv_attention")
     return out
 

@@ -239,13 +239,13 @@ size_t bitnest_kv_attention_workspace_bytes(int M, int Hq, int T) {
     return bitnest::kv_attention_workspace_bytes(M, Hq, T);
 }
 
-bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int T, const uint8_t *k_hi,
+bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int T, int t_cap, const uint8_t *k_hi,
                                     const uint8_t *k_lo, const uint16_t *k_scale, const uint8_t *v_hi,
                                     const uint8_t *v_lo, const uint16_t *v_scale, float *out, void *work,
                                     size_t work_bytes, void *stream) {
-    if (M < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || T < M) return BITNEST_EINVAL;
+    if (M < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || T < M || t_cap < T) return BITNEST_EINVAL;
     if (static_cast<long long>(M) * (Hq / Hkv) > BITNEST_KV_MAX_ROWS || Hkv > 65535) return BITNEST_EUNSUPPORTED;
-    if (static_cast<long long>(T) * Hkv * (BITNEST_KV_HEAD_DIM / 2) > 0x7FFFFFFFLL) return BITNEST_EUNSUPPORTED;
+    if (static_cast<long long>(T) * (BITNEST_KV_HEAD_DIM / 2) > 0x7FFFFFFFLL) return BITNEST_EUNSUPPORTED;
     if (!q || !k_hi || !k_scale || !v_hi || !v_scale || !out || !work) return BITNEST_EINVAL;
     if ((k_lo == nullptr) != (v_lo == nullptr)) return BITNEST_EINVAL;
     if (work_bytes < bitnest::kv_attention_workspace_bytes(M, Hq, T)) return BITNEST_EINVAL;
@@ -253,7 +253,8 @@ bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int 
         !aligned16(out) || !aligned16(work) || (k_lo && (!aligned16(k_lo) || !aligned16(v_lo))))
         return BITNEST_EALIGN;
     bitnest::KvArgs a{q, k_hi, k_lo, k_scale, v_hi, v_lo, v_scale, out, static_cast<float *>(work),
-                      M, Hq, Hkv, T, static_cast<float>(1.0 / std::sqrt(static_cast<double>(BITNEST_KV_HEAD_DIM)))};
+                      M, Hq, Hkv, T, t_cap,
+                      static_cast<float>(1.0 / std::sqrt(static_cast<double>(BITNEST_KV_HEAD_DIM)))};
     return to_status(bitnest::launch_kv_attention(a, static_cast<hipStream_t>(stream)));
 }
 

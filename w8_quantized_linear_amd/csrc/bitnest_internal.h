@@ -74,13 +74,14 @@ constexpr int kKvChunk = 64;        // positions per chunk; a split (one partial
 constexpr int kKvMaxRows = 16;      // M x (Hq / Hkv) query rows per KV head
 struct KvArgs {
     const float *q;                 // [M, Hq, 128]
-    const uint8_t *k_hi, *k_lo;     // [T, Hkv, 64] (k_lo, v_lo null: KV4)
-    const uint16_t *k_scale;        // [T, Hkv]
+    const uint8_t *k_hi, *k_lo;     // [Hkv, t_cap, 64] (k_lo, v_lo null: KV4)
+    const uint16_t *k_scale;        // [Hkv, t_cap]
     const uint8_t *v_hi, *v_lo;
     const uint16_t *v_scale;
     float *out;                     // [M, Hq, 128]
     float *work;                    // kv_attention_workspace_bytes(M, Hq, T)
     int M, Hq, Hkv, T;
+    int t_cap;                      // positions per head in the cache, >= T
     float inv_sqrt_d;
 };
 size_t kv_attention_workspace_bytes(int M, int Hq, int T);

@@ -3,7 +3,8 @@
 // the target KV8; abstract: the progressive-precision design extends to the
 // KV cache for long contexts). The reading, written out in bitnest.h: every
 // (token, KV head) vector of 128 values is packed like one 128-column weight
-// group (planes [T, Hkv, 64], fp16 scales [T, Hkv]); KV4 = (hi - 8) s,
+// group, head-major (planes [Hkv, t_cap, 64], fp16 scales [Hkv, t_cap], the
+// first T positions of each head valid); KV4 = (hi - 8) s,
 // KV8 = (16 (hi - 8) + (lo - 8)) s / 16; grouped-query heads; the M query
 // tokens are the last M positions (token i sees t <= T - M + i).
 //
@@ -150,15 +151,20 @@ void kv_attn_split_kernel(const KvArgs a, int cps) {
 
     // step loads: this lane's K rows (position 16 u + c, bytes 16 g ..), its
     // V dwords (dword c of positions 16 u + 4 g + i) and the K / V scales of
-    // positions 16 u + c. The descriptors end at the split's last position:
-    // rows past it read zero and touch no memory (Hkv < 2^16 keeps every
-    // offset below 2^32).
-    const unsigned cache_bytes = static_cast<unsigned>(span1) * a.Hkv * (kD / 2);
-    const unsigned scale_bytes = static_cast<unsigned>(span1) * a.Hkv * 2;
-    const __amdgpu_buffer_rsrc_t rkh = rsrc(a.k_hi, cache_bytes), rvh = rsrc(a.v_hi, cache_bytes);
-    const __amdgpu_buffer_rsrc_t rkl = rsrc(KV8 ? a.k_lo : a.k_hi, cache_bytes);
-    const __amdgpu_buffer_rsrc_t rvl = rsrc(KV8 ? a.v_lo : a.v_hi, cache_bytes);
-    const __amdgpu_buffer_rsrc_t rks = rsrc(a.k_scale, scale_bytes), rvs = rsrc(a.v_scale, scale_bytes);
+    // positions 16 u + c, all within KV head h's run of positions (the cache
+    // is head-major, so a 16-position K load is 1 KiB of contiguous bytes).
+    // The descriptors end at the split's last position: rows past it read
+    // zero and touch no memory (T 64 < 2^31 keeps every offset below 2^32).
+    const size_t head_planes = static_cast<size_t>(h) * a.t_cap * (kD / 2);
+    const size_t head_scales = static_cast<size_t>(h) * a.t_cap;
+    const unsigned cache_bytes = static_cast<unsigned>(span1) * (kD / 2);
+    const unsigned scale_bytes = static_cast<unsigned>(span1) * 2;
+    const __amdgpu_buffer_rsrc_t rkh = rsrc(a.k_hi + head_planes, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rvh = rsrc(a.v_hi + head_planes, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rkl = rsrc((KV8 ? a.k_lo : a.k_hi) + head_planes, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rvl = rsrc((KV8 ? a.v_lo : a.v_hi) + head_planes, cache_bytes);
+    const __amdgpu_buffer_rsrc_t rks = rsrc(a.k_scale + head_scales, scale_bytes);
+    const __amdgpu_buffer_rsrc_t rvs = rsrc(a.v_scale + head_scales, scale_bytes);
     struct Stage {
         u32x4 kh[NT], kl[NT];
         unsigned vh[NP], vl[NP];
@@ -170,14 +176,14 @@ void kv_attn_split_kernel(const KvArgs a, int cps) {
     unsigned ok[NT], ov[NP], os[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-        ok[u] = (static_cast<unsigned>(pf + 16 * u + c) * a.Hkv + h) * (kD / 2) + 16 * g;
-        os[u] = (static_cast<unsigned>(pf + 16 * u + c) * a.Hkv + h) * 2;
+        ok[u] = static_cast<unsigned>(pf + 16 * u + c) * (kD / 2) + 16 * g;
+        os[u] = static_cast<unsigned>(pf + 16 * u + c) * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            ov[4 * u + i] = (static_cast<unsigned>(pf + 16 * u + 4 * g + i) * a.Hkv + h) * (kD / 2) + 4 * c;
+            ov[4 * u + i] = static_cast<unsigned>(pf + 16 * u + 4 * g + i) * (kD / 2) + 4 * c;
     }
-    const unsigned step_planes = static_cast<unsigned>(WSTEP) * a.Hkv * (kD / 2);
-    const unsigned step_scales = static_cast<unsigned>(WSTEP) * a.Hkv * 2;
+    constexpr unsigned step_planes = static_cast<unsigned>(WSTEP) * (kD / 2);
+    constexpr unsigned step_scales = static_cast<unsigned>(WSTEP) * 2;
     auto fetch = [&](Stage &st) {
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
