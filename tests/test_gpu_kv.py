@@ -149,3 +149,13 @@ def test_kv_pack_writes_the_oracle_planes():
     assert np.array_equal(hi.cpu().numpy().reshape(8 * 33, 64), h_r)
     assert np.array_equal(lo.cpu().numpy().reshape(8 * 33, 64), l_r)
     assert np.array_equal(sc.cpu().numpy().view(np.uint16).reshape(8 * 33, 1), s_r)
+
+
+def test_kv_sequence_longer_than_the_cache_is_rejected():
+    # T > t_cap: rejected on the host before any launch
+    kc, vc = _cache(64, 8, seed=12)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(_head_major(a, 64, 0))).cuda()
+    q = torch.zeros((1, 32, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(bn.BitnestError) as e:
+        bn.bitnest_kv_attention(q, d(kc[0]), d(kc[2]).view(torch.int16), d(vc[0]), d(vc[2]).view(torch.int16), T=65)
+    assert e.value.status == bn.EINVAL
