@@ -324,7 +324,7 @@ def _rows_sample(N, n=384):
 
 
 @pytest.mark.parametrize("N", [6144, 10000])     # 24 and 40 rows per workgroup on 256 CUs
-@pytest.mark.parametrize("K", [4096, 14336])     # 2 and 7 chunks of 16 groups
+@pytest.mark.parametrize("K", [4096, 6016, 14336])     # 2, 3 (the last partial) and 7 chunks of 16 groups
 @pytest.mark.parametrize("M", [8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 @pytest.mark.parametrize("target", [False, True])
