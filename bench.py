@@ -8,7 +8,8 @@ base model and the default draft length gamma = 3 of the BitNest-Llama-3-8B
 model card): three draft passes at M = 1 (hi plane only) and one target
 (verify) pass at M = gamma + 1 = 4 (hi and lo planes). Every linear is an
 activation quantisation followed by the nested linear, so one round is
-4 passes x 32 layers x 4 linears x 2 kernels = 1024 launches, replayed from
+4 passes x 32 layers x 4 linears: 640 launches (one fused launch per draft
+linear, a quantisation launch and the linear per verify linear), replayed from
 one HIP graph. Weights are seeded synthetic tensors in the layout and with
 the distributions of the weight package (generated on the GPU, 3.49 GB per
 plane, so the stream is far larger than the 256 MB Infinity Cache); they are

@@ -118,7 +118,14 @@ bitnest_status bitnest_linear_draft(const int8_t *xq, const float *xs, int act_g
  *   y[m, n]   = sum_g float(P8[m,n,g]) * (scale[n,g] / 16) * s_a
  * Arguments as for the draft, plus `lo` uint8 [N, K/2]. M <= 7 runs the
  * plane-streaming GEMV, M >= 8 the batched-verify int8 matrix-core kernel; the
- * results obey the same definition.
+ * results obey the same definition. How each kernel forms P8 (both exact):
+ *   M <= 7  one dot product per column for both planes, on the byte
+ *           16*(hi-8) + lo = w8 + 8 in [-128, 127] (the two nibble fields
+ *           carry into each other nowhere, so by linearity the dot product
+ *           is 16 P_hi + P_lo + 8 sum_k xq), then minus 8 * sum_k xq over the
+ *           group;
+ *   M >= 8  separate int8 matrix-core contractions of the hi and the lo
+ *           plane, combined as 16 P_hi + P_lo in int32.
  */
 bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_group,
                                      const uint8_t *hi, const uint8_t *lo,
@@ -297,8 +304,13 @@ bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int 
                                     float *out, void *work, size_t work_bytes, void *stream);
 
 /*
- * The integer partials of the draft and target calls above, from the same kernels' integer
- * loop (for checking; not a fast path).
+ * The integer partials of the draft and target calls above, for checking (not a
+ * fast path), from the same kernels and integer loops as those calls:
+ *   M <= 7  the GEMV's loop: P8 exactly as the target forms it (the merged
+ *           byte and the code-sum correction), P_hi from the draft's loop,
+ *           P_lo = P8 - 16 P_hi;
+ *   M >= 8  the matrix-core kernel's two contractions: P_hi and P_lo as
+ *           computed, P8 = 16 P_hi + P_lo as the target combines them.
  *   p_hi  int32 [M, N, K/128] <- P_hi (always written)
  *   p_lo  int32 [M, N, K/128] <- P_lo              (only if lo != NULL)
  *   p8    int32 [M, N, K/128] <- 16 * P_hi + P_lo  (only if lo != NULL)

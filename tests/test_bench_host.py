@@ -56,15 +56,22 @@ def test_algorithmic_bytes_per_launch():
 
 
 def test_traffic_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    # a profile recorded with the hash of the sources it was taken on: its
+    # traffic is reported while they are unchanged, and not after an edit
+    import hashlib
     src_json = os.path.join(ROOT, "profiles", "gemv_planes_round_traffic.json")
     with open(src_json) as f:
         prof = json.load(f)
+    h = hashlib.sha256()
     for rel in prof["sources"]:
         dst = tmp_path / rel
         dst.parent.mkdir(parents=True, exist_ok=True)
         shutil.copyfile(os.path.join(ROOT, rel), dst)
+        h.update(dst.read_bytes())
+    prof["sources_sha256"] = h.hexdigest()
     (tmp_path / "profiles").mkdir()
-    shutil.copyfile(src_json, tmp_path / "profiles" / "gemv_planes_round_traffic.json")
+    with open(tmp_path / "profiles" / "gemv_planes_round_traffic.json", "w") as f:
+        json.dump(prof, f)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic() == prof["traffic_bytes_per_launch"]
     changed = tmp_path / prof["sources"][0]

@@ -87,21 +87,35 @@ def test_fused_rotation_linear(M, N, K, block, target):
     assert err <= TOL * np.abs(y64).max()
 
 
-def test_full_size_down_proj_with_rotation():
-    # Llama-3-8B down_proj (4096 x 14336, 28 blocks of 512), one token and the
-    # verify batch; y checked on sampled rows against the oracle
+@pytest.mark.parametrize("target", [False, True])
+def test_full_size_down_proj_with_rotation(target):
+    # Llama-3-8B down_proj (4096 x 14336, 28 blocks of 512), one token (the
+    # fused launch a pass times, every row checked) and the verify batch
+    # (sampled rows); codes bit-exact, fused y bit-identical to the rotation
+    # call followed by the plain linear, y within the bar of the oracle
     N, K, block = 4096, 14336, 512
     w = synth.make_weights(N, K, seed=24, layer=0, linear=3)
-    rows = np.random.default_rng(0).choice(N, 48, replace=False)
     hi_n, lo_n, sc_n = w.numpy()
+    hi, lo, sc = w.hi.cuda(), w.lo.cuda(), w.scale.cuda()
     for M in (1, 4):
         x = synth.make_activations(M, K, seed=24, layer=0, linear=3, step=M)
-        y, fq, fs = bn.bitnest_hadamard_quant_linear_target(x.cuda(), block, w.hi.cuda(), w.lo.cuda(),
-                                                            w.scale.cuda())
+        xd = x.cuda()
+        xq, xs = bn.bitnest_hadamard_quant_act(xd, block)
+        if target:
+            y_ref = bn.bitnest_linear_target(xq, xs, hi, lo, sc)
+            y, fq, fs = bn.bitnest_hadamard_quant_linear_target(xd, block, hi, lo, sc)
+        else:
+            y_ref = bn.bitnest_linear_draft(xq, xs, hi, sc)
+            y, fq, fs = bn.bitnest_hadamard_quant_linear_draft(xd, block, hi, sc)
         torch.cuda.synchronize()
+        assert torch.equal(fq, xq) and torch.equal(fs.view(torch.int32), xs.view(torch.int32))
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
         q, s, _ = oracle.hadamard_quant_act(x.numpy(), block)
         assert np.array_equal(fq.cpu().numpy(), q)
-        y64 = oracle.linear(q, s, hi_n[rows], sc_n[rows], lo_n[rows], 0)
+        assert np.array_equal(_bits(fs.cpu().numpy()), _bits(s))
+        rows = np.arange(N) if M == 1 else np.sort(np.random.default_rng(0).choice(N, 48, replace=False))
+        y64 = oracle.linear(q, s, np.ascontiguousarray(hi_n[rows]), np.ascontiguousarray(sc_n[rows]),
+                            np.ascontiguousarray(lo_n[rows]) if target else None, 0)
         err = np.abs(y.double().cpu().numpy()[:, rows] - y64).max()
         assert err <= TOL * np.abs(y64).max()
 

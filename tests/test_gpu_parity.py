@@ -362,7 +362,7 @@ def test_llama_layer_full_size(llama_layer, M, target):
         y64 = oracle.linear(q_ref, s_ref, np.ascontiguousarray(hi[rows]), np.ascontiguousarray(sc[rows]),
                             np.ascontiguousarray(lo[rows]) if target else None, g)
         _check_y(y[:, torch.from_numpy(rows).cuda()], y64, "%s M=%d target=%s" % (name, M, target))
-        if M in (1, 8):
+        if M in (1, 4, 8):
             p = bn.bitnest_linear_partials(xq, wd.hi[:64].contiguous(), wd.lo[:64].contiguous())
             r = oracle.partials(q_ref, hi[:64], lo[:64])
             for a, b in zip(p, r):
@@ -398,6 +398,34 @@ def test_fused_quant_linear_equals_two_calls(M, N, K, act_group, target):
     assert np.array_equal(fq.cpu().numpy(), q)
     hi_n, lo_n, sc_n = w.numpy()
     _check_y(y, oracle.linear(q, s, hi_n, sc_n, lo_n if target else None, act_group), "fused")
+
+
+@pytest.mark.parametrize("target", [False, True])
+def test_fused_single_token_full_layer(llama_layer, target):
+    # The launch a draft pass times: quantisation and the linear in one launch
+    # (one workgroup per CU, several rows per wave) at the four Llama-3-8B
+    # shapes, o_proj with per-group activation scales. Codes, scales and y are
+    # bit-identical to the two-call path; every row of y is within the bar of
+    # the oracle.
+    for li, (name, N, K, g, w, wd) in enumerate(llama_layer):
+        x = synth.make_activations(1, K, seed=0, layer=1, linear=li)
+        xd = _dev(x)
+        xq, xs = bn.bitnest_quant_act(xd, g)
+        if target:
+            y_ref = bn.bitnest_linear_target(xq, xs, wd.hi, wd.lo, wd.scale, g)
+            y, fq, fs = bn.bitnest_quant_linear_target(xd, wd.hi, wd.lo, wd.scale, g)
+        else:
+            y_ref = bn.bitnest_linear_draft(xq, xs, wd.hi, wd.scale, g)
+            y, fq, fs = bn.bitnest_quant_linear_draft(xd, wd.hi, wd.scale, g)
+        torch.cuda.synchronize()
+        assert torch.equal(fq, xq), name
+        assert torch.equal(fs.view(torch.int32), xs.view(torch.int32)), name
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32)), name
+        q, s = oracle.quant_act(x.numpy(), g)
+        assert np.array_equal(fq.cpu().numpy(), q), name
+        assert np.array_equal(fs.cpu().numpy(), s), name
+        hi, lo, sc = w.numpy()
+        _check_y(y, oracle.linear(q, s, hi, sc, lo if target else None, g), "%s fused t=%s" % (name, target))
 
 
 def test_fused_quant_linear_with_no_rows_still_quantises():

@@ -10,23 +10,30 @@
 // nibble) and 2j+1 (high nibble)); scales fp16 [N, K/128]; codes int8 [M, K].
 //
 // Work split. The kernel is bound by HBM: every plane byte is read once.
-//  - A wave owns whole weight rows (grid-stride over rows). Lane l reads the
-//    16-byte slot l of each 1 KiB chunk of the row with one 128-bit
-//    non-temporal load, so one wave instruction moves 1 KiB, fully coalesced.
-//    All chunks of a row (and both planes for the target) are issued before
-//    any arithmetic, to keep enough bytes in flight.
+//  - A wave owns a contiguous run of whole weight rows. Lane l reads the
+//    16-byte slot l of each 1 KiB chunk of a row with one 128-bit
+//    non-temporal buffer load, so one wave instruction moves 1 KiB, fully
+//    coalesced. The wave streams its (row, chunk) items through a ring of D
+//    items in flight (both planes of an item for the target).
 //  - A 16-byte slot holds 32 columns, a quarter of a 128-column group, so the
 //    four lanes of a quad hold one group.
 //  - The workgroup first copies the int8 codes of all M tokens into LDS,
 //    permuted so that each activation dword lines up with the even or the odd
 //    nibbles of a weight dword; the tile is shared by the M tokens' rows and
 //    by both planes.
-//  - Per slot: even nibbles = w & 0x0F0F0F0F, odd nibbles = (w >> 4) &
-//    0x0F0F0F0F (unsigned 0..15), two v_dot4_i32_i8 per weight dword per
-//    token. The sign shift (u - 8) is applied per group as - 8 * sum(q) for
-//    the draft and - 136 * sum(q) for the target's 16 hi + lo, with the
-//    per-(group, token) code sums precomputed in LDS. The 8-bit code
-//    16 (hi - 8) + (lo - 8) in [-136, 119] is never formed as an int8.
+//  - Draft, per 16-byte slot: each nibble u becomes the signed byte
+//    16 (u - 8) (xor 0x8, then placed in the high half of a byte), the even
+//    and the odd columns of a weight dword in separate dwords, and two
+//    v_dot4_i32_i8 per weight dword per token give 16 P_hi exactly.
+//  - Target: both planes are combined inside the dot product. The byte
+//    16 (hi - 8) + lo (hi xor 8 in the high half, the unsigned lo nibble in
+//    the low half; no carry between the two fields) is w8 + 8 in [-128, 127],
+//    so by linearity one dot4 per dword gives 16 P_hi + P_lo + 8 sum(q) =
+//    P8 + 8 sum(q), and the per-(group, token) code sums staged in LDS remove
+//    the 8 sum(q). The 8-bit code w8 = 16 (hi - 8) + (lo - 8) in [-136, 119]
+//    itself is never formed as an int8. The partials export runs this same
+//    loop: it writes P8 as computed here, P_hi from the draft's loop and
+//    P_lo = P8 - 16 P_hi.
 //  - A 2-step DPP quad sum gives the exact int32 group partial, converted
 //    once to fp32 and scaled by the group's weight scale (and, for o_proj,
 //    the group's activation scale). A 4-step reduction over the 16 quads
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // draft: (16 P_hi) * scale / 16; target: P8 * scale / 16
     const float fscale = 0.0625f;
-    constexpr bool kSums = PLANES == 2 && !EXPORT;   // the target's code sums
+    constexpr bool kSums = PLANES == 2;   // the target's code sums (also when exporting)
 
     const unsigned plane_bytes = static_cast<unsigned>(N) * static_cast<unsigned>(row_bytes);
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hi, plane_bytes);
@@ -443,46 +450,52 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
         const int ss = valid ? s : 0;
         const int g = ss >> 2;
         const float sc = half_bits_to_float(static_cast<uint16_t>(x.sbits)) * fscale;
-        if (EXPORT) {
-            // the planes' partials separately
-            const Signed16 nh = to_signed16(x.h);
-            Signed16 nl;
-            if (PLANES == 2) nl = to_signed16(x.l);
+        if constexpr (PLANES == 2) {
+            // target: P8 = sum q (16 (hi - 8) + lo) - 8 sum q, one dot product
+            // per dword for both planes (the merged byte of to_combined16)
+            const Signed16 n = to_combined16(x.h, x.l);
+            int cs[kMP];
+#pragma unroll
+            for (int i = 0; i < kMP; i += 4) {
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(qsum + g * kMP + i);
+                cs[i] = v.x; cs[i + 1] = v.y; cs[i + 2] = v.z; cs[i + 3] = v.w;
+            }
+            Signed16 nh;
+            if (EXPORT) nh = to_signed16(x.h);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const u32x4 a0 = act4[m * tok4 + ss];
                 const u32x4 a1 = act4[m * tok4 + half4 + ss];
-                const int ph = quad_sum_i32(dot_slot16(nh, a0, a1)) >> 4;
-                int pl = 0;
-                if (PLANES == 2) pl = quad_sum_i32(dot_slot16(nl, a0, a1)) >> 4;
-                if (valid && (lane & 3) == 0) {
-                    const size_t o = (static_cast<size_t>(m) * N + row) * G + g;
-                    a.p_hi[o] = ph;
-                    if (PLANES == 2) {
-                        a.p_lo[o] = pl;
-                        a.p8[o] = 16 * ph + pl;
+                const int p8 = quad_sum_i32(dot_slot16(n, a0, a1)) - 8 * cs[m];
+                if (EXPORT) {
+                    // the production P8 as computed above; P_hi from the
+                    // draft's loop; P_lo the rest of P8
+                    const int ph = quad_sum_i32(dot_slot16(nh, a0, a1)) >> 4;
+                    if (valid && (lane & 3) == 0) {
+                        const size_t o = (static_cast<size_t>(m) * N + row) * G + g;
+                        a.p_hi[o] = ph;
+                        a.p8[o] = p8;
+                        a.p_lo[o] = p8 - 16 * ph;
                     }
+                } else {
+                    const float w = GA ? sc * sact[g * kMP + m] : sc;
+                    acc[m] += valid ? static_cast<float>(p8) * w : 0.0f;
                 }
             }
         } else {
-            // draft: 16 P_hi; target: P8 = sum q (16 (hi - 8) + lo) - 8 sum q
-            const Signed16 n = PLANES == 2 ? to_combined16(x.h, x.l) : to_signed16(x.h);
-            int cs[kMP];
-            if (PLANES == 2) {
-#pragma unroll
-                for (int i = 0; i < kMP; i += 4) {
-                    const i32x4 v = *reinterpret_cast<const i32x4 *>(qsum + g * kMP + i);
-                    cs[i] = v.x; cs[i + 1] = v.y; cs[i + 2] = v.z; cs[i + 3] = v.w;
-                }
-            }
+            // draft: 16 P_hi
+            const Signed16 n = to_signed16(x.h);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const u32x4 a0 = act4[m * tok4 + ss];
                 const u32x4 a1 = act4[m * tok4 + half4 + ss];
-                int p = quad_sum_i32(dot_slot16(n, a0, a1));
-                if (PLANES == 2) p -= 8 * cs[m];
-                const float w = GA ? sc * sact[g * kMP + m] : sc;
-                acc[m] += valid ? static_cast<float>(p) * w : 0.0f;
+                const int p = quad_sum_i32(dot_slot16(n, a0, a1));
+                if (EXPORT) {
+                    if (valid && (lane & 3) == 0) a.p_hi[(static_cast<size_t>(m) * N + row) * G + g] = p >> 4;
+                } else {
+                    const float w = GA ? sc * sact[g * kMP + m] : sc;
+                    acc[m] += valid ? static_cast<float>(p) * w : 0.0f;
+                }
             }
         }
         if (++cchunk == C) {                     // row complete (uniform)
@@ -600,7 +613,7 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
     const int waves = fused ? kFusedWaves : kGemvWaves;
-    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused, waves, target && !exporting);
+    const size_t lds = gemv_lds_bytes(a.M, a.K, grouped, fused, waves, target);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
     if (lds > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
