@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 4
+#define BITNEST_ABI_VERSION 5
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
@@ -254,6 +254,24 @@ size_t bitnest_greedy_accept_workspace_bytes(int R, int V);
 bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft,
                                      int32_t *targ, int32_t *result, void *work, size_t work_bytes,
                                      void *stream);
+
+/*
+ * bitnest_greedy_accept without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The per-slice partials go to a scratch
+ * array the library holds in each device's memory for the life of the
+ * process (BITNEST_ACCEPT_NOALLOC_SCRATCH_BYTES, enough for every R <=
+ * BITNEST_MAX_M and any V). The call allocates and frees nothing. Results are
+ * those of bitnest_greedy_accept, bit for bit. All calls on one device share
+ * that device's scratch: calls that may overlap on one device (different
+ * streams without ordering between them) race and must not be made; calls
+ * in one stream's order are safe. Arguments and errors as for
+ * bitnest_greedy_accept, without `work` / `work_bytes`; a size beyond the
+ * scratch (R > BITNEST_MAX_M) gives BITNEST_EUNSUPPORTED.
+ */
+#define BITNEST_ACCEPT_NOALLOC_SCRATCH_BYTES 16384
+bitnest_status bitnest_greedy_accept_noalloc(const float *logits, int R, int V, const int32_t *draft,
+                                             int32_t *targ, int32_t *result, void *stream);
 
 /*
  * Decode attention over the nested KV cache (model card, recipe table row

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
               "bitnest_quant_linear_draft", "bitnest_quant_linear_target", "bitnest_hadamard_quant_act",
               "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
               "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_kv_attention",
-              "bitnest_kv_attention_workspace_bytes", "bitnest_greedy_accept_workspace_bytes"):
+              "bitnest_kv_attention_workspace_bytes", "bitnest_greedy_accept_workspace_bytes",
+              "bitnest_greedy_accept_noalloc"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bn.bitnest_abi_version() == 4
+    assert bn.bitnest_abi_version() == 5
     seen = set()
     for s in range(5):
         txt = bn.bitnest_status_string(s)
@@ -92,6 +93,10 @@ _DEFAULT = object()
 
 def _ga(lg, R, V, dr, tg, res, w=_DEFAULT, wb=1 << 20):
     return bn.lib().bitnest_greedy_accept(lg, R, V, dr, tg, res, A if w is _DEFAULT else w, wb, None)
+
+
+def _gn(lg, R, V, dr, tg, res):
+    return bn.lib().bitnest_greedy_accept_noalloc(lg, R, V, dr, tg, res, None)
 
 
 def _pk(W, N, K, hi, lo, sc):
@@ -211,6 +216,16 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _ga(A, 4, 100, B, C, D, NUL), bn.EINVAL),
     (lambda: _ga(A, 4, 100, B, C, D, A, 31), bn.EINVAL),
     (lambda: _ga(A, 4, 100, B, C, D, MIS), bn.EALIGN),
+    # greedy verification without a workspace (the library's scratch)
+    (lambda: _gn(A, 0, 100, B, C, D), bn.EINVAL),
+    (lambda: _gn(A, 4, 0, B, C, D), bn.EINVAL),
+    (lambda: _gn(A, 33, 100, B, C, D), bn.EUNSUPPORTED),
+    (lambda: _gn(NUL, 4, 100, B, C, D), bn.EINVAL),
+    (lambda: _gn(A, 4, 100, NUL, C, D), bn.EINVAL),
+    (lambda: _gn(A, 4, 100, B, NUL, D), bn.EINVAL),
+    (lambda: _gn(A, 4, 100, B, C, NUL), bn.EINVAL),
+    (lambda: _gn(MIS, 4, 100, B, C, D), bn.EALIGN),
+    (lambda: _gn(A, 4, 100, B, C, MIS), bn.EALIGN),
     # nested KV attention: every case fails validation (none may launch)
     (lambda: _kv(A, 0, 32, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),
     (lambda: _kv(A, 4, 30, 8, 100, B, NUL, C, D, NUL, E, F, A, 1 << 20), bn.EINVAL),

@@ -21,7 +21,8 @@ __all__ = [
     "bitnest_linear_draft", "bitnest_linear_target", "bitnest_linear_partials",
     "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
     "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
-    "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_greedy_accept_workspace_bytes", "bitnest_kv_attention",
+    "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_greedy_accept_workspace_bytes",
+    "bitnest_greedy_accept_noalloc", "bitnest_kv_attention",
     "bitnest_kv_attention_workspace_bytes", "kv_pack",
 ]
 
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.bitnest_hadamard_quant_linear_target.argtypes = [P, I, P, P, P, P, P, P, I, I, I, P]
         L.bitnest_pack_nested.argtypes = [P, I, I, P, P, P, P]
         L.bitnest_greedy_accept.argtypes = [P, I, I, P, P, P, P, ctypes.c_size_t, P]
+        L.bitnest_greedy_accept_noalloc.argtypes = [P, I, I, P, P, P, P]
         L.bitnest_greedy_accept_workspace_bytes.argtypes = [I, I]
         L.bitnest_greedy_accept_workspace_bytes.restype = ctypes.c_size_t
         L.bitnest_kv_attention_workspace_bytes.argtypes = [I, I, I]
@@ -78,7 +80,7 @@ def lib() -> ctypes.CDLL:
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
                   "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested", "bitnest_greedy_accept",
-                  "bitnest_kv_attention"):
+                  "bitnest_greedy_accept_noalloc", "bitnest_kv_attention"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -356,6 +358,28 @@ def bitnest_greedy_accept(logits: torch.Tensor, draft: torch.Tensor, targ: torch
     _call(lib().bitnest_greedy_accept(_p(logits), R, V, _p(draft) if R > 1 else None, _p(targ), _p(result),
                                       _p(work), work.numel() * work.element_size(), _stream(logits)),
           "bitnest_greedy_accept")
+    return targ, result
+
+
+def bitnest_greedy_accept_noalloc(logits: torch.Tensor, draft: torch.Tensor, targ: torch.Tensor | None = None,
+                                  result: torch.Tensor | None = None):
+    """bitnest_greedy_accept with the library's per-device scratch instead of
+    a workspace: allocates nothing on the device when ``targ`` and ``result``
+    are given. Calls that overlap on one device race on that scratch."""
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = logits.shape
+    _need(draft, "draft", torch.int32, (R - 1,))
+    if targ is None:
+        targ = torch.empty((R,), dtype=torch.int32, device=logits.device)
+    if result is None:
+        result = torch.empty((2,), dtype=torch.int32, device=logits.device)
+    _need(targ, "targ", torch.int32, (R,))
+    _need(result, "result", torch.int32, (2,))
+    _call(lib().bitnest_greedy_accept_noalloc(_p(logits), R, V, _p(draft) if R > 1 else None, _p(targ),
+                                              _p(result), _stream(logits)),
+          "bitnest_greedy_accept_noalloc")
     return targ, result
 
 

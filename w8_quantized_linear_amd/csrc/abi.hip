@@ -234,6 +234,18 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
                                                    static_cast<hipStream_t>(stream)));
 }
 
+bitnest_status bitnest_greedy_accept_noalloc(const float *logits, int R, int V, const int32_t *draft,
+                                             int32_t *targ, int32_t *result, void *stream) {
+    if (R < 1 || V < 1) return BITNEST_EINVAL;
+    if (R > BITNEST_MAX_M) return BITNEST_EUNSUPPORTED;
+    if (bitnest::accept_workspace_bytes(R, V) > BITNEST_ACCEPT_NOALLOC_SCRATCH_BYTES) return BITNEST_EUNSUPPORTED;
+    if (!logits || !targ || !result || (R > 1 && !draft)) return BITNEST_EINVAL;
+    if (!aligned16(logits) || !aligned16(targ) || !aligned16(result) || (draft && !aligned16(draft)))
+        return BITNEST_EALIGN;
+    return to_status(bitnest::launch_greedy_accept_noalloc(logits, R, V, draft, targ, result,
+                                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t bitnest_kv_attention_workspace_bytes(int M, int Hq, int T) {
     if (M < 1 || Hq < 1 || T < 1) return 0;
     return bitnest::kv_attention_workspace_bytes(M, Hq, T);

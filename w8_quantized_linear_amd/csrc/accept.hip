@@ -13,8 +13,11 @@
 // tokens. The pair order
 // (larger value, then smaller index) makes every result independent of the
 // order of the reductions.
+#include "bitnest.h"
 #include "bitnest_internal.h"
 #include "device_common.h"
+
+#include <atomic>
 
 namespace bitnest {
 namespace {
@@ -137,6 +140,35 @@ __global__ __launch_bounds__(64 * kAcceptWaves) void accept_kernel(int R, int S,
     }
 }
 
+// Scratch of the entry point that allocates nothing: the per-slice pairs of
+// the largest call (kMaxM rows x kMaxSlices slices). Each GPU the library
+// runs on holds its own copy until the process ends. Host code uses the
+// device address from hipGetSymbolAddress, never this name.
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(kMaxM) * kMaxSlices * sizeof(uint2);   // 16 KiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes == BITNEST_ACCEPT_NOALLOC_SCRATCH_BYTES, "the size the header states");
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current) and kept.
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 size_t accept_workspace_bytes(int R, int V) {
@@ -157,6 +189,19 @@ hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t
     const int waves = R < kAcceptWaves ? R : kAcceptWaves;
     hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64 * waves), 0, stream, R, S, part, draft, targ, result);
     return hipGetLastError();
+}
+
+size_t accept_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t launch_greedy_accept_noalloc(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
+                                        int32_t *result, hipStream_t stream) {
+    if (accept_workspace_bytes(R, V) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+    void *work = nullptr;
+    const hipError_t e = scratch_address(&work);
+    if (e != hipSuccess) return e;
+    // every pair the second launch reads is written by the first: nothing
+    // of the scratch needs clearing
+    return launch_greedy_accept(logits, R, V, draft, targ, result, work, stream);
 }
 
 }  // namespace bitnest

@@ -67,6 +67,12 @@ hipError_t launch_pack_nested(const float *W, int N, int K, uint8_t *hi, uint8_t
 size_t accept_workspace_bytes(int R, int V);
 hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
                                 int32_t *result, void *work, hipStream_t stream);
+// The same with the library's own per-device scratch (a static device array
+// of accept_noalloc_scratch_bytes(), enough for R <= kMaxM and any V): no
+// allocation; calls that overlap on one device race on it.
+size_t accept_noalloc_scratch_bytes();
+hipError_t launch_greedy_accept_noalloc(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
+                                        int32_t *result, hipStream_t stream);
 
 // Decode attention over the nested KV cache.
 constexpr int kKvHeadDim = 128;
