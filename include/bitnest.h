@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 5
+#define BITNEST_ABI_VERSION 6
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
@@ -203,6 +203,80 @@ bitnest_status bitnest_hadamard_quant_linear_target(const float *x, int block,
                                                     const uint16_t *scale,
                                                     float *y, int8_t *xq, float *xs,
                                                     int M, int N, int K, void *stream);
+
+/*
+ * A chain of linears in one launch (model card introduction: the draft runs
+ * the model's linears on the high-nibble plane for each of the gamma = 3
+ * draft tokens, then the target runs them on both planes over the gamma + 1
+ * verify tokens; each of these passes is a sequence of linears in which
+ * every input is produced after the previous linear's output).
+ *
+ * bitnest_linear_chain runs links[0], links[1], ..., links[count - 1] in
+ * that order, each the call bitnest_quant_linear_draft (a draft chain: `lo`
+ * NULL in every link with N > 0) or bitnest_quant_linear_target (a target
+ * chain: no such `lo` NULL) on its own tensors, M tokens each, with the same
+ * results bit for bit (codes, activation scales, y).
+ * Ordering: everything link j reads from `x` is read after every output of
+ * links 0 .. j-1 is written, so a link's input may be an earlier link's
+ * output (or be written by nothing in the chain); outputs of one link must
+ * not overlap its own inputs, and no output may overlap any link's planes or
+ * scales (weights are read ahead of the ordering: they are constant for the
+ * whole call).
+ *
+ * One launch instead of count: a persistent grid (one workgroup per compute
+ * unit, every workgroup resident at once) streams the planes of all links
+ * and waits on a device-scope counter in `work` between links. Each wait is
+ * bounded: after `max_polls` polls (0 selects BITNEST_CHAIN_DEFAULT_POLLS,
+ * about a second) the workgroup stops waiting, sets the time-out word, and
+ * the kernel runs to its end; the results of that call are then not
+ * defined. A wait runs out only when the grid cannot be resident at once
+ * (e.g. other kernels holding compute units for that long).
+ *
+ *   links      HOST array of `count` links, validated before anything is
+ *              launched (the fields below; BITNEST_EINVAL /
+ *              BITNEST_EALIGN / BITNEST_EUNSUPPORTED as for the single calls)
+ *   links_dev  DEVICE copy of the same array (same bytes), 16-byte aligned;
+ *              the kernel reads the links from it
+ *   count      0 <= count <= BITNEST_CHAIN_MAX_LINEARS (0: nothing is done)
+ *   M          1 <= M <= BITNEST_CHAIN_MAX_M tokens, the same for every link
+ *   work       caller-owned device workspace of at least
+ *              BITNEST_CHAIN_WORKSPACE_BYTES, 16-byte aligned, ZERO-FILLED
+ *              before its first use; a call leaves word 0 (uint32 arrival
+ *              counter) at zero again; word 1 (uint32) becomes nonzero,
+ *              and stays so, when a wait of some call ran out. Calls that may
+ *              overlap in time must not share a workspace.
+ * Per link: x fp32 [M, K]; hi, lo uint8 [N, K/2]; scale fp16 bits
+ * [N, K/128]; y fp32 [M, N]; xq int8 [M, K] and xs fp32 [M] (act_group 0)
+ * or [M, K/128] (act_group 128): both written, or both NULL and not
+ * written; 128 <= K <= BITNEST_MAX_K, K % 128 == 0; N >= 0 (N == 0: only
+ * the quantisation); act_group 0 or 128; rot_block must be 0 (reserved).
+ */
+typedef struct bitnest_chain_linear {
+    const float *x;
+    const uint8_t *hi;
+    const uint8_t *lo;
+    const uint16_t *scale;
+    float *y;
+    int8_t *xq;
+    float *xs;
+    int32_t N;
+    int32_t K;
+    int32_t act_group;
+    int32_t rot_block;
+} bitnest_chain_linear;
+
+#define BITNEST_CHAIN_MAX_LINEARS 512
+#define BITNEST_CHAIN_MAX_M 4
+#define BITNEST_CHAIN_WORKSPACE_BYTES 2048
+#define BITNEST_CHAIN_DEFAULT_POLLS (1u << 20)
+
+/* BITNEST_CHAIN_WORKSPACE_BYTES, for callers that load the library at run time. */
+size_t bitnest_chain_workspace_bytes(void);
+
+bitnest_status bitnest_linear_chain(const bitnest_chain_linear *links,
+                                    const bitnest_chain_linear *links_dev, int count, int M,
+                                    uint32_t max_polls, void *work, size_t work_bytes,
+                                    void *stream);
 
 /*
  * Offline nested packing of fp32 weights into the two planes (model card

@@ -23,7 +23,7 @@ __all__ = [
     "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
     "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_greedy_accept_workspace_bytes",
     "bitnest_greedy_accept_noalloc", "bitnest_kv_attention",
-    "bitnest_kv_attention_workspace_bytes", "kv_pack",
+    "bitnest_kv_attention_workspace_bytes", "kv_pack", "bitnest_linear_chain", "LinearChain", "ChainLink",
 ]
 
 GROUP = 128
@@ -76,11 +76,14 @@ def lib() -> ctypes.CDLL:
         L.bitnest_kv_attention_workspace_bytes.argtypes = [I, I, I]
         L.bitnest_kv_attention_workspace_bytes.restype = ctypes.c_size_t
         L.bitnest_kv_attention.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.bitnest_linear_chain.argtypes = [P, P, I, I, ctypes.c_uint32, P, ctypes.c_size_t, P]
+        L.bitnest_chain_workspace_bytes.argtypes = []
+        L.bitnest_chain_workspace_bytes.restype = ctypes.c_size_t
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
                   "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested", "bitnest_greedy_accept",
-                  "bitnest_greedy_accept_noalloc", "bitnest_kv_attention"):
+                  "bitnest_greedy_accept_noalloc", "bitnest_kv_attention", "bitnest_linear_chain"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -440,6 +443,95 @@ def bitnest_kv_attention(q: torch.Tensor, k_hi: torch.Tensor, k_scale: torch.Ten
                                      _p(v_lo), _p(v_scale), _p(out), _p(work), work.numel() * work.element_size(),
                                      _stream(q)), "bitnest_kv_attention")
     return out
+
+
+class ChainLink(ctypes.Structure):
+    """One link of bitnest_linear_chain (the C struct bitnest_chain_linear)."""
+    _fields_ = [("x", ctypes.c_void_p), ("hi", ctypes.c_void_p), ("lo", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("y", ctypes.c_void_p), ("xq", ctypes.c_void_p),
+                ("xs", ctypes.c_void_p), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("act_group", ctypes.c_int32), ("rot_block", ctypes.c_int32)]
+
+
+CHAIN_MAX_M = 4
+
+
+class LinearChain:
+    """A fixed chain of (quantise, linear) steps run by one bitnest_linear_chain
+    launch per call of run(). Each link is a dict with the tensors of one
+    bitnest_quant_linear_draft/_target call: x fp32 [M, K], hi uint8 [N, K/2],
+    lo (target chains; None or absent for draft chains), scale [N, K/128],
+    y fp32 [M, N], optional xq int8 [M, K] and xs fp32 [M] or [M, K/128]
+    (both or neither), act_group 0 or 128. The link table is built and copied
+    to the device once here (so run() can be captured in a HIP graph); the
+    tensors must stay alive and in place, which this object ensures by holding
+    them. A link's x may be an earlier link's y."""
+
+    def __init__(self, links, max_polls: int = 0, work: torch.Tensor | None = None):
+        if not links:
+            raise ValueError("a chain needs at least one link")
+        self.count = len(links)
+        self.M = None
+        self.device = None
+        self._keep = []
+        host = (ChainLink * self.count)()
+        for j, d in enumerate(links):
+            x, hi, scale, y = d["x"], d["hi"], _scale_tensor(d["scale"]), d["y"]
+            lo, xq, xs = d.get("lo"), d.get("xq"), d.get("xs")
+            g = int(d.get("act_group", 0))
+            _need(x, "x", torch.float32)
+            if x.dim() != 2:
+                raise ValueError("link %d: x must be [M, K]" % j)
+            M, K = x.shape
+            if self.M is None:
+                self.M, self.device = M, x.device
+            elif M != self.M:
+                raise ValueError("link %d: every link must have the same M" % j)
+            _need(hi, "hi", torch.uint8)
+            if hi.dim() != 2 or hi.shape[1] * 2 != K:
+                raise ValueError("link %d: hi must be [N, K/2] with K=%d" % (j, K))
+            N = hi.shape[0]
+            _need(scale, "scale", torch.int16, (N, K // GROUP))
+            if lo is not None:
+                _need(lo, "lo", torch.uint8, tuple(hi.shape))
+            _need(y, "y", torch.float32, (M, N))
+            if (xq is None) != (xs is None):
+                raise ValueError("link %d: give xq and xs together" % j)
+            if xq is not None:
+                _need(xq, "xq", torch.int8, (M, K))
+                _need(xs, "xs", torch.float32, (M,) if g == 0 else (M, K // GROUP))
+            host[j] = ChainLink(x.data_ptr(), hi.data_ptr(), None if lo is None else lo.data_ptr(),
+                                scale.data_ptr(), y.data_ptr(), None if xq is None else xq.data_ptr(),
+                                None if xs is None else xs.data_ptr(), N, K, g, 0)
+            self._keep += [x, hi, lo, scale, y, xq, xs]
+        self._host = host
+        raw = bytes(memoryview(host).cast("B"))
+        self._dev = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+        nbytes = int(lib().bitnest_chain_workspace_bytes())
+        if work is None:
+            work = torch.zeros((nbytes,), dtype=torch.uint8, device=self.device)
+        _need(work, "work", torch.uint8)
+        if work.numel() < nbytes:
+            raise ValueError("work must hold %d bytes" % nbytes)
+        self.work = work
+        self.max_polls = int(max_polls)
+
+    def run(self):
+        """Enqueue the chain on torch's current stream (one launch)."""
+        _call(lib().bitnest_linear_chain(ctypes.cast(self._host, ctypes.c_void_p), _p(self._dev), self.count,
+                                         self.M, self.max_polls, _p(self.work), self.work.numel(),
+                                         _stream(self.work)), "bitnest_linear_chain")
+
+    def timed_out(self) -> bool:
+        """Whether a wait of some call on this workspace ran out (synchronises)."""
+        return bool(self.work[4:8].view(torch.int32).item())
+
+
+def bitnest_linear_chain(links, max_polls: int = 0):
+    """Build a LinearChain over `links` and run it once; returns the chain."""
+    c = LinearChain(links, max_polls=max_polls)
+    c.run()
+    return c
 
 
 # Short aliases

@@ -7,6 +7,10 @@
 
 #include <atomic>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
 
 namespace bitnest {
 
@@ -14,7 +18,54 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_lds[kMaxDevices];
+
+// Host-side facts about a kernel on a device, looked up once: whether its
+// dynamic-LDS limit has been raised, and its occupancy per LDS size.
+std::mutex g_kernel_mutex;
+std::map<std::pair<const void *, int>, bool> g_lds_raised;
+std::map<std::tuple<const void *, int, int, size_t>, int> g_occupancy;
 }  // namespace
+
+hipError_t set_max_dynamic_lds(const void *kernel, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    DeviceInfo info;
+    e = device_info(&info);
+    if (e != hipSuccess) return e;
+    if (bytes > static_cast<size_t>(info.max_lds)) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(g_kernel_mutex);
+    const auto key = std::make_pair(kernel, dev);
+    if (g_lds_raised.count(key)) return hipSuccess;
+    // raised once to the device's limit, so every later size fits
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, info.max_lds);
+    if (e != hipSuccess) return e;
+    g_lds_raised[key] = true;
+    return hipSuccess;
+}
+
+hipError_t occupancy(const void *kernel, int threads, size_t lds, int *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const auto key = std::make_tuple(kernel, dev, threads, lds);
+    {
+        std::lock_guard<std::mutex> lock(g_kernel_mutex);
+        const auto it = g_occupancy.find(key);
+        if (it != g_occupancy.end()) {
+            *out = it->second;
+            return hipSuccess;
+        }
+    }
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_kernel_mutex);
+    g_occupancy[key] = occ;
+    *out = occ;
+    return hipSuccess;
+}
 
 hipError_t device_info(DeviceInfo *out) {
     int dev = 0;
@@ -269,6 +320,43 @@ bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int 
                       static_cast<float>(1.0 / std::sqrt(static_cast<double>(BITNEST_KV_HEAD_DIM)))};
     return to_status(bitnest::launch_kv_attention(a, static_cast<hipStream_t>(stream)));
 }
+
+bitnest_status bitnest_linear_chain(const bitnest_chain_linear *links, const bitnest_chain_linear *links_dev,
+                                    int count, int M, uint32_t max_polls, void *work, size_t work_bytes,
+                                    void *stream) {
+    if (count < 0) return BITNEST_EINVAL;
+    if (count > BITNEST_CHAIN_MAX_LINEARS) return BITNEST_EUNSUPPORTED;
+    if (count == 0) return BITNEST_OK;
+    if (M < 1) return BITNEST_EINVAL;
+    if (M > BITNEST_CHAIN_MAX_M) return BITNEST_EUNSUPPORTED;
+    if (!links || !links_dev || !work || work_bytes < BITNEST_CHAIN_WORKSPACE_BYTES) return BITNEST_EINVAL;
+    if (!aligned16(links_dev) || !aligned16(work)) return BITNEST_EALIGN;
+    // the kind of the chain: that of its links with rows (a link with N == 0
+    // only quantises, and its weight pointers are not read)
+    int first = 0;
+    while (first < count && links[first].N == 0) ++first;
+    const bool target = first < count && links[first].lo != nullptr;
+    int kmax = 0;
+    for (int j = 0; j < count; ++j) {
+        const bitnest_chain_linear &L = links[j];
+        if (L.N > 0 && (L.lo != nullptr) != target) return BITNEST_EINVAL;      // one kind per chain
+        if (L.act_group != 0 && L.act_group != kGroup) return BITNEST_EINVAL;
+        if (L.rot_block != 0) return BITNEST_EUNSUPPORTED;
+        const bitnest_status st = check_sizes(M, L.N, L.K);
+        if (st != BITNEST_OK) return st;
+        if (!L.x || (L.xq == nullptr) != (L.xs == nullptr)) return BITNEST_EINVAL;
+        if (L.N > 0 && (!L.hi || !L.scale || !L.y)) return BITNEST_EINVAL;
+        if (!aligned16(L.x) || (L.xq && (!aligned16(L.xq) || !aligned16(L.xs)))) return BITNEST_EALIGN;
+        if (L.N > 0 && (!aligned16(L.hi) || !aligned16(L.scale) || !aligned16(L.y) || (target && !aligned16(L.lo))))
+            return BITNEST_EALIGN;
+        if (L.K > kmax) kmax = L.K;
+    }
+    const unsigned polls = max_polls ? max_polls : BITNEST_CHAIN_DEFAULT_POLLS;
+    return to_status(bitnest::launch_chain(links_dev, count, M, target, kmax, static_cast<unsigned *>(work), polls,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t bitnest_chain_workspace_bytes(void) { return BITNEST_CHAIN_WORKSPACE_BYTES; }
 
 bitnest_status bitnest_linear_partials(const int8_t *xq, const uint8_t *hi, const uint8_t *lo, int32_t *p_hi,
                                        int32_t *p_lo, int32_t *p8, int M, int N, int K, void *stream) {

@@ -19,6 +19,14 @@ struct DeviceInfo {
 };
 hipError_t device_info(DeviceInfo *out);
 
+// Raise a kernel's dynamic-LDS limit on the current device when a launch
+// needs more than 64 KiB (once per kernel and device).
+hipError_t set_max_dynamic_lds(const void *kernel, size_t bytes);
+
+// Workgroups of `threads` threads with `lds` bytes of dynamic LDS that fit on
+// one compute unit of the current device (looked up once and kept).
+hipError_t occupancy(const void *kernel, int threads, size_t lds, int *out);
+
 // Everything a linear launch needs. Pointers are device pointers.
 struct LinearArgs {
     const int8_t *xq;
@@ -109,5 +117,19 @@ hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream);
 
 // 8 <= M <= kMaxM.
 hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStream_t stream);
+
+}  // namespace bitnest
+
+struct bitnest_chain_linear;
+
+namespace bitnest {
+
+// A chain of quantise + linear steps in one launch (chain.hip). links_dev:
+// device copy of the validated chain; M <= 4 tokens; kmax the largest K;
+// sync: the caller's workspace words (arrival counter, time-out flag).
+constexpr int kChainMaxM = 4;
+size_t chain_lds_bytes(int count, int M, int kmax);
+hipError_t launch_chain(const bitnest_chain_linear *links_dev, int count, int M, bool target, int kmax,
+                        unsigned *sync, unsigned max_polls, hipStream_t stream);
 
 }  // namespace bitnest

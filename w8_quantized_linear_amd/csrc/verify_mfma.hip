@@ -412,11 +412,8 @@ hipError_t launch_verify_mfma(const LinearArgs &a, bool export_partials, hipStre
     const size_t stream_lds = kChunkLead * (target ? chunk_lds_bytes<2>() : chunk_lds_bytes<1>());
     const size_t lds = (stream_lds > exchange ? stream_lds : exchange) + (grouped ? G * 16 * T * 4 : 0);
     if (lds > static_cast<size_t>(dev.max_lds)) return hipErrorInvalidValue;
-    if (lds > 65536) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-    }
+    e = set_max_dynamic_lds(reinterpret_cast<const void *>(k), lds);
+    if (e != hipSuccess) return e;
     const int blocks = (a.N + R - 1) / R;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(64 * kSplit), lds, stream, a, R);
     return hipGetLastError();
