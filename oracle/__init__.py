@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bitnest_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A prebuilt copy of this same source (for instance one compiled with
+# sanitizers) may be named here; it is then loaded as it is, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("BITNEST_ORACLE_LIB")
 GROUP = 128
 
 
@@ -41,9 +44,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
