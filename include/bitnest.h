@@ -371,8 +371,10 @@ bitnest_status bitnest_greedy_accept_noalloc(const float *logits, int R, int V, 
  *   - out[i, hq] = sum_t softmax_t(q[i, hq] . k[t] / sqrt(128)) v[t].
  * Computed in fp32: the sequence is cut into splits (runs of 64-position
  * chunks, their number sized to the device), each split keeps a running
- * softmax, and the splits are merged exactly as the softmax requires;
- * |out - out_exact| stays within a few 1e-6 of the values' magnitude.
+ * softmax, and the splits are merged exactly as the softmax requires.
+ * Scores and P.V run on the fp16 matrix cores with each fp32 operand split
+ * into three fp16 pieces, so each (token, head) output is within 1e-5 of
+ * its own largest magnitude (measured: below 1e-6) of the exact result.
  *
  *   q        fp32 [M, Hq, 128]
  *   T        positions in the sequence; t_cap  positions per head in the cache
@@ -394,6 +396,26 @@ bitnest_status bitnest_kv_attention(const float *q, int M, int Hq, int Hkv, int 
                                     const uint8_t *k_hi, const uint8_t *k_lo, const uint16_t *k_scale,
                                     const uint8_t *v_hi, const uint8_t *v_lo, const uint16_t *v_scale,
                                     float *out, void *work, size_t work_bytes, void *stream);
+
+/*
+ * Measurement, not part of the linear: reads `bytes` bytes at p with the
+ * plane stream's loads (1 KiB per wave load instruction, non-temporal
+ * 128-bit loads, 8-wave workgroups, each wave a contiguous run of rounds of
+ * `depth` items with one round in flight) and none of its arithmetic, so
+ * that the time of one call bounds what a linear streaming that many plane
+ * bytes can reach (the model card's introduction prices a draft step by the
+ * plane bytes it reads). The data are folded into one word, which is
+ * written to sink[0] only if it equals `never` (pick a value the data
+ * cannot fold to; the store keeps the loads from being dropped).
+ *   p      device memory, 16-byte aligned; bytes a multiple of 1024,
+ *          1024 <= bytes <= 2^32 - 1024
+ *   depth  items in flight per wave: 2, 4 or 8
+ *   waves_per_cu  resident waves per compute unit to use at most (0: as
+ *          many as fit); the grid is min(rounds, that many per CU) waves
+ *   sink   device memory for one uint32, written at most once
+ */
+bitnest_status bitnest_stream_read(const void *p, size_t bytes, int depth, int waves_per_cu, uint32_t never,
+                                   uint32_t *sink, void *stream);
 
 /*
  * The integer partials of the draft and target calls above, for checking (not a

@@ -3,10 +3,15 @@ KV8) against the CPU oracle, through the C ABI.
 
 The caches are packed on the CPU by the oracle (in its [T, Hkv] order) and
 uploaded in the library's head-major layout, so every input of the oracle is
-its own. Bar: max|out - out_oracle| <= 1e-5 * max|V| over the
-visible values (the oracle is fp64; the kernel accumulates in fp32 over
-splits of 64-position chunks with a running softmax, then merges the
-splits). Invariants checked bit for bit on the GPU: KV8 with lo
+its own. Bar, per (token, query head): max over the 128 dimensions of
+|out - out_oracle| <= 1e-5 * max|out_oracle| of that (token, head), plus
+1e-8 * max|V| so that an output that cancels to nearly zero is not held to
+a bound below fp32 resolution (the oracle is fp64; the kernel accumulates
+in fp32 over splits of 64-position chunks with a running softmax, then
+merges the splits; measured on these cases: at most 7e-7 of the output's
+own magnitude). At long contexts a flat softmax makes the output about
+max|V| / sqrt(T), so a bar relative to max|V| alone would admit
+percent-level errors there; this one does not. Invariants checked bit for bit on the GPU: KV8 with lo
 planes of 8 equals KV4; token i of an M-token call equals a one-token call on
 the cache cut after its last visible position.
 """
@@ -19,7 +24,8 @@ import w8_quantized_linear_amd as bn
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-5
+TOL = 1e-5          # relative to each (token, head) output
+FLOOR = 1e-8        # relative to max|V|
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -67,6 +73,13 @@ def _ref(q, kc, vc, kv8):
     return oracle.kv_attention(q, kc[0], kc[2], vc[0], vc[2], kc[1] if kv8 else None, vc[1] if kv8 else None)
 
 
+def _check(got, want, vmax):
+    err = np.abs(got - want).max(axis=-1)             # [M, Hq]
+    bound = TOL * np.abs(want).max(axis=-1) + FLOOR * vmax
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert (err <= bound).all(), ("token, head", worst, err[worst], bound[worst])
+
+
 def _vmax(vc, kv8):
     hi, lo, sc = vc
     T, Hkv, _ = hi.shape
@@ -87,8 +100,7 @@ def test_kv_attention_matches_oracle(M, Hq, Hkv, T, kv8):
     q = np.random.default_rng(T).standard_normal((M, Hq, 128)).astype(np.float32)
     got = _run(q, kc, vc, kv8)
     want = _ref(q, kc, vc, kv8)
-    err = np.abs(got - want).max()
-    assert err <= TOL * _vmax(vc, kv8), (err, _vmax(vc, kv8))
+    _check(got, want, _vmax(vc, kv8))
 
 
 @pytest.mark.parametrize("M,T,t_cap", [(1, 2048, 2049), (4, 1000, 4096), (4, 20001, 20480)])
@@ -100,7 +112,7 @@ def test_kv_attention_reads_only_the_first_t_positions_of_each_head(M, T, t_cap,
     q = np.random.default_rng(T).standard_normal((M, 32, 128)).astype(np.float32)
     got = _run(q, kc, vc, kv8, t_cap=t_cap)
     want = _ref(q, kc, vc, kv8)
-    assert np.abs(got - want).max() <= TOL * _vmax(vc, kv8)
+    _check(got, want, _vmax(vc, kv8))
 
 
 def test_kv_peaked_scores():
@@ -109,7 +121,7 @@ def test_kv_peaked_scores():
     q = (np.random.default_rng(8).standard_normal((4, 32, 128)) * 3).astype(np.float32)
     got = _run(q, kc, vc, True)
     want = _ref(q, kc, vc, True)
-    assert np.abs(got - want).max() <= TOL * _vmax(vc, True)
+    _check(got, want, _vmax(vc, True))
 
 
 @pytest.mark.parametrize("T", [300, 20000])    # one chunk per split / runs of chunks
