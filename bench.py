@@ -33,6 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+COLD_BYTES = 512 << 20         # distinct bytes a cold-read cycle covers (2x the 256 MiB Infinity Cache)
+# buffer sizes of the read ceiling: each linear's plane bytes (draft: hi,
+# target: hi + lo) of the Llama-3-8B shapes, and a large buffer
+READ_CEILING_MIB = (8, 12, 16, 24, 28, 56, 112, 2048)
 GAMMA = 3
 
 
@@ -53,6 +57,8 @@ def parse_args(argv=None):
                         "reference dispatch for hardware byte counters)")
     p.add_argument("--verify-batches", default="8,16,32",
                    help="token counts for the batched-verify (matrix-core) layer timing; empty to skip")
+    p.add_argument("--no-read-ceiling", dest="read_ceiling", action="store_false", default=True,
+                   help="skip the streaming-read ceiling (bitnest_stream_read per buffer size)")
     p.add_argument("--no-per-linear", dest="per_linear", action="store_false", default=True,
                    help="skip the per-linear timing (each shape on its own, draft/target M=1, target M=4)")
     p.add_argument("--no-r4", dest="r4", action="store_false", default=True,
@@ -81,6 +87,9 @@ class Stack:
         from w8_quantized_linear_amd import synth
         self.linears = synth.LLAMA3_8B_LINEARS
         self.layers = layers
+        self.seed = seed
+        self.device = device
+        self.extra = {}          # linear index -> weights past the stack's layers (cold cycles)
         self.w = []
         for l in range(layers):
             self.w.append([synth.make_weights(N, K, seed=seed, layer=l, linear=i, device=device)
@@ -126,6 +135,21 @@ class Stack:
 
     def gemv_launches_per_round(self):
         return (GAMMA + 1) * self.layers * len(self.linears)
+
+    def cold_weights(self, i, planes, at_least=COLD_BYTES):
+        """Distinct weights of linear i whose `planes` plane bytes add up to
+        at least `at_least` (the stack's layers first, then extra seeded
+        layers of the same shape), so that cycling through them reads every
+        byte from HBM: twice the 256 MiB Infinity Cache."""
+        from w8_quantized_linear_amd import synth
+        _, N, K, _ = self.linears[i]
+        need = -(-at_least // (planes * N * K // 2))
+        ws = [self.w[l][i] for l in range(min(need, self.layers))]
+        extra = self.extra.setdefault(i, [])
+        while len(ws) + len(extra) < need:
+            extra.append(synth.make_weights(N, K, seed=self.seed, layer=self.layers + len(extra), linear=i,
+                                            device=self.device))
+        return ws + extra[:need - len(ws)]
 
 
 def run_round(stack, bn, mode="fused", rot_block=0):
@@ -210,13 +234,64 @@ def gemv_kernel_timing(stack, bn, steps):
 INT8_DENSE_PEAK_OPS = 5.0e15       # MI355X dense int8 matrix-core peak, ops/s
 
 
-def per_linear(stack, bn, reps=5):
-    """Each linear shape on its own: one launch per layer of the stack (cold
-    weights, a different layer each launch) replayed from a HIP graph and
-    timed with HIP events; us per launch and plane GB/s with its fraction of
-    the 8 TB/s peak. Modes: draft M=1 and target M=1 (the fused call, one
-    launch), target M=4 (the linear on ready codes; its separate
-    quantisation launch is timed on its own as quant_M4)."""
+READ_CONFIGS = ((2, 0), (4, 0), (8, 0), (4, 8), (8, 8), (4, 16), (8, 16))   # (depth, waves per CU; 0 = all)
+
+
+def read_ceiling(bn, reps=5):
+    """The HBM read ceiling per buffer size: bitnest_stream_read (the plane
+    stream's loads, no arithmetic) over a cycle of distinct buffers of that
+    size covering at least 512 MiB (one buffer of 2 GiB), so every launch
+    reads cold memory, replayed from a HIP graph and timed with HIP events,
+    launch overhead included as it is for a linear of the same plane bytes.
+    Every (items in flight per wave, waves per CU) of READ_CONFIGS is timed;
+    the ceiling is the fastest, reported with its configuration."""
+    import torch
+    out = {}
+    sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    for mib in READ_CEILING_MIB:
+        size = mib << 20
+        count = max(1, -(-COLD_BYTES // size))
+        pool = torch.empty((count, size), dtype=torch.uint8, device="cuda")
+        best = None
+        for depth, wpc in READ_CONFIGS:
+            def fn(pool=pool, count=count, depth=depth, wpc=wpc):
+                for c in range(count):
+                    bn.bitnest_stream_read(pool[c], sink, depth=depth, waves_per_cu=wpc)
+            g = capture(fn)
+            g.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3 / count)
+            t = sorted(ts)[len(ts) // 2]
+            if best is None or t < best[0]:
+                best = (t, depth, wpc)
+            del g
+        t, depth, wpc = best
+        out["%dMiB" % mib] = {"us": round(t * 1e6, 3), "GBps": round(size / t / 1e9, 1),
+                              "frac": round(size / t / 1e9 / HBM_PEAK_GBS, 4), "buffers": count,
+                              "depth": depth, "waves_per_cu": wpc or "max"}
+        del pool
+        torch.cuda.empty_cache()
+    log("read ceiling: %s" % ", ".join("%s %.0f GB/s (%.2f us)" % (k, v["GBps"], v["us"]) for k, v in out.items()))
+    return out
+
+
+def per_linear(stack, bn, ceiling=None, reps=5):
+    """Each linear shape on its own: a cycle of launches over distinct
+    weights of that shape covering at least 512 MiB of plane bytes (the
+    stack's layers, then extra seeded layers), so that every launch reads
+    cold weights, replayed from a HIP graph and timed with HIP events; us per
+    launch and plane GB/s with its fraction of the 8 TB/s peak and of the
+    measured read ceiling at the same number of bytes. Modes: draft M=1 and
+    target M=1 (the fused call, one launch), target M=4 (the linear on ready
+    codes; its separate quantisation launch is timed on its own as
+    quant_M4, one launch per layer)."""
     import torch
     out = {}
     L = stack.layers
@@ -241,13 +316,18 @@ def per_linear(stack, bn, reps=5):
             M = 4 if mode.endswith("M4") else 1
             xq, xs, y = stack.buf[(M, i)]
 
-            def fn(i=i, g=g, xq=xq, xs=xs, y=y):
-                for l in range(L):
-                    w = stack.w[l][i]
+            planes = 1 if mode == "draft_M1" else 2
+            ws = stack.cold_weights(i, planes) if mode != "quant_M4" else []
+            n = len(ws) if ws else L
+
+            def fn(i=i, g=g, xq=xq, xs=xs, y=y, ws=ws):
+                for l in range(n):
+                    w = ws[l] if ws else None
                     if mode == "draft_M1":
-                        bn.bitnest_quant_linear_draft(stack.x_draft[0][l][i], w.hi, w.scale, g, y=y, xq=xq, xs=xs)
+                        bn.bitnest_quant_linear_draft(stack.x_draft[0][l % L][i], w.hi, w.scale, g,
+                                                      y=y, xq=xq, xs=xs)
                     elif mode == "target_M1":
-                        bn.bitnest_quant_linear_target(stack.x_draft[0][l][i], w.hi, w.lo, w.scale, g,
+                        bn.bitnest_quant_linear_target(stack.x_draft[0][l % L][i], w.hi, w.lo, w.scale, g,
                                                        y=y, xq=xq, xs=xs)
                     elif mode == "target_M4":
                         bn.bitnest_linear_target(xq, xs, w.hi, w.lo, w.scale, g, y=y)
@@ -255,12 +335,16 @@ def per_linear(stack, bn, reps=5):
                         bn.bitnest_quant_act(stack.x_verify[l][i], g, xq=xq, xs=xs)
             if mode == "target_M4":
                 bn.bitnest_quant_act(stack.x_verify[0][i], g, xq=xq, xs=xs)
-            t = timed(fn, L)
+            t = timed(fn, n)
             entry = {"us": round(t * 1e6, 3)}
             if mode != "quant_M4":
-                plane = N * K // 2 * (1 if mode == "draft_M1" else 2)
+                plane = N * K // 2 * planes
                 gbs = plane / t / 1e9
-                entry.update({"plane_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+                entry.update({"plane_GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "cold_set": {"launches": n, "plane_bytes": n * plane}})
+                ceil = (ceiling or {}).get("%dMiB" % (plane >> 20))
+                if ceil and plane % (1 << 20) == 0:
+                    entry["of_read_ceiling"] = round(gbs / ceil["GBps"], 4)
             res[name] = entry
         out[mode] = res
         log("per linear %s: %s" % (mode, ", ".join("%s %.2f us%s" % (k, v["us"], (" %.0f GB/s" % v["plane_GBps"])
@@ -525,13 +609,26 @@ def measured_traffic():
     return prof["traffic_bytes_per_launch"] if h.hexdigest() == prof["sources_sha256"] else None
 
 
-def cpu_baseline(stack, budget_s):
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(stack, budget_s, threads=None):
     """The oracle on the machine's host cores over a bounded sample of the round:
     the first layer(s) of the stack, 3 draft passes + 1 verify pass each,
-    quantisation plus linear, until about `budget_s` seconds of CPU work."""
-    import numpy as np
+    quantisation plus linear, until about `budget_s` seconds of CPU work
+    (at least one layer). `threads`: the oracle's thread count (default: all
+    it may use)."""
     import oracle
-    threads = oracle.max_threads()
+    threads = oracle.max_threads() if threads is None else threads
     done_bytes = 0
     t_total = 0.0
     layers_done = 0
@@ -619,7 +716,8 @@ def main(argv=None):
                     "algorithmic_bytes_per_launch": int(per_launch_bytes)}
         log("GEMV: %.3f us per launch (events), %.1f GB/s algorithmic" % (t_gemv * 1e6, achieved))
 
-    linears = per_linear(stack, bn) if args.per_linear else None
+    ceiling = read_ceiling(bn) if args.read_ceiling else None
+    linears = per_linear(stack, bn, ceiling) if args.per_linear else None
     r4 = r4_timing(stack, bn, steps=min(args.steps, 10)) if args.r4 else None
     pack = pack_timing(stack, bn) if args.pack else None
     accept = accept_timing(bn) if args.accept else None
@@ -633,7 +731,11 @@ def main(argv=None):
     cpu = None
     if args.cpu_baseline:
         cpu = cpu_baseline(stack, args.cpu_seconds)
-        log("cpu oracle: %s GB/s on %d threads" % (cpu["value"], cpu["cores"]))
+        cpu["cpu_model"] = cpu_model()
+        log("cpu oracle: %s GB/s on %d threads (%s)" % (cpu["value"], cpu["cores"], cpu["cpu_model"]))
+        one = cpu_baseline(stack, args.cpu_seconds / 2, threads=1)
+        cpu["one_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+        log("cpu oracle: %s GB/s on 1 thread" % one["value"])
 
     out = {
         "metric": "nested W4/W8 linear: plane GB/s (% HBM peak), draft M=1 & verify M=4",
@@ -656,6 +758,7 @@ def main(argv=None):
                    "replay": "hip_graph"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
+        "read_ceiling": ceiling,
         "per_linear": linears,
         "r4": r4,
         "pack": pack,

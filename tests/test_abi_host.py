@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
               "bitnest_hadamard_quant_linear_draft", "bitnest_hadamard_quant_linear_target",
               "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_kv_attention",
               "bitnest_kv_attention_workspace_bytes", "bitnest_greedy_accept_workspace_bytes",
-              "bitnest_greedy_accept_noalloc"):
+              "bitnest_greedy_accept_noalloc", "bitnest_stream_read"):
         assert n in names
 
 
@@ -97,6 +97,10 @@ def _ga(lg, R, V, dr, tg, res, w=_DEFAULT, wb=1 << 20):
 
 def _gn(lg, R, V, dr, tg, res):
     return bn.lib().bitnest_greedy_accept_noalloc(lg, R, V, dr, tg, res, None)
+
+
+def _sr(p, nbytes, sink, depth=4, wpc=0):
+    return bn.lib().bitnest_stream_read(p, nbytes, depth, wpc, 0, sink, None)
 
 
 def _pk(W, N, K, hi, lo, sc):
@@ -192,6 +196,16 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _hd(NUL, 512, NUL, NUL, NUL, NUL, NUL, 0, 8, 512), bn.OK),
     (lambda: _ht(A, 512, B, NUL, C, D, E, F, 1, 8, 512), bn.EINVAL),
     (lambda: _ht(A, 512, B, MIS, C, D, E, F, 1, 8, 512), bn.EALIGN),
+    # read-ceiling measurement: whole KiB, at least one, below 4 GiB
+    (lambda: _sr(NUL, 1024, B), bn.EINVAL),
+    (lambda: _sr(A, 1024, NUL), bn.EINVAL),
+    (lambda: _sr(A, 0, B), bn.EINVAL),
+    (lambda: _sr(A, 1000, B), bn.EINVAL),
+    (lambda: _sr(A, 1 << 32, B), bn.EINVAL),
+    (lambda: _sr(MIS, 1024, B), bn.EALIGN),
+    (lambda: _sr(A, 1024, B, 3), bn.EINVAL),
+    (lambda: _sr(A, 1024, B, 16), bn.EINVAL),
+    (lambda: _sr(A, 1024, B, 4, -1), bn.EINVAL),
     # nested packing
     (lambda: _pk(NUL, 4, 128, B, C, D), bn.EINVAL),
     (lambda: _pk(A, 4, 128, NUL, C, D), bn.EINVAL),

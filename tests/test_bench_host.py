@@ -82,3 +82,25 @@ def test_traffic_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
 @pytest.mark.parametrize("gpus", ["0", "8"])
 def test_gpu_count_other_than_one_exits_before_touching_a_gpu(gpus):
     assert bench.main(["--gpus", gpus]) == 2
+
+
+def test_cold_weight_cycles_cover_the_requested_bytes():
+    # the stack's layers first, then extra seeded layers of the same shape,
+    # until the plane bytes of the cycle reach the requested amount
+    import bench
+    from w8_quantized_linear_amd import synth
+    st = bench.Stack.__new__(bench.Stack)
+    st.linears = [("a", 8, 256, 0), ("b", 16, 128, 0)]
+    st.layers, st.seed, st.device, st.extra = 2, 5, "cpu", {}
+    st.w = [[synth.make_weights(N, K, seed=5, layer=l, linear=i) for i, (_, N, K, _) in enumerate(st.linears)]
+            for l in range(2)]
+    one = 8 * 256 // 2
+    ws = st.cold_weights(0, 1, at_least=5 * one)
+    assert len(ws) == 5 and ws[0] is st.w[0][0] and ws[1] is st.w[1][0]
+    assert len({w.hi.data_ptr() for w in ws}) == 5
+    extra = synth.make_weights(8, 256, seed=5, layer=2, linear=0)
+    assert (ws[2].hi == extra.hi).all() and (ws[2].scale == extra.scale).all()
+    # target cycles count both planes; the extra layers are reused
+    wt = st.cold_weights(0, 2, at_least=5 * one)
+    assert len(wt) == 3 and wt[2] is ws[2]
+    assert len(st.cold_weights(1, 1, at_least=1)) == 1

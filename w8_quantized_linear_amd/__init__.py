@@ -24,6 +24,7 @@ __all__ = [
     "bitnest_pack_nested", "bitnest_greedy_accept", "bitnest_greedy_accept_workspace_bytes",
     "bitnest_greedy_accept_noalloc", "bitnest_kv_attention",
     "bitnest_kv_attention_workspace_bytes", "kv_pack", "bitnest_linear_chain", "LinearChain", "ChainLink",
+    "bitnest_stream_read",
 ]
 
 GROUP = 128
@@ -78,12 +79,14 @@ def lib() -> ctypes.CDLL:
         L.bitnest_kv_attention.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bitnest_linear_chain.argtypes = [P, P, I, I, ctypes.c_uint32, P, ctypes.c_size_t, P]
         L.bitnest_chain_workspace_bytes.argtypes = []
+        L.bitnest_stream_read.argtypes = [P, ctypes.c_size_t, I, I, ctypes.c_uint32, P, P]
         L.bitnest_chain_workspace_bytes.restype = ctypes.c_size_t
         for f in ("bitnest_quant_act", "bitnest_linear_draft", "bitnest_linear_target",
                   "bitnest_linear_partials", "bitnest_quant_linear_draft", "bitnest_quant_linear_target",
                   "bitnest_hadamard_quant_act", "bitnest_hadamard_quant_linear_draft",
                   "bitnest_hadamard_quant_linear_target", "bitnest_pack_nested", "bitnest_greedy_accept",
-                  "bitnest_greedy_accept_noalloc", "bitnest_kv_attention", "bitnest_linear_chain"):
+                  "bitnest_greedy_accept_noalloc", "bitnest_kv_attention", "bitnest_linear_chain",
+                  "bitnest_stream_read"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -384,6 +387,21 @@ def bitnest_greedy_accept_noalloc(logits: torch.Tensor, draft: torch.Tensor, tar
                                               _p(result), _stream(logits)),
           "bitnest_greedy_accept_noalloc")
     return targ, result
+
+
+def bitnest_stream_read(buf: torch.Tensor, sink: torch.Tensor, never: int = 0x5EEDF00D, depth: int = 4,
+                        waves_per_cu: int = 0):
+    """Read all of ``buf`` (contiguous, 16-byte aligned, a multiple of 1 KiB)
+    with the plane stream's loads and no arithmetic: a measurement of the HBM
+    read ceiling. ``depth`` items in flight per wave (2, 4 or 8), at most
+    ``waves_per_cu`` resident waves per compute unit (0: as many as fit).
+    ``sink`` (one int32 on the device) is written only if the folded data
+    equal ``never``."""
+    _need(buf, "buf", buf.dtype)
+    _need(sink, "sink", torch.int32)
+    nbytes = buf.numel() * buf.element_size()
+    _call(lib().bitnest_stream_read(_p(buf), nbytes, depth, waves_per_cu, never & 0xFFFFFFFF, _p(sink),
+                                    _stream(buf)), "bitnest_stream_read")
 
 
 KV_HEAD_DIM = 128

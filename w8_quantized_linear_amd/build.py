@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libbitnest.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "quant_act.hip", "gemv_planes.hip", "verify_mfma.hip", "pack_nested.hip", "accept.hip", "kv_attention.hip",
-           "chain.hip"]
+           "chain.hip", "stream_read.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -297,6 +297,15 @@ bitnest_status bitnest_greedy_accept_noalloc(const float *logits, int R, int V, 
                                                            static_cast<hipStream_t>(stream)));
 }
 
+bitnest_status bitnest_stream_read(const void *p, size_t bytes, int depth, int waves_per_cu, uint32_t never,
+                                   uint32_t *sink, void *stream) {
+    if (!p || !sink || bytes < 1024 || bytes % 1024 != 0 || bytes > 0xFFFFFC00ull) return BITNEST_EINVAL;
+    if ((depth != 2 && depth != 4 && depth != 8) || waves_per_cu < 0) return BITNEST_EINVAL;
+    if (!aligned16(p)) return BITNEST_EALIGN;
+    return to_status(bitnest::launch_stream_read(p, bytes, depth, waves_per_cu, never, sink,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 size_t bitnest_kv_attention_workspace_bytes(int M, int Hq, int T) {
     if (M < 1 || Hq < 1 || T < 1) return 0;
     return bitnest::kv_attention_workspace_bytes(M, Hq, T);

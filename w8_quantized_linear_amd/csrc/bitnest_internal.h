@@ -79,6 +79,8 @@ hipError_t launch_greedy_accept(const float *logits, int R, int V, const int32_t
 // of accept_noalloc_scratch_bytes(), enough for R <= kMaxM and any V): no
 // allocation; calls that overlap on one device race on it.
 size_t accept_noalloc_scratch_bytes();
+hipError_t launch_stream_read(const void *p, size_t bytes, int depth, int waves_per_cu, unsigned never,
+                              unsigned *sink, hipStream_t stream);
 hipError_t launch_greedy_accept_noalloc(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
                                         int32_t *result, hipStream_t stream);
 
