@@ -375,12 +375,14 @@ FUSED_SHAPES = [(256, 512), (37, 640), (70, 2176), (33, 14336), (129, 4096), (17
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
-@pytest.mark.parametrize("M", [1, 2, 4, 7, 8, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 8, 32])
 @pytest.mark.parametrize("act_group", [0, 128])
 @pytest.mark.parametrize("target", [False, True])
 def test_fused_quant_linear_equals_two_calls(M, N, K, act_group, target):
     # One fused call must give the codes, scales and y of quant_act followed by
-    # the linear, bit for bit (one launch when M*K <= 16384, else two).
+    # the linear, bit for bit (one launch for one token up to K = 16384 and
+    # for up to four tokens up to K = 4096, else two).
+    assert bn.fused_in_one_launch(M, K) == ((M == 1 and K <= 16384) or (M <= 4 and K <= 4096))
     w, x = _problem(M, N, K, seed=9)
     xd, hi, lo, sc = _dev(x), _dev(w.hi), _dev(w.lo), _dev(w.scale)
     xq, xs = bn.bitnest_quant_act(xd, act_group)
@@ -400,15 +402,16 @@ def test_fused_quant_linear_equals_two_calls(M, N, K, act_group, target):
     _check_y(y, oracle.linear(q, s, hi_n, sc_n, lo_n if target else None, act_group), "fused")
 
 
-@pytest.mark.parametrize("target", [False, True])
-def test_fused_single_token_full_layer(llama_layer, target):
-    # The launch a draft pass times: quantisation and the linear in one launch
-    # (one workgroup per CU, several rows per wave) at the four Llama-3-8B
-    # shapes, o_proj with per-group activation scales. Codes, scales and y are
-    # bit-identical to the two-call path; every row of y is within the bar of
-    # the oracle.
+@pytest.mark.parametrize("M,target", [(1, False), (1, True), (4, True), (4, False), (2, True)])
+def test_fused_single_token_full_layer(llama_layer, M, target):
+    # The launches a round times: quantisation and the linear in one launch
+    # (one token: a draft pass, all four shapes; four tokens: the verify pass
+    # at K = 4096, qkv, o_proj and gate_up, while down takes two launches) at
+    # the Llama-3-8B shapes, o_proj with per-group activation scales. Codes,
+    # scales and y are bit-identical to the two-call path; every row of y is
+    # within the bar of the oracle.
     for li, (name, N, K, g, w, wd) in enumerate(llama_layer):
-        x = synth.make_activations(1, K, seed=0, layer=1, linear=li)
+        x = synth.make_activations(M, K, seed=0, layer=1, linear=li)
         xd = _dev(x)
         xq, xs = bn.bitnest_quant_act(xd, g)
         if target:

@@ -114,7 +114,14 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
 // return hipErrorNotSupported; the caller then runs launch_quant_act and a
 // linear launch.
 constexpr int kFusedMaxMK = 16384;
-inline bool fused_in_one_launch(int M, int K) { return M == 1 && K <= kFusedMaxMK; }
+// Several tokens fit one launch when each thread holds one 8-column unit of
+// every token (K <= 8 units x 512 threads), without the rotation.
+constexpr int kFusedMaxTokens = 4;
+constexpr int kFusedMaxTokensK = 4096;
+inline bool fused_in_one_launch(int M, int K, int rot_block) {
+    return (M == 1 && K <= kFusedMaxMK) ||
+           (rot_block == 0 && M >= 1 && M <= kFusedMaxTokens && K <= kFusedMaxTokensK);
+}
 hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream);
 
 // 8 <= M <= kMaxM.

@@ -212,30 +212,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
         }
         __syncthreads();
     } else {
-        static_assert(M == 1, "the fused prologue quantises one token");
-        // 1) the fp32 row in 8-column units u = tid + k * threads (k < XU),
-        //    two 16-byte loads each; lanes past the row read zeros (the
-        //    descriptor ends with the row, and such loads make no memory
-        //    traffic). The loads are unconditional (under a branch, the
-        //    compiler adds register copies at its join). Every code needs the
-        //    row's maximum, so the row's loads are the critical path: a
-        //    workgroup barrier (which waits for no data) puts every wave's row
-        //    loads ahead of any item load in the compute unit's load queue,
-        //    and the ring is then issued at once, its latency overlapping
-        //    the row's arrival and the quantisation. (Measured: issued per
-        //    wave right behind its own row loads, the later waves' row loads
-        //    queued behind the earlier waves' items; waiting for the row
-        //    before issuing the ring cost 0.1-0.2 us more per launch than
-        //    this order.)
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, static_cast<unsigned>(K) * 4u);
+        static_assert(M == 1 || (XU == 1 && ROT == 0), "several tokens: one unit per thread, no rotation");
+        // 1) the fp32 rows in 8-column units u = tid + k * threads (k < XU),
+        //    two 16-byte loads each; units past a row read zeros (an offset
+        //    past the descriptor's end makes no memory traffic). The loads
+        //    are unconditional (under a branch, the compiler adds register
+        //    copies at its join). Every code needs its row's maximum, so the
+        //    row loads are the critical path: a workgroup barrier (which
+        //    waits for no data) puts every wave's row loads ahead of any item
+        //    load in the compute unit's load queue, and the ring is then
+        //    issued at once, its latency overlapping the rows' arrival and
+        //    the quantisation. (Measured: issued per wave right behind its
+        //    own row loads, the later waves' row loads queued behind the
+        //    earlier waves' items; waiting for the rows before issuing the
+        //    ring cost 0.1-0.2 us more per launch than this order.)
+        const unsigned x_bytes = static_cast<unsigned>(M) * static_cast<unsigned>(K) * 4u;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, x_bytes);
         const int nunit = K >> 3;
-        u32x4 xr[XU][2];
+        u32x4 xr[M][XU][2];
 #pragma unroll
-        for (int k = 0; k < XU; ++k) {
-            const int off = (threadIdx.x + k * kThreads) * 32;
-            xr[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-            xr[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
-        }
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int k = 0; k < XU; ++k) {
+                const int u = threadIdx.x + k * kThreads;
+                const int off = u < nunit ? (m * K + u * 8) * 4 : static_cast<int>(x_bytes);
+                xr[m][k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+                xr[m][k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
+            }
         __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(ring[d]);
@@ -243,14 +246,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
         // (each element is copied out before the bit cast: a bit cast applied
         // directly to a vector-element lvalue reads element 0 with this
         // compiler)
-        float xf[XU][8];
+        float xf[M][XU][8];
 #pragma unroll
-        for (int k = 0; k < XU; ++k)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xf[k][i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][0][i]));
-                xf[k][4 + i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[k][1][i]));
-            }
+            for (int k = 0; k < XU; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xf[m][k][i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[m][k][0][i]));
+                    xf[m][k][4 + i] = __builtin_bit_cast(float, static_cast<unsigned>(xr[m][k][1][i]));
+                }
         if constexpr (ROT != 0) {
             // unit u = tid + k * threads: one wave's units at one k are 512
             // consecutive columns, so every rotation block is inside a wave
@@ -259,10 +264,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
                 // wave-uniform: units past the row stay zero (marked as the
                 // rare case, so that the transform is laid out in line)
                 if (__builtin_expect(k * kThreads + wave * 64 < nunit, 1)) {
-                    if constexpr (ROT == 1) fwht_unit(xf[k], lane, a.rot_block);
-                    else fwht_unit_fixed<ROT>(xf[k], lane);
+                    if constexpr (ROT == 1) fwht_unit(xf[0][k], lane, a.rot_block);
+                    else fwht_unit_fixed<ROT>(xf[0][k], lane);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) xf[k][i] = xf[k][i] * a.rot_scale;
+                    for (int i = 0; i < 8; ++i) xf[0][k][i] = xf[0][k][i] * a.rot_scale;
                 }
             }
         }
@@ -275,70 +280,84 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_planes_kernel(const LinearArg
 
         // 2) scales: per 128-column group (16 consecutive units = one row of
         //    16 lanes) or per token (a workgroup-wide maximum)
-        float us[XU], ur[XU];
+        float us[M][XU], ur[M][XU];
         if (GA) {
 #pragma unroll
-            for (int k = 0; k < XU; ++k) {
-                const int u = threadIdx.x + k * kThreads;
-                us[k] = row16_max_f32(absmax8(xf[k])) / 127.0f;
-                ur[k] = quant_recip(us[k]);
-                if (u < nunit && (u & 15) == 0) {
-                    sact[(u >> 4) * kMP] = us[k];
-                    if (blockIdx.x == 0) a.xs_out[u >> 4] = us[k];
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int k = 0; k < XU; ++k) {
+                    const int u = threadIdx.x + k * kThreads;
+                    us[m][k] = row16_max_f32(absmax8(xf[m][k])) / 127.0f;
+                    ur[m][k] = quant_recip(us[m][k]);
+                    if (u < nunit && (u & 15) == 0) {
+                        sact[(u >> 4) * kMP + m] = us[m][k];
+                        if (blockIdx.x == 0) a.xs_out[static_cast<size_t>(m) * G + (u >> 4)] = us[m][k];
+                    }
                 }
-            }
         } else {
-            float *part = sact;                 // [WAVES] scratch (no grouped table)
-            float am = 0.0f;
+            float *part = sact;                 // [M][WAVES] scratch (no grouped table)
 #pragma unroll
-            for (int k = 0; k < XU; ++k) am = fmaxf(am, absmax8(xf[k]));
-            am = wave_max_dpp_f32(am);
-            if (lane == 0) part[wave] = am;
+            for (int m = 0; m < M; ++m) {
+                float am = 0.0f;
+#pragma unroll
+                for (int k = 0; k < XU; ++k) am = fmaxf(am, absmax8(xf[m][k]));
+                am = wave_max_dpp_f32(am);
+                if (lane == 0) part[m * WAVES + wave] = am;
+            }
             __syncthreads();
-            // the per-wave maxima as 16-byte reads, all in flight together
+            // each token's per-wave maxima as 16-byte reads, all in flight
+            // together
             static_assert(WAVES % 4 == 0, "per-wave maxima are read four at a time");
-            float4 pm[WAVES / 4];
 #pragma unroll
-            for (int w = 0; w < WAVES / 4; ++w) pm[w] = reinterpret_cast<const float4 *>(part)[w];
-            am = fmaxf(fmaxf(pm[0].x, pm[0].y), fmaxf(pm[0].z, pm[0].w));
+            for (int m = 0; m < M; ++m) {
+                float4 pm[WAVES / 4];
 #pragma unroll
-            for (int w = 1; w < WAVES / 4; ++w)
-                am = fmaxf(am, fmaxf(fmaxf(pm[w].x, pm[w].y), fmaxf(pm[w].z, pm[w].w)));
-            tok_scale[0] = am / 127.0f;
-            const float r = quant_recip(tok_scale[0]);
-            if (blockIdx.x == 0 && threadIdx.x == 0) a.xs_out[0] = tok_scale[0];
+                for (int w = 0; w < WAVES / 4; ++w) pm[w] = reinterpret_cast<const float4 *>(part + m * WAVES)[w];
+                float am = fmaxf(fmaxf(pm[0].x, pm[0].y), fmaxf(pm[0].z, pm[0].w));
 #pragma unroll
-            for (int k = 0; k < XU; ++k) {
-                us[k] = tok_scale[0];
-                ur[k] = r;
+                for (int w = 1; w < WAVES / 4; ++w)
+                    am = fmaxf(am, fmaxf(fmaxf(pm[w].x, pm[w].y), fmaxf(pm[w].z, pm[w].w)));
+                tok_scale[m] = am / 127.0f;
+                const float r = quant_recip(tok_scale[m]);
+                if (blockIdx.x == 0 && threadIdx.x == 0) a.xs_out[m] = tok_scale[m];
+#pragma unroll
+                for (int k = 0; k < XU; ++k) {
+                    us[m][k] = tok_scale[m];
+                    ur[m][k] = r;
+                }
             }
         }
         // 3) codes -> LDS, unit u as the 8-byte [even | odd] pair (u & 1) of
-        //    half (u >> 1) & 1 of slot u >> 2; and to xq_out from workgroup 0
+        //    half (u >> 1) & 1 of slot u >> 2 of its token's row; and to
+        //    xq_out from workgroup 0
 #pragma unroll
-        for (int k = 0; k < XU; ++k) {
-            const int u = threadIdx.x + k * kThreads;
-            int cs = 0;
-            if (u < nunit) {
-                unsigned y[8];
-                quant_codes<8>(xf[k], us[k], ur[k], y);
-                unsigned char *dst = act + ((u >> 1) & 1) * row_bytes + (u >> 2) * 16 + (u & 1) * 8;
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_low_bytes(y[0], y[2], y[4], y[6]),
-                                                             pack_low_bytes(y[1], y[3], y[5], y[7]));
-                const unsigned c0 = pack_low_bytes(y[0], y[1], y[2], y[3]);
-                const unsigned c1 = pack_low_bytes(y[4], y[5], y[6], y[7]);
-                if (blockIdx.x == 0)
-                    *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(u) * 8) = make_uint2(c0, c1);
-                if (kSums) cs = sdot4(c1, 0x01010101u, sdot4(c0, 0x01010101u, 0));
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int k = 0; k < XU; ++k) {
+                const int u = threadIdx.x + k * kThreads;
+                int cs = 0;
+                if (u < nunit) {
+                    unsigned y[8];
+                    quant_codes<8>(xf[m][k], us[m][k], ur[m][k], y);
+                    unsigned char *dst = act + static_cast<size_t>(m) * K + ((u >> 1) & 1) * row_bytes + (u >> 2) * 16 +
+                                         (u & 1) * 8;
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_low_bytes(y[0], y[2], y[4], y[6]),
+                                                                 pack_low_bytes(y[1], y[3], y[5], y[7]));
+                    const unsigned c0 = pack_low_bytes(y[0], y[1], y[2], y[3]);
+                    const unsigned c1 = pack_low_bytes(y[4], y[5], y[6], y[7]);
+                    if (blockIdx.x == 0)
+                        *reinterpret_cast<uint2 *>(a.xq_out + static_cast<size_t>(m) * K + static_cast<size_t>(u) * 8) =
+                            make_uint2(c0, c1);
+                    if (kSums) cs = sdot4(c1, 0x01010101u, sdot4(c0, 0x01010101u, 0));
+                }
+                if (kSums) {
+                    // a group is 16 units = one row of 16 lanes
+                    cs = quad_sum_i32(cs);
+                    cs += dpp_i32<kDppRowRor4>(cs);
+                    cs += dpp_i32<kDppRowRor8>(cs);
+                    if (u < nunit && (u & 15) == 0) qsum[(u >> 4) * kMP + m] = cs;
+                }
             }
-            if (kSums) {
-                // a group is 16 units = one row of 16 lanes
-                cs = quad_sum_i32(cs);
-                cs += dpp_i32<kDppRowRor4>(cs);
-                cs += dpp_i32<kDppRowRor8>(cs);
-                if (u < nunit && (u & 15) == 0) qsum[(u >> 4) * kMP] = cs;
-            }
-        }
         __syncthreads();
     }
 
@@ -489,8 +508,22 @@ GemvKernel pick_fused_xu(bool grouped, int rot_block) {
                    : gemv_planes_kernel<PLANES, 1, false, false, D, kFusedWaves, XU, 0>;
 }
 
+// several tokens (M <= kFusedMaxTokens, one unit per thread, no rotation)
+template <int PLANES, int M>
+GemvKernel pick_fused_tokens(bool grouped) {
+    constexpr int D = items_in_flight<PLANES>();
+    return grouped ? gemv_planes_kernel<PLANES, M, true, false, D, kFusedWaves, 1, 0>
+                   : gemv_planes_kernel<PLANES, M, false, false, D, kFusedWaves, 1, 0>;
+}
+
 template <int PLANES>
-GemvKernel pick_fused(int K, bool grouped, int rot_block) {
+GemvKernel pick_fused(int M, int K, bool grouped, int rot_block) {
+    static_assert(kFusedMaxTokens == 4, "pick_fused covers up to four tokens");
+    if (M > 1) {
+        if (fused_units(K) > 1 || rot_block > 0) return nullptr;
+        return M == 2 ? pick_fused_tokens<PLANES, 2>(grouped)
+                      : M == 3 ? pick_fused_tokens<PLANES, 3>(grouped) : pick_fused_tokens<PLANES, 4>(grouped);
+    }
     const int xu = fused_units(K);
     return xu <= 1 ? pick_fused_xu<PLANES, 1>(grouped, rot_block)
                    : xu <= 2 ? pick_fused_xu<PLANES, 2>(grouped, rot_block)
@@ -515,7 +548,7 @@ hipError_t launch(const LinearArgs &a, bool exporting, bool fused, hipStream_t s
     const bool grouped = a.act_group == kGroup && !exporting;
     GemvKernel k;
     if (fused)
-        k = target ? pick_fused<2>(a.K, grouped, a.rot_block) : pick_fused<1>(a.K, grouped, a.rot_block);
+        k = target ? pick_fused<2>(a.M, a.K, grouped, a.rot_block) : pick_fused<1>(a.M, a.K, grouped, a.rot_block);
     else
         k = target ? pick_m<2>(a.M, grouped, exporting) : pick_m<1>(a.M, grouped, exporting);
     if (!k) return hipErrorInvalidValue;
@@ -554,7 +587,7 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
 }
 
 hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream) {
-    if (!fused_in_one_launch(a.M, a.K)) return hipErrorNotSupported;
+    if (!fused_in_one_launch(a.M, a.K, a.rot_block)) return hipErrorNotSupported;
     if (a.rot_block > 0 && (a.act_group != 0 || a.rot_block > kMaxRotBlock)) return hipErrorInvalidValue;
     return launch(a, false, true, stream);
 }
