@@ -17,6 +17,15 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       measures, and writes the JSON that bench.py reads (traffic per launch of
       the round's linear kernel, with the hash of the kernel sources).
 
+  python bench_profile.py counters DIR
+      DIR holds the output of one rocprofv3 --pmc pass (any counters) of
+      bench.py. Prints, per round shape and per batched-verify
+      instantiation, the mean of each counter per dispatch, and the derived
+      L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) and LDS bank conflicts
+      per access (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE -
+      SQ_LDS_BANK_CONFLICT), rocprofv3's LdsBankConflict) where the counters
+      are present.
+
   python bench_profile.py mfma DIR
       DIR holds the output of
         rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_VALU_MFMA_BUSY_CYCLES
@@ -52,17 +61,19 @@ LABELS = [
     (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 1, 0>", ["draft qkv", "draft gate_up"]),
     (r"^gemv_planes_kernel<1, 1, true, false, \d+, \d+, 1, 0>", ["draft o_proj"]),
     (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 4, 0>", ["draft down"]),
-    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 0, 0>", ["verify qkv", "verify gate_up", "verify down"]),
-    (r"^gemv_planes_kernel<2, 4, true, false, \d+, \d+, 0, 0>", ["verify o_proj"]),
-    (r"^quant_token_kernel<2>", ["quant qkv", "quant gate_up"]),
+    # the verify pass quantises inside the linear's launch at K = 4096 and
+    # takes a quantisation launch before down_proj's linear
+    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 1, 0>", ["verify qkv", "verify gate_up"]),
+    (r"^gemv_planes_kernel<2, 4, true, false, \d+, \d+, 1, 0>", ["verify o_proj"]),
+    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 0, 0>", ["verify down"]),
     (r"^quant_token_kernel<7>", ["quant down"]),
-    (r"^quant_group_kernel", ["quant o_proj"]),
 ]
 ROUND_SHAPES = ["draft qkv", "draft o_proj", "draft gate_up", "draft down",
                 "verify qkv", "verify o_proj", "verify gate_up", "verify down"]
 # launches of each linear shape per layer in one round: 3 draft passes, 1 verify pass
 ROUND_WEIGHT = {s: (3 if s.startswith("draft") else 1) for s in ROUND_SHAPES}
 KERNEL_SOURCES = ["w8_quantized_linear_amd/csrc/gemv_planes.hip",
+                  "w8_quantized_linear_amd/csrc/gemv_common.h",
                   "w8_quantized_linear_amd/csrc/device_common.h",
                   "w8_quantized_linear_amd/csrc/bitnest_internal.h"]
 
@@ -231,6 +242,40 @@ def cmd_mfma(directory: str):
             mean("SQ_INSTS_VALU_MFMA_I8"), busy, 100.0 * busy / (dur * CLOCK_GHZ)))
 
 
+def cmd_counters(directory: str):
+    rows = read_csv(directory, "counter_collection.csv")
+    names = sorted({r["Counter_Name"] for r in rows})
+    per = {}
+    for r in rows:
+        if "bitnest" not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {"row": r, "dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lab = label_rows([d["row"] for d in per.values()], lambda r: int(r["Dispatch_Id"]))
+    by_id = {d["row"]["Dispatch_Id"]: d for d in per.values()}
+    derived = []
+    if "TCC_HIT" in " ".join(names) and "TCC_MISS" in " ".join(names):
+        derived.append("L2 hit %")
+    if "SQ_LDS_BANK_CONFLICT" in names and "SQ_LDS_IDX_ACTIVE" in names:
+        derived.append("LDS conflicts per access")
+    print("| kernel / shape | dispatches | mean us | " + " | ".join(names + derived) + " |")
+    print("|---|---:|---:|" + "---:|" * (len(names) + len(derived)))
+    hit = next((n for n in names if n.startswith("TCC_HIT")), None)
+    miss = next((n for n in names if n.startswith("TCC_MISS")), None)
+    for k in sorted(lab):
+        ds = [by_id[r["Dispatch_Id"]] for r in lab[k]]
+        n = len(ds)
+        mean = lambda key: sum(d.get(key, 0.0) for d in ds) / n
+        cells = ["%.4g" % mean(c) for c in names]
+        if "L2 hit %" in derived:
+            h, m = mean(hit), mean(miss)
+            cells.append("%.1f" % (100.0 * h / (h + m)) if h + m else "-")
+        if "LDS conflicts per access" in derived:
+            c, a = mean("SQ_LDS_BANK_CONFLICT"), mean("SQ_LDS_IDX_ACTIVE")
+            cells.append("%.4f" % (c / (a - c)) if a > c else "-")
+        print("| %s | %d | %.2f | %s |" % (k, n, mean("dur_ns") / 1e3, " | ".join(cells)))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -243,11 +288,15 @@ def main(argv=None):
     c.add_argument("--copy-mib", type=int, default=256)
     m = sub.add_parser("mfma")
     m.add_argument("dir")
+    k = sub.add_parser("counters")
+    k.add_argument("dir")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         cmd_trace(a.dir)
     elif a.cmd == "mfma":
         cmd_mfma(a.dir)
+    elif a.cmd == "counters":
+        cmd_counters(a.dir)
     else:
         cmd_traffic(a.fetch_dir, a.write_dir, a.json, a.copy_mib)
 
