@@ -7,18 +7,20 @@ per-128-group activation scales, gate_up 28672x4096, down 4096x14336; the
 base model and the default draft length gamma = 3 of the BitNest-Llama-3-8B
 model card): three draft passes at M = 1 (hi plane only) and one target
 (verify) pass at M = gamma + 1 = 4 (hi and lo planes). Every linear is an
-activation quantisation followed by the nested linear, so one round is
-4 passes x 32 layers x 4 linears: 640 launches (one fused launch per draft
-linear, a quantisation launch and the linear per verify linear), replayed from
-one HIP graph. Weights are seeded synthetic tensors in the layout and with
+activation quantisation followed by the nested linear, 4 passes x 32 layers
+x 4 linears; the quantisation runs inside the linear's launch except for the
+verify pass's down_proj (K = 14336, four tokens), which takes a quantisation
+launch first: 544 launches per round, replayed from one HIP graph. Weights are seeded synthetic tensors in the layout and with
 the distributions of the weight package (generated on the GPU, 3.49 GB per
 plane, so the stream is far larger than the 256 MB Infinity Cache); they are
 resident in HBM before timing starts.
 
 Printed: one JSON line with the aggregate plane GB/s of the round (plane bytes
 read / time per round), the roofline of the dominant kernel (the
-plane-streaming GEMV, timed per launch with HIP events on the launch stream)
-and the CPU oracle's throughput on a bounded sample of the same work.
+plane-streaming GEMV, timed per launch with HIP events on the launch stream),
+the measured read ceiling per plane size, per-linear timings against it, the
+next rows' timings, and the CPU oracle's throughput (all host threads and
+one thread) on a bounded sample of the same work.
 """
 from __future__ import annotations
 

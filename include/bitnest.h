@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 6
+#define BITNEST_ABI_VERSION 7
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */

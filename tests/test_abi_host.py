@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bn.bitnest_abi_version() == 6
+    assert bn.bitnest_abi_version() == 7
     seen = set()
     for s in range(5):
         txt = bn.bitnest_status_string(s)
