@@ -17,9 +17,13 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library
  *     allocates nothing, frees nothing, keeps no pointer after returning, holds
- *     no per-call state and never synchronises. Work is enqueued on `stream`
- *     (a hipStream_t passed as void*; NULL is the default stream); results are
- *     ready when that stream reaches the point of the call.
+ *     no per-call state (the one exception: the scratch array of
+ *     bitnest_greedy_accept_noalloc, below) and never synchronises. Work is
+ *     enqueued on `stream` (a hipStream_t passed as void*; NULL is the default
+ *     stream); results are ready when that stream reaches the point of the
+ *     call.
+ *   - Every call works on the calling thread's current HIP device (the one
+ *     hipGetDevice returns): the tensors and the stream must belong to it.
  *   - Tensors are row-major and contiguous. Every tensor pointer must be
  *     16-byte aligned.
  *   - Sizes: 0 <= M <= BITNEST_MAX_M, 0 <= N, 128 <= K <= BITNEST_MAX_K, K a
@@ -38,7 +42,9 @@
  *     A fault inside a kernel surfaces at the caller's next synchronisation
  *     of the stream, as for any HIP kernel.
  *   - Outputs must not overlap inputs.
- *   - Calls are reentrant; calls on different streams may run concurrently.
+ *   - Calls are reentrant; calls on different streams may run concurrently,
+ *     except two bitnest_greedy_accept_noalloc calls on one device, which
+ *     share that device's scratch, and two calls that share a workspace.
  *   - Nothing throws across this boundary.
  */
 #ifndef BITNEST_H

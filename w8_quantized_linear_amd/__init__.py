@@ -100,8 +100,18 @@ def bitnest_status_string(status: int) -> str:
     return lib().bitnest_status_string(int(status)).decode()
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+def _stream(t: torch.Tensor, *others):
+    """torch's current stream of t's device, after checking that every tensor
+    of the call is on that device and that it is the current device (the
+    library works on the calling thread's current device)."""
+    dev = t.device
+    for o in others:
+        if o is not None and o.device != dev:
+            raise ValueError("all tensors of a call must be on one device, got %s and %s" % (dev, o.device))
+    if torch.cuda.current_device() != dev.index:
+        raise ValueError("the tensors are on %s but the current device is cuda:%d; call under "
+                         "torch.cuda.device(%s)" % (dev, torch.cuda.current_device(), dev))
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def _need(t: torch.Tensor, name: str, dtype, shape=None):
@@ -146,7 +156,8 @@ def bitnest_quant_act(x: torch.Tensor, act_group: int = 0, xq: torch.Tensor | No
         xs = torch.empty((M,) if act_group == 0 else (M, K // GROUP), dtype=torch.float32, device=x.device)
     _need(xq, "xq", torch.int8, (M, K))
     _need(xs, "xs", torch.float32, (M,) if act_group == 0 else (M, K // GROUP))
-    _call(lib().bitnest_quant_act(_p(x), M, K, act_group, _p(xq), _p(xs), _stream(x)), "bitnest_quant_act")
+    _call(lib().bitnest_quant_act(_p(x), M, K, act_group, _p(xq), _p(xs), _stream(x, xq, xs)),
+          "bitnest_quant_act")
     return xq, xs
 
 
@@ -173,7 +184,7 @@ def bitnest_linear_draft(xq: torch.Tensor, xs: torch.Tensor, hi: torch.Tensor, s
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
     _need(y, "y", torch.float32, (M, N))
     _call(lib().bitnest_linear_draft(_p(xq), _p(xs), act_group, _p(hi), _p(scale), _p(y), M, N, K,
-                                     _stream(xq)), "bitnest_linear_draft")
+                                     _stream(xq, xs, hi, scale, y)), "bitnest_linear_draft")
     return y
 
 
@@ -188,7 +199,7 @@ def bitnest_linear_target(xq: torch.Tensor, xs: torch.Tensor, hi: torch.Tensor, 
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
     _need(y, "y", torch.float32, (M, N))
     _call(lib().bitnest_linear_target(_p(xq), _p(xs), act_group, _p(hi), _p(lo), _p(scale), _p(y),
-                                      M, N, K, _stream(xq)), "bitnest_linear_target")
+                                      M, N, K, _stream(xq, xs, hi, lo, scale, y)), "bitnest_linear_target")
     return y
 
 
@@ -208,7 +219,7 @@ def bitnest_linear_partials(xq: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor
         p_lo = torch.empty_like(p_hi)
         p8 = torch.empty_like(p_hi)
     _call(lib().bitnest_linear_partials(_p(xq), _p(hi), _p(lo), _p(p_hi), _p(p_lo), _p(p8), M, N, K,
-                                        _stream(xq)), "bitnest_linear_partials")
+                                        _stream(xq, hi, lo, p_hi, p_lo, p8)), "bitnest_linear_partials")
     return p_hi if lo is None else (p_hi, p_lo, p8)
 
 
@@ -232,7 +243,7 @@ def bitnest_hadamard_quant_act(x: torch.Tensor, block: int, xq: torch.Tensor | N
     _need(xs, "xs", torch.float32, (M,))
     if xr is not None:
         _need(xr, "xr", torch.float32, (M, K))
-    _call(lib().bitnest_hadamard_quant_act(_p(x), M, K, int(block), _p(xq), _p(xs), _p(xr), _stream(x)),
+    _call(lib().bitnest_hadamard_quant_act(_p(x), M, K, int(block), _p(xq), _p(xs), _p(xr), _stream(x, xq, xs, xr)),
           "bitnest_hadamard_quant_act")
     return (xq, xs) if xr is None else (xq, xs, xr)
 
@@ -262,16 +273,17 @@ def _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, what, block=0):
     if block:
         if lo is None:
             st = lib().bitnest_hadamard_quant_linear_draft(_p(x), int(block), _p(hi), _p(scale), _p(y), _p(xq),
-                                                           _p(xs), M, N, K, _stream(x))
+                                                           _p(xs), M, N, K, _stream(x, hi, scale, y, xq, xs))
         else:
             st = lib().bitnest_hadamard_quant_linear_target(_p(x), int(block), _p(hi), _p(lo), _p(scale), _p(y),
-                                                            _p(xq), _p(xs), M, N, K, _stream(x))
+                                                            _p(xq), _p(xs), M, N, K,
+                                                            _stream(x, hi, lo, scale, y, xq, xs))
     elif lo is None:
         st = lib().bitnest_quant_linear_draft(_p(x), act_group, _p(hi), _p(scale), _p(y), _p(xq), _p(xs),
-                                              M, N, K, _stream(x))
+                                              M, N, K, _stream(x, hi, scale, y, xq, xs))
     else:
         st = lib().bitnest_quant_linear_target(_p(x), act_group, _p(hi), _p(lo), _p(scale), _p(y), _p(xq),
-                                               _p(xs), M, N, K, _stream(x))
+                                               _p(xs), M, N, K, _stream(x, hi, lo, scale, y, xq, xs))
     _call(st, what)
     return y, xq, xs
 
@@ -337,7 +349,8 @@ def bitnest_pack_nested(W: torch.Tensor, hi: torch.Tensor | None = None, lo: tor
     _need(hi, "hi", torch.uint8, (N, K // 2))
     _need(lo, "lo", torch.uint8, (N, K // 2))
     _need(scale, "scale", torch.int16, (N, K // GROUP))
-    _call(lib().bitnest_pack_nested(_p(W), N, K, _p(hi), _p(lo), _p(scale), _stream(W)), "bitnest_pack_nested")
+    _call(lib().bitnest_pack_nested(_p(W), N, K, _p(hi), _p(lo), _p(scale), _stream(W, hi, lo, scale)),
+          "bitnest_pack_nested")
     return hi, lo, scale
 
 
@@ -367,7 +380,8 @@ def bitnest_greedy_accept(logits: torch.Tensor, draft: torch.Tensor, targ: torch
         work = torch.empty((max(need, 16),), dtype=torch.uint8, device=logits.device)
     _need(work, "work", work.dtype)
     _call(lib().bitnest_greedy_accept(_p(logits), R, V, _p(draft) if R > 1 else None, _p(targ), _p(result),
-                                      _p(work), work.numel() * work.element_size(), _stream(logits)),
+                                      _p(work), work.numel() * work.element_size(),
+                                      _stream(logits, draft, targ, result, work)),
           "bitnest_greedy_accept")
     return targ, result
 
@@ -389,7 +403,7 @@ def bitnest_greedy_accept_noalloc(logits: torch.Tensor, draft: torch.Tensor, tar
     _need(targ, "targ", torch.int32, (R,))
     _need(result, "result", torch.int32, (2,))
     _call(lib().bitnest_greedy_accept_noalloc(_p(logits), R, V, _p(draft) if R > 1 else None, _p(targ),
-                                              _p(result), _stream(logits)),
+                                              _p(result), _stream(logits, draft, targ, result)),
           "bitnest_greedy_accept_noalloc")
     return targ, result
 
@@ -406,7 +420,7 @@ def bitnest_stream_read(buf: torch.Tensor, sink: torch.Tensor, never: int = 0x5E
     _need(sink, "sink", torch.int32)
     nbytes = buf.numel() * buf.element_size()
     _call(lib().bitnest_stream_read(_p(buf), nbytes, depth, waves_per_cu, never & 0xFFFFFFFF, _p(sink),
-                                    _stream(buf)), "bitnest_stream_read")
+                                    _stream(buf, sink)), "bitnest_stream_read")
 
 
 KV_HEAD_DIM = 128
@@ -464,7 +478,8 @@ def bitnest_kv_attention(q: torch.Tensor, k_hi: torch.Tensor, k_scale: torch.Ten
     _need(work, "work", work.dtype)
     _call(lib().bitnest_kv_attention(_p(q), M, Hq, Hkv, T, t_cap, _p(k_hi), _p(k_lo), _p(k_scale), _p(v_hi),
                                      _p(v_lo), _p(v_scale), _p(out), _p(work), work.numel() * work.element_size(),
-                                     _stream(q)), "bitnest_kv_attention")
+                                     _stream(q, k_hi, k_lo, k_scale, v_hi, v_lo, v_scale, out, work)),
+          "bitnest_kv_attention")
     return out
 
 
@@ -523,6 +538,9 @@ class LinearChain:
             if xq is not None:
                 _need(xq, "xq", torch.int8, (M, K))
                 _need(xs, "xs", torch.float32, (M,) if g == 0 else (M, K // GROUP))
+            for name, t in (("x", x), ("hi", hi), ("lo", lo), ("scale", scale), ("y", y), ("xq", xq), ("xs", xs)):
+                if t is not None and t.device != self.device:
+                    raise ValueError("link %d: %s is on %s, the chain runs on %s" % (j, name, t.device, self.device))
             host[j] = ChainLink(x.data_ptr(), hi.data_ptr(), None if lo is None else lo.data_ptr(),
                                 scale.data_ptr(), y.data_ptr(), None if xq is None else xq.data_ptr(),
                                 None if xs is None else xs.data_ptr(), N, K, g, 0)
@@ -534,6 +552,8 @@ class LinearChain:
         if work is None:
             work = torch.zeros((nbytes,), dtype=torch.uint8, device=self.device)
         _need(work, "work", torch.uint8)
+        if work.device != self.device:
+            raise ValueError("work is on %s, the chain runs on %s" % (work.device, self.device))
         if work.numel() < nbytes:
             raise ValueError("work must hold %d bytes" % nbytes)
         self.work = work
