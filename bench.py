@@ -9,8 +9,9 @@ model card): three draft passes at M = 1 (hi plane only) and one target
 (verify) pass at M = gamma + 1 = 4 (hi and lo planes). Every linear is an
 activation quantisation followed by the nested linear, 4 passes x 32 layers
 x 4 linears; the quantisation runs inside the linear's launch except for the
-verify pass's down_proj (K = 14336, four tokens), which takes a quantisation
-launch first: 544 launches per round, replayed from one HIP graph. Weights are seeded synthetic tensors in the layout and with
+verify pass's gate_up and down_proj (four tokens; N = 28672, K = 14336), which
+take a quantisation launch first: 576 launches per round, replayed from one
+HIP graph. Weights are seeded synthetic tensors in the layout and with
 the distributions of the weight package (generated on the GPU, 3.49 GB per
 plane, so the stream is far larger than the 256 MB Infinity Cache); they are
 resident in HBM before timing starts.
@@ -128,7 +129,7 @@ class Stack:
             for (_, N, K, g) in self.linears:
                 S = 1 if g == 0 else K // 128
                 b = planes * N * K // 2 + N * (K // 128) * 2 + M * N * 4
-                if bn.fused_in_one_launch(M, K):
+                if bn.fused_in_one_launch(M, N, K):
                     b += 4 * M * K + M * K + 4 * M * S
                 else:
                     b += M * K + 4 * M * S
@@ -173,7 +174,7 @@ def run_round(stack, bn, mode="fused", rot_block=0):
                 xq, xs, y = stack.buf[(M, i)]
                 w = stack.w[l][i]
                 x = stack.x_verify[l][i] if verify else stack.x_draft[p][l][i]
-                one = bn.fused_in_one_launch(M, K)
+                one = bn.fused_in_one_launch(M, N, K)
                 if rot_block and mode == "fused" and name == "down":
                     if verify:
                         bn.bitnest_hadamard_quant_linear_target(x, rot_block, w.hi, w.lo, w.scale, y=y, xq=xq, xs=xs)
@@ -293,7 +294,9 @@ def per_linear(stack, bn, ceiling=None, reps=5):
     measured read ceiling at the same number of bytes. Modes: draft M=1 and
     target M=1 (the fused call, one launch), target M=4 (the linear on ready
     codes; its separate quantisation launch is timed on its own as
-    quant_M4, one launch per layer)."""
+    quant_M4, one launch per layer), and verify_M4: the fused call at M=4 as
+    the round makes it where that is one launch (K <= 4096: qkv, o_proj,
+    gate_up)."""
     import torch
     out = {}
     L = stack.layers
@@ -312,10 +315,12 @@ def per_linear(stack, bn, ceiling=None, reps=5):
             ts.append(e0.elapsed_time(e1) * 1e-3 / n)
         return sorted(ts)[len(ts) // 2]
 
-    for mode in ("draft_M1", "target_M1", "target_M4", "quant_M4"):
+    for mode in ("draft_M1", "target_M1", "target_M4", "quant_M4", "verify_M4"):
         res = {}
         for i, (name, N, K, g) in enumerate(stack.linears):
-            M = 4 if mode.endswith("M4") else 1
+            M = 4 if "M4" in mode else 1
+            if mode == "verify_M4" and not bn.fused_in_one_launch(M, N, K):
+                continue
             xq, xs, y = stack.buf[(M, i)]
 
             planes = 1 if mode == "draft_M1" else 2
@@ -333,6 +338,9 @@ def per_linear(stack, bn, ceiling=None, reps=5):
                                                        y=y, xq=xq, xs=xs)
                     elif mode == "target_M4":
                         bn.bitnest_linear_target(xq, xs, w.hi, w.lo, w.scale, g, y=y)
+                    elif mode == "verify_M4":
+                        bn.bitnest_quant_linear_target(stack.x_verify[l % L][i], w.hi, w.lo, w.scale, g,
+                                                       y=y, xq=xq, xs=xs)
                     else:
                         bn.bitnest_quant_act(stack.x_verify[l][i], g, xq=xq, xs=xs)
             if mode == "target_M4":

@@ -61,11 +61,13 @@ LABELS = [
     (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 1, 0>", ["draft qkv", "draft gate_up"]),
     (r"^gemv_planes_kernel<1, 1, true, false, \d+, \d+, 1, 0>", ["draft o_proj"]),
     (r"^gemv_planes_kernel<1, 1, false, false, \d+, \d+, 4, 0>", ["draft down"]),
-    # the verify pass quantises inside the linear's launch at K = 4096 and
-    # takes a quantisation launch before down_proj's linear
-    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 1, 0>", ["verify qkv", "verify gate_up"]),
+    # the verify pass quantises inside the linear's launch for qkv and o_proj
+    # and takes a quantisation launch before gate_up's and down_proj's
+    # linears
+    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 1, 0>", ["verify qkv"]),
     (r"^gemv_planes_kernel<2, 4, true, false, \d+, \d+, 1, 0>", ["verify o_proj"]),
-    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 0, 0>", ["verify down"]),
+    (r"^gemv_planes_kernel<2, 4, false, false, \d+, \d+, 0, 0>", ["verify gate_up", "verify down"]),
+    (r"^quant_token_kernel<2>", ["quant gate_up"]),
     (r"^quant_token_kernel<7>", ["quant down"]),
 ]
 ROUND_SHAPES = ["draft qkv", "draft o_proj", "draft gate_up", "draft down",

@@ -143,8 +143,8 @@ bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_
  * and y, bit for bit, as bitnest_quant_act(x, M, K, act_group, xq, xs, stream)
  * followed by bitnest_linear_draft(xq, xs, act_group, hi, scale, y, M, N, K,
  * stream). For one token up to K = 16384, and for up to four tokens up to
- * K = 4096, each workgroup quantises x itself and the whole linear is one
- * launch; otherwise the call makes the two launches.
+ * K = 4096 and N = 8192, each workgroup quantises x itself and the whole
+ * linear is one launch; otherwise the call makes the two launches.
  *   x    fp32 [M, K] input;  xq int8 [M, K], xs fp32 [M] or [M, K/128]:
  *        outputs, as written by bitnest_quant_act (always required)
  *   hi, scale, y as for bitnest_linear_draft (may be NULL when N == 0).

@@ -381,8 +381,9 @@ FUSED_SHAPES = [(256, 512), (37, 640), (70, 2176), (33, 14336), (129, 4096), (17
 def test_fused_quant_linear_equals_two_calls(M, N, K, act_group, target):
     # One fused call must give the codes, scales and y of quant_act followed by
     # the linear, bit for bit (one launch for one token up to K = 16384 and
-    # for up to four tokens up to K = 4096, else two).
-    assert bn.fused_in_one_launch(M, K) == ((M == 1 and K <= 16384) or (M <= 4 and K <= 4096))
+    # for up to four tokens up to K = 4096 and N = 8192, else two).
+    one = (M == 1 and K <= 16384) or (M <= 4 and K <= 4096 and N <= 8192)
+    assert bn.fused_in_one_launch(M, N, K) == one
     w, x = _problem(M, N, K, seed=9)
     xd, hi, lo, sc = _dev(x), _dev(w.hi), _dev(w.lo), _dev(w.scale)
     xq, xs = bn.bitnest_quant_act(xd, act_group)

@@ -291,16 +291,17 @@ def _quant_linear(x, hi, lo, scale, act_group, y, xq, xs, what, block=0):
 FUSED_MAX_MK = 16384
 FUSED_MAX_TOKENS = 4
 FUSED_MAX_TOKENS_K = 4096
+FUSED_MAX_TOKENS_N = 8192
 
 
-def fused_in_one_launch(M: int, K: int, rot_block: int = 0) -> bool:
+def fused_in_one_launch(M: int, N: int, K: int, rot_block: int = 0) -> bool:
     """Whether bitnest_quant_linear_* (or, with rot_block, the rotating call)
     runs as a single kernel launch for this shape (otherwise it is a
     quantisation launch followed by the linear); the library's rule: one
-    token and K <= 16384, or up to four tokens and K <= 4096 without the
-    rotation."""
+    token and K <= 16384, or up to four tokens, K <= 4096 and N <= 8192
+    without the rotation."""
     return (M == 1 and K <= FUSED_MAX_MK) or (rot_block == 0 and 1 <= M <= FUSED_MAX_TOKENS
-                                              and K <= FUSED_MAX_TOKENS_K)
+                                              and K <= FUSED_MAX_TOKENS_K and N <= FUSED_MAX_TOKENS_N)
 
 
 def bitnest_quant_linear_draft(x: torch.Tensor, hi: torch.Tensor, scale: torch.Tensor, act_group: int = 0,

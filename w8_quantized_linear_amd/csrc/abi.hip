@@ -202,7 +202,7 @@ bitnest_status quant_linear(const float *x, int act_group, int rot_block, const 
     const float rs = rot_block ? rot_scale_of(rot_block) : 0.0f;
     bitnest::LinearArgs a{xq, xs, hi, lo, scale, y, nullptr, nullptr, nullptr, M, N, K, act_group, x, xq, xs,
                           rot_block, rs};
-    if (N > 0 && bitnest::fused_in_one_launch(M, K, rot_block))
+    if (N > 0 && bitnest::fused_in_one_launch(M, N, K, rot_block))
         return to_status(bitnest::launch_gemv_fused(a, s));
     if (rot_block)
         st = to_status(bitnest::launch_hadamard_quant_act(x, M, K, rot_block, rs, xq, xs, nullptr, s));

@@ -115,12 +115,16 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
 // linear launch.
 constexpr int kFusedMaxMK = 16384;
 // Several tokens fit one launch when each thread holds one 8-column unit of
-// every token (K <= 8 units x 512 threads), without the rotation.
+// every token (K <= 8 units x 512 threads), without the rotation, and when a
+// wave has few rows: the one-launch grid is one 8-wave workgroup per CU, and
+// with many rows per wave (gate_up's 28672 over 2048 waves) the two-launch
+// linear, sized by occupancy, streams faster than the saved launch is worth.
 constexpr int kFusedMaxTokens = 4;
 constexpr int kFusedMaxTokensK = 4096;
-inline bool fused_in_one_launch(int M, int K, int rot_block) {
-    return (M == 1 && K <= kFusedMaxMK) ||
-           (rot_block == 0 && M >= 1 && M <= kFusedMaxTokens && K <= kFusedMaxTokensK);
+constexpr int kFusedMaxTokensN = 8192;
+inline bool fused_in_one_launch(int M, int N, int K, int rot_block) {
+    return (M == 1 && K <= kFusedMaxMK) || (rot_block == 0 && M >= 1 && M <= kFusedMaxTokens &&
+                                            K <= kFusedMaxTokensK && N <= kFusedMaxTokensN);
 }
 hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream);
 

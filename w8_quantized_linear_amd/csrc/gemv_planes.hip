@@ -72,8 +72,9 @@ struct GemvLds {
 
 // PLANES: 1 draft (hi), 2 target (hi + lo). GA: per-128-group activation
 // scales. EXPORT: write the integer partials instead of y. D: items in flight
-// per wave. WAVES: waves per workgroup. XU: 0, or (one token only) quantise
-// the fp32 input in the prologue, XU 8-column units per thread. ROT (with XU):
+// per wave. WAVES: waves per workgroup. XU: 0, or quantise the fp32 input in
+// the prologue, XU 8-column units per thread and token (several tokens only
+// with XU = 1 and no rotation). ROT (with XU):
 // 0, or apply the R4 rotation (blocks of a.rot_block columns, times
 // a.rot_scale) to the fp32 input before quantising it: ROT = 1 takes the
 // block size from a.rot_block, any other value is that block size fixed when
@@ -587,7 +588,7 @@ hipError_t launch_gemv(const LinearArgs &a, bool export_partials, hipStream_t st
 }
 
 hipError_t launch_gemv_fused(const LinearArgs &a, hipStream_t stream) {
-    if (!fused_in_one_launch(a.M, a.K, a.rot_block)) return hipErrorNotSupported;
+    if (!fused_in_one_launch(a.M, a.N, a.K, a.rot_block)) return hipErrorNotSupported;
     if (a.rot_block > 0 && (a.act_group != 0 || a.rot_block > kMaxRotBlock)) return hipErrorInvalidValue;
     return launch(a, false, true, stream);
 }
