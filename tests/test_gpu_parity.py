@@ -371,7 +371,8 @@ def test_llama_layer_full_size(llama_layer, M, target):
 
 # --------------------------------------------------------------------------- fused quant + linear
 
-FUSED_SHAPES = [(256, 512), (37, 640), (70, 2176), (33, 14336), (129, 4096), (17, 16384)]
+FUSED_SHAPES = [(256, 512), (37, 640), (70, 2176), (33, 14336), (129, 4096), (17, 16384), (9, 128), (300, 256),
+                (8192, 384)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
