@@ -6,8 +6,11 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       DIR holds the output of
         rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python -u bench.py ...
       Prints markdown tables: the --stats summary of the library's kernels,
-      the average duration over all gemv_planes_kernel dispatches, and
-      per-shape durations of the round's launches.
+      the average duration over all gemv_planes_kernel dispatches,
+      per-shape durations of the round's launches (mean, p10, median, p90,
+      min), and per round the sum of its dispatch durations against the
+      span from its first start to its last end (--layers: the run's layer
+      count, default 32).
 
   python bench_profile.py traffic FETCH_DIR WRITE_DIR [--json PATH]
       The two directories hold
@@ -49,6 +52,7 @@ import glob
 import gzip
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -118,7 +122,30 @@ def label_rows(rows, order_key):
     return out
 
 
-def cmd_trace(directory: str):
+def quantile(v, q):
+    """Nearest-rank quantile of the sorted list v (0 < q < 1)."""
+    return v[min(len(v) - 1, max(0, math.ceil(q * len(v)) - 1))]
+
+
+def round_accounting(trace, layers):
+    """[(busy us, span us)] per round: the library dispatches in start order,
+    cut into rounds of 18 * layers launches from the first one while every
+    dispatch of a round is one of the round's kernels (LABELS)."""
+    rows = sorted((r for r in trace if "bitnest" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    n = 18 * layers
+    out = []
+    for i in range(0, len(rows) - n + 1, n):
+        chunk = rows[i:i + n]
+        if not all(any(re.match(p, short(r["Kernel_Name"])) for p, _ in LABELS) for r in chunk):
+            break
+        starts = [int(r["Start_Timestamp"]) for r in chunk]
+        ends = [int(r["End_Timestamp"]) for r in chunk]
+        busy = sum(e - b for b, e in zip(starts, ends)) / 1e3
+        out.append((busy, (max(ends) - min(starts)) / 1e3))
+    return out
+
+
+def cmd_trace(directory: str, layers: int = 32):
     stats = read_csv(directory, "kernel_stats.csv")
     print("## rocprofv3 --stats (kernel_stats.csv, library kernels)\n")
     print("| kernel | calls | average ns | total ns |")
@@ -139,11 +166,23 @@ def cmd_trace(directory: str):
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     lab = label_rows(trace, lambda r: int(r["Start_Timestamp"]))
     print("## Per shape (kernel_trace.csv)\n")
-    print("| shape | dispatches | mean us | median us | min us |")
-    print("|---|---:|---:|---:|---:|")
+    print("| shape | dispatches | mean us | p10 us | median us | p90 us | min us |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
     for k in sorted(lab):
         v = sorted(dur(r) for r in lab[k])
-        print("| %s | %d | %.3f | %.3f | %.3f |" % (k, len(v), sum(v) / len(v), v[len(v) // 2], v[0]))
+        print("| %s | %d | %.3f | %.3f | %.3f | %.3f | %.3f |"
+              % (k, len(v), sum(v) / len(v), quantile(v, 0.1), quantile(v, 0.5), quantile(v, 0.9), v[0]))
+    rounds = round_accounting(trace, layers)
+    if rounds:
+        print("\n## Rounds (kernel_trace.csv)\n")
+        print("The first %d x %d dispatches, taken in rounds of %d (%d layers x 18: three draft passes of 4 "
+              "linears, 4 verify linears and 2 verify quantisation launches); round 0 is the eager run on the "
+              "capture stream, the others are graph replays. busy = sum of the round's dispatch durations, "
+              "span = first start to last end.\n" % (len(rounds), 18 * layers, 18 * layers, layers))
+        print("| round | busy ms | span ms | span - busy, us per launch |")
+        print("|---|---:|---:|---:|")
+        for i, (busy, span) in enumerate(rounds):
+            print("| %d | %.3f | %.3f | %.3f |" % (i, busy / 1e3, span / 1e3, (span - busy) / (18 * layers)))
 
 
 def copy_factor(rows, counter: str, copy_bytes: float):
@@ -283,6 +322,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("dir")
+    t.add_argument("--layers", type=int, default=32, help="layers of the profiled bench.py run")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
@@ -294,7 +334,7 @@ def main(argv=None):
     k.add_argument("dir")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        cmd_trace(a.dir)
+        cmd_trace(a.dir, a.layers)
     elif a.cmd == "mfma":
         cmd_mfma(a.dir)
     elif a.cmd == "counters":

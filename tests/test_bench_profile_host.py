@@ -1,0 +1,107 @@
+"""The profile summariser (bench_profile.py) on a synthetic rocprofv3 trace:
+dispatches in the round's launch order with known durations, so the shape
+labels, the quantiles and the per-round accounting can be checked exactly."""
+import csv
+import io
+import os
+import sys
+from contextlib import redirect_stdout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench_profile as bp  # noqa: E402
+
+NS = "void bitnest::(anonymous namespace)::"
+GEMV = NS + "gemv_planes_kernel<%s>(bitnest::LinearArgs)"
+QUANT = NS + "quant_token_kernel<%d>(float const*, int, signed char*, float*)"
+
+# (kernel name, label, duration ns) of one layer of one round, in launch order
+DRAFT = [(GEMV % "1, 1, false, false, 4, 8, 1, 0", "draft qkv", 4800),
+         (GEMV % "1, 1, true, false, 4, 8, 1, 0", "draft o_proj", 4000),
+         (GEMV % "1, 1, false, false, 4, 8, 1, 0", "draft gate_up", 11500),
+         (GEMV % "1, 1, false, false, 4, 8, 4, 0", "draft down", 7800)]
+VERIFY = [(GEMV % "2, 4, false, false, 2, 8, 1, 0", "verify qkv", 9400),
+          (GEMV % "2, 4, true, false, 2, 8, 1, 0", "verify o_proj", 7800),
+          (QUANT % 2, "quant gate_up", 3000),
+          (GEMV % "2, 4, false, false, 2, 8, 0, 0", "verify gate_up", 22200),
+          (QUANT % 7, "quant down", 4500),
+          (GEMV % "2, 4, false, false, 2, 8, 0, 0", "verify down", 13000)]
+GAP = 250
+
+
+def launches(layers, rounds):
+    seq = []
+    for r in range(rounds):
+        for p in range(4):
+            for _ in range(layers):
+                seq.extend(VERIFY if p == 3 else DRAFT)
+    # the batched-verify section that follows the rounds
+    seq.append((NS + "verify_mfma_kernel<2, 1, false, false, 1>(bitnest::LinearArgs, int)", "mfma", 16000))
+    seq.append((QUANT % 2, "quant gate_up", 3000))
+    return seq
+
+
+def write_trace(d, seq, jitter):
+    t = 1_000_000
+    rows = []
+    for i, (name, _, ns) in enumerate(seq):
+        ns += jitter(i)
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + ns})
+        t += ns + GAP
+    with open(os.path.join(d, "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    with open(os.path.join(d, "run_kernel_stats.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "TotalDurationNs"])
+        w.writeheader()
+        w.writerow({"Name": GEMV % "1, 1, false, false, 4, 8, 1, 0", "Calls": 2, "AverageNs": 5000.0,
+                    "TotalDurationNs": 10000})
+
+
+def test_quantile_is_nearest_rank():
+    v = list(range(1, 11))
+    assert bp.quantile(v, 0.1) == 1 and bp.quantile(v, 0.5) == 5 and bp.quantile(v, 0.9) == 9
+    assert bp.quantile([7], 0.1) == 7 and bp.quantile([7], 0.9) == 7
+    w = list(range(1, 12))
+    assert bp.quantile(w, 0.5) == 6 and bp.quantile(w, 0.9) == 10
+
+
+def test_labels_follow_the_round_launch_order(tmp_path):
+    layers, rounds = 2, 3
+    seq = launches(layers, rounds)
+    write_trace(tmp_path, seq, lambda i: 0)
+    trace = bp.read_csv(str(tmp_path), "kernel_trace.csv")
+    lab = bp.label_rows(trace, lambda r: int(r["Start_Timestamp"]))
+    want = {}
+    for name, label, ns in seq:
+        if label != "mfma":
+            want.setdefault(label, set()).add(ns)
+    for label, durs in want.items():
+        got = {int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in lab[label]}
+        assert got == durs, label
+    assert len(lab["draft qkv"]) == 3 * layers * rounds
+    assert len(lab["verify down"]) == layers * rounds
+    assert len(lab["verify_mfma_kernel<2, 1, false, false, 1>"]) == 1
+
+
+def test_round_accounting(tmp_path):
+    layers, rounds = 2, 3
+    seq = launches(layers, rounds)
+    write_trace(tmp_path, seq, lambda i: i % 3)     # a few ns of jitter, known per dispatch
+    trace = bp.read_csv(str(tmp_path), "kernel_trace.csv")
+    got = bp.round_accounting(trace, layers)
+    assert len(got) == rounds                        # stops at the batched-verify section
+    n = 18 * layers
+    for r, (busy, span) in enumerate(got):
+        idx = range(r * n, (r + 1) * n)
+        want_busy = sum(seq[i][2] + i % 3 for i in idx)
+        assert abs(busy * 1e3 - want_busy) < 1e-6
+        assert abs(span * 1e3 - (want_busy + (n - 1) * GAP)) < 1e-6
+    out = io.StringIO()
+    with redirect_stdout(out):
+        bp.cmd_trace(str(tmp_path), layers)
+    text = out.getvalue()
+    assert "| shape | dispatches | mean us | p10 us | median us | p90 us | min us |" in text
+    assert "## Rounds" in text and "| 2 |" in text
