@@ -5,12 +5,13 @@ the kernels address a plane with 32-bit byte offsets. At K = 16384 that is
 N = 262143 rows (2,147,475,456 bytes per plane); one row more is refused
 before any launch. Every path is run at that size: the single-token fused
 draft and target, the four-token target GEMV, the batched target and draft
-on the matrix cores (one and two token tiles), and the partials export of
-both kernel families. The rows checked against the oracle are a spread over
+on the matrix cores (one and two token tiles), the partials export of
+both kernel families, and the offline packer (whose fp32 input then has more
+than 2^32 elements). The rows checked against the oracle are a spread over
 the whole plane plus the last 64 rows, whose offsets come closest to the
 limit; y within 1e-5 * max|y| of the fp64 oracle (BitNest-Llama-3-8B model
-card, "Files", planes.safetensors: W4 and W8 dequantisation), codes, scales
-and partials exact.
+card, "Files", planes.safetensors: W4 and W8 dequantisation), codes, scales,
+partials and packed planes exact.
 """
 import ctypes
 
@@ -102,3 +103,23 @@ def test_largest_plane_partials_exact(big, M):
         assert np.array_equal(got[:, ridx].cpu().numpy(), want)
     del p
     torch.cuda.empty_cache()
+
+
+def test_largest_plane_pack_bit_exact():
+    # the offline packer over fp32 weights [N, K] with N * K / 2 just under
+    # 2^31 (about 4.3e9 weights, 17 GB of input: element offsets beyond 32
+    # bits); sampled rows bit for bit against the oracle's packing
+    g = torch.Generator(device="cuda")
+    g.manual_seed(43)
+    W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32)
+    W[N - 1, :128] = 0.0                        # an all-zero group in the last row
+    hi, lo, sc = bn.bitnest_pack_nested(W)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.linspace(0, N - 1, 64).astype(int), np.arange(N - 16, N)]))
+    ridx = torch.from_numpy(rows).cuda()
+    want = oracle.pack_nested(W[ridx].cpu().numpy())
+    del W
+    torch.cuda.empty_cache()
+    assert np.array_equal(hi[ridx].cpu().numpy(), want[0])
+    assert np.array_equal(lo[ridx].cpu().numpy(), want[1])
+    assert np.array_equal(sc[ridx].cpu().numpy().view(np.uint16), want[2])
