@@ -115,6 +115,36 @@ def test_kv_attention_reads_only_the_first_t_positions_of_each_head(M, T, t_cap,
     _check(got, want, _vmax(vc, kv8))
 
 
+@pytest.mark.parametrize("kv8", [False, True])
+def test_kv_attention_head_bases_beyond_2_31(kv8):
+    # t_cap so large that heads 4..7 start more than 2^31 bytes into their
+    # planes (head h at h * t_cap * 64 bytes); only the first T positions of
+    # each head are read. The cache is built on the GPU; positions past T
+    # hold codes and scales that would dominate the result if read.
+    M, Hq, Hkv, T = 4, 32, 8, 3000
+    t_cap = (1 << 31) // (64 * 4) + 1000
+    assert 4 * t_cap * 64 > 2**31 - 1 and T * 64 < 2**31
+    kc, vc = _cache(T, Hkv, seed=77)
+    q = np.random.default_rng(77).standard_normal((M, Hq, 128)).astype(np.float32)
+
+    def d(a, fill, dtype):
+        out = torch.full((Hkv, t_cap) + a.shape[2:], fill, dtype=dtype, device="cuda")
+        out[:, :T] = torch.from_numpy(np.ascontiguousarray(np.swapaxes(a, 0, 1)).view(dtype_np[dtype])).cuda()
+        return out
+
+    dtype_np = {torch.uint8: np.uint8, torch.int16: np.int16}
+    big = 0x7B53                    # fp16 60000 (its bit pattern fits int16)
+    out = bn.bitnest_kv_attention(torch.from_numpy(q).cuda(),
+                                  d(kc[0], 0xFF, torch.uint8), d(kc[2], big, torch.int16),
+                                  d(vc[0], 0xFF, torch.uint8), d(vc[2], big, torch.int16),
+                                  d(kc[1], 0xFF, torch.uint8) if kv8 else None,
+                                  d(vc[1], 0xFF, torch.uint8) if kv8 else None, T=T)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    torch.cuda.empty_cache()
+    _check(got, _ref(q, kc, vc, kv8), _vmax(vc, kv8))
+
+
 def test_kv_peaked_scores():
     # large scores (sharp softmax) stay accurate
     kc, vc = _cache(512, 8, seed=7, spread=3.0)
