@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BITNEST_ABI_VERSION 7
+#define BITNEST_ABI_VERSION 8
 #define BITNEST_GROUP 128      /* columns per weight scale (and per o_proj act scale) */
 #define BITNEST_MAX_M 32       /* most tokens per call */
 #define BITNEST_MAX_K 16384    /* largest input width */
@@ -327,7 +327,9 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K,
  *     n       = length of the longest prefix with draft[r] == targ[r]
  *     result  = {n, targ[n]}            the round emits draft[0 .. n-1], then targ[n]
  *
- *   logits  fp32 [R, V], R = gamma + 1 (1 <= R <= BITNEST_MAX_M), V >= 1, finite
+ *   logits  fp32 [R, V], R = gamma + 1 (1 <= R <= BITNEST_MAX_M),
+ *           1 <= V <= BITNEST_ACCEPT_MAX_V (column indices and slice bounds
+ *           are 32-bit; a larger V gives BITNEST_EUNSUPPORTED), finite
  *   draft   int32 [R - 1] (may be NULL when R == 1)
  *   targ    int32 [R], written;  result int32 [2], written
  *   work    caller-owned scratch of at least
@@ -335,7 +337,8 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K,
  *           8 bytes per row and slice of about 4096 logits, at most 64 slices),
  *           overwritten; 16-byte aligned
  */
-size_t bitnest_greedy_accept_workspace_bytes(int R, int V);
+#define BITNEST_ACCEPT_MAX_V (1 << 30)   /* most logits per row */
+size_t bitnest_greedy_accept_workspace_bytes(int R, int V);   /* 0 if R or V is out of range */
 
 bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft,
                                      int32_t *targ, int32_t *result, void *work, size_t work_bytes,

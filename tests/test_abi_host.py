@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bn.bitnest_abi_version() == 7
+    assert bn.bitnest_abi_version() == 8
     seen = set()
     for s in range(5):
         txt = bn.bitnest_status_string(s)
@@ -221,6 +221,8 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _ga(A, 0, 100, B, C, D), bn.EINVAL),
     (lambda: _ga(A, 4, 0, B, C, D), bn.EINVAL),
     (lambda: _ga(A, 33, 100, B, C, D), bn.EUNSUPPORTED),
+    (lambda: _ga(A, 4, (1 << 30) + 1, B, C, D), bn.EUNSUPPORTED),
+    (lambda: _ga(A, 4, 2 ** 31 - 1, B, C, D), bn.EUNSUPPORTED),
     (lambda: _ga(NUL, 4, 100, B, C, D), bn.EINVAL),
     (lambda: _ga(A, 4, 100, NUL, C, D), bn.EINVAL),
     (lambda: _ga(A, 4, 100, B, NUL, D), bn.EINVAL),
@@ -234,6 +236,7 @@ def _ht(x, b, hi, lo, sc, y, xq, xs, M, N, K):
     (lambda: _gn(A, 0, 100, B, C, D), bn.EINVAL),
     (lambda: _gn(A, 4, 0, B, C, D), bn.EINVAL),
     (lambda: _gn(A, 33, 100, B, C, D), bn.EUNSUPPORTED),
+    (lambda: _gn(A, 4, (1 << 30) + 1, B, C, D), bn.EUNSUPPORTED),
     (lambda: _gn(NUL, 4, 100, B, C, D), bn.EINVAL),
     (lambda: _gn(A, 4, 100, NUL, C, D), bn.EINVAL),
     (lambda: _gn(A, 4, 100, B, NUL, D), bn.EINVAL),
@@ -281,8 +284,10 @@ def test_accept_workspace_size():
     assert bn.bitnest_greedy_accept_workspace_bytes(32, 4097) == 32 * 2 * 8
     assert bn.bitnest_greedy_accept_workspace_bytes(2, 10 ** 6) == 2 * 64 * 8
     assert bn.bitnest_greedy_accept_workspace_bytes(0, 100) == 0
-    # the largest V: still 64 slices (no overflow in the slice count)
-    assert bn.bitnest_greedy_accept_workspace_bytes(2, 2 ** 31 - 1) == 2 * 64 * 8
+    # the largest V: still 64 slices; beyond it (or beyond the row limit) no size
+    assert bn.bitnest_greedy_accept_workspace_bytes(2, 2 ** 30) == 2 * 64 * 8
+    assert bn.bitnest_greedy_accept_workspace_bytes(2, 2 ** 30 + 1) == 0
+    assert bn.bitnest_greedy_accept_workspace_bytes(33, 100) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -7,7 +7,8 @@ before any launch. Every path is run at that size: the single-token fused
 draft and target, the four-token target GEMV, the batched target and draft
 on the matrix cores (one and two token tiles), the partials export of
 both kernel families, and the offline packer (whose fp32 input then has more
-than 2^32 elements). The rows checked against the oracle are a spread over
+than 2^32 elements). Greedy verification is run at its largest vocabulary
+(BITNEST_ACCEPT_MAX_V = 2^30 logits per row) with planted maxima and ties. The rows checked against the oracle are a spread over
 the whole plane plus the last 64 rows, whose offsets come closest to the
 limit; y within 1e-5 * max|y| of the fp64 oracle (BitNest-Llama-3-8B model
 card, "Files", planes.safetensors: W4 and W8 dequantisation), codes, scales,
@@ -123,3 +124,23 @@ def test_largest_plane_pack_bit_exact():
     assert np.array_equal(hi[ridx].cpu().numpy(), want[0])
     assert np.array_equal(lo[ridx].cpu().numpy(), want[1])
     assert np.array_equal(sc[ridx].cpu().numpy().view(np.uint16), want[2])
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_greedy_accept_at_the_largest_vocabulary(noalloc):
+    # V = BITNEST_ACCEPT_MAX_V = 2^30 logits per row (4 GiB): the slices of
+    # the last workgroups end at the row's last column. The answer is fixed by
+    # construction: row 0 peaks at V - 5 and V - 3 (tie: the smaller index),
+    # row 1 at 7 and at V - 1 (tie: 7)
+    V = 1 << 30
+    logits = torch.full((2, V), -1.0, dtype=torch.float32, device="cuda")
+    logits[0, V - 5] = logits[0, V - 3] = 5.0
+    logits[1, 7] = logits[1, V - 1] = 3.0
+    f = bn.bitnest_greedy_accept_noalloc if noalloc else bn.bitnest_greedy_accept
+    for draft, want in (([V - 5], [1, 7]), ([V - 3], [0, V - 5])):
+        targ, result = f(logits, torch.tensor(draft, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        assert targ.cpu().tolist() == [V - 5, 7]
+        assert result.cpu().tolist() == want
+    del logits
+    torch.cuda.empty_cache()

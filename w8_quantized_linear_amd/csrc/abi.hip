@@ -268,14 +268,14 @@ bitnest_status bitnest_pack_nested(const float *W, int N, int K, uint8_t *hi, ui
 }
 
 size_t bitnest_greedy_accept_workspace_bytes(int R, int V) {
-    if (R < 1 || V < 1) return 0;
+    if (R < 1 || V < 1 || R > BITNEST_MAX_M || V > BITNEST_ACCEPT_MAX_V) return 0;
     return bitnest::accept_workspace_bytes(R, V);
 }
 
 bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const int32_t *draft, int32_t *targ,
                                      int32_t *result, void *work, size_t work_bytes, void *stream) {
     if (R < 1 || V < 1) return BITNEST_EINVAL;
-    if (R > BITNEST_MAX_M) return BITNEST_EUNSUPPORTED;
+    if (R > BITNEST_MAX_M || V > BITNEST_ACCEPT_MAX_V) return BITNEST_EUNSUPPORTED;
     if (!logits || !targ || !result || !work || (R > 1 && !draft)) return BITNEST_EINVAL;
     if (work_bytes < bitnest::accept_workspace_bytes(R, V)) return BITNEST_EINVAL;
     if (!aligned16(logits) || !aligned16(targ) || !aligned16(result) || !aligned16(work) ||
@@ -288,7 +288,7 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
 bitnest_status bitnest_greedy_accept_noalloc(const float *logits, int R, int V, const int32_t *draft,
                                              int32_t *targ, int32_t *result, void *stream) {
     if (R < 1 || V < 1) return BITNEST_EINVAL;
-    if (R > BITNEST_MAX_M) return BITNEST_EUNSUPPORTED;
+    if (R > BITNEST_MAX_M || V > BITNEST_ACCEPT_MAX_V) return BITNEST_EUNSUPPORTED;
     if (bitnest::accept_workspace_bytes(R, V) > BITNEST_ACCEPT_NOALLOC_SCRATCH_BYTES) return BITNEST_EUNSUPPORTED;
     if (!logits || !targ || !result || (R > 1 && !draft)) return BITNEST_EINVAL;
     if (!aligned16(logits) || !aligned16(targ) || !aligned16(result) || (draft && !aligned16(draft)))
