@@ -29,6 +29,14 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       SQ_LDS_BANK_CONFLICT), rocprofv3's LdsBankConflict) where the counters
       are present.
 
+  python bench_profile.py ceiling DIR
+      DIR holds the output of
+        rocprofv3 --kernel-trace --output-format csv -d DIR -o run -- python -u bench.py ...
+      of a run that times the read ceiling. Prints, per buffer size and
+      configuration (items in flight per wave, waves per CU) of the sweep,
+      the median dispatch duration of the timed graph replays with its GB/s
+      (the fastest configuration of each size marked).
+
   python bench_profile.py mfma DIR
       DIR holds the output of
         rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_VALU_MFMA_BUSY_CYCLES
@@ -143,6 +151,52 @@ def round_accounting(trace, layers):
         busy = sum(e - b for b, e in zip(starts, ends)) / 1e3
         out.append((busy, (max(ends) - min(starts)) / 1e3))
     return out
+
+
+def ceiling_sweep(trace, sizes_mib, configs, cold_bytes, reps):
+    """{(MiB, depth, waves per CU): (median dispatch us, us per launch over
+    the timed replays' spans)} from the stream_read dispatches of bench.py's
+    read-ceiling sweep, in its order: per size and configuration, one eager
+    pass and 1 + reps graph replays over ceil(cold_bytes / size) buffers."""
+    rows = sorted((r for r in trace if re.match(r"^stream_read_kernel<\d+>", short(r["Kernel_Name"]))),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    plan = []
+    for mib in sizes_mib:
+        count = max(1, -(-cold_bytes // (mib << 20)))
+        plan.extend((mib, depth, wpc, count) for depth, wpc in configs)
+    need = sum(count * (2 + reps) for *_, count in plan)
+    if len(rows) != need:
+        sys.exit("expected %d stream_read dispatches, found %d" % (need, len(rows)))
+    out = {}
+    i = 0
+    for mib, depth, wpc, count in plan:
+        block = rows[i:i + count * (2 + reps)]
+        i += len(block)
+        assert all(short(r["Kernel_Name"]) == "stream_read_kernel<%d>" % depth for r in block)
+        timed = block[2 * count:]
+        durs = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed)
+        spans = sorted((int(timed[k * count + count - 1]["End_Timestamp"]) - int(timed[k * count]["Start_Timestamp"]))
+                       / 1e3 / count for k in range(reps))
+        out[(mib, depth, wpc)] = (quantile(durs, 0.5), spans[len(spans) // 2])
+    return out
+
+
+def cmd_ceiling(directory: str):
+    sys.path.insert(0, ROOT)
+    import inspect
+    import bench
+    trace = read_csv(directory, "kernel_trace.csv")
+    reps = inspect.signature(bench.read_ceiling).parameters["reps"].default
+    sweep = ceiling_sweep(trace, bench.READ_CEILING_MIB, bench.READ_CONFIGS, bench.COLD_BYTES, reps)
+    print("| size | depth | waves per CU | median dispatch us | GB/s |")
+    print("|---|---:|---:|---:|---:|")
+    for mib in bench.READ_CEILING_MIB:
+        cands = {k: v for k, v in sweep.items() if k[0] == mib}
+        best = min(cands, key=lambda k: cands[k][0])
+        for k in sorted(cands, key=lambda k: bench.READ_CONFIGS.index(k[1:])):
+            d = cands[k][0]
+            print("| %d MiB | %d | %s | %.3f%s | %.0f |"
+                  % (mib, k[1], k[2] or "all", d, " **best**" if k == best else "", (mib << 20) / d / 1e3))
 
 
 def cmd_trace(directory: str, layers: int = 32):
@@ -332,6 +386,8 @@ def main(argv=None):
     m.add_argument("dir")
     k = sub.add_parser("counters")
     k.add_argument("dir")
+    r = sub.add_parser("ceiling")
+    r.add_argument("dir")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         cmd_trace(a.dir, a.layers)
@@ -339,6 +395,8 @@ def main(argv=None):
         cmd_mfma(a.dir)
     elif a.cmd == "counters":
         cmd_counters(a.dir)
+    elif a.cmd == "ceiling":
+        cmd_ceiling(a.dir)
     else:
         cmd_traffic(a.fetch_dir, a.write_dir, a.json, a.copy_mib)
 

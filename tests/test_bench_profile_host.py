@@ -105,3 +105,28 @@ def test_round_accounting(tmp_path):
     text = out.getvalue()
     assert "| shape | dispatches | mean us | p10 us | median us | p90 us | min us |" in text
     assert "## Rounds" in text and "| 2 |" in text
+
+
+def test_ceiling_sweep_labels_and_spans(tmp_path):
+    # two sizes x two configurations; per (size, config): an eager pass, a
+    # warm replay and `reps` timed replays over ceil(cold / size) buffers
+    sizes, configs, cold, reps = [1, 4], [(2, 0), (4, 8)], 4 << 20, 3
+    seq = []
+    want = {}
+    for mib in sizes:
+        count = max(1, -(-cold // (mib << 20)))
+        for ci, (depth, wpc) in enumerate(configs):
+            base = 1000 * mib + 100 * ci
+            for p in range(2 + reps):
+                for c in range(count):
+                    seq.append((NS + "stream_read_kernel<%d>(unsigned char const*, unsigned int)" % depth, "sr",
+                                base + p + c))
+            timed = [base + p + c for p in range(2, 2 + reps) for c in range(count)]
+            spans = sorted((sum(base + p + c for c in range(count)) + (count - 1) * GAP) / count
+                           for p in range(2, 2 + reps))
+            want[(mib, depth, wpc)] = (bp.quantile(sorted(timed), 0.5) / 1e3, spans[len(spans) // 2] / 1e3)
+    write_trace(tmp_path, seq, lambda i: 0)
+    got = bp.ceiling_sweep(bp.read_csv(str(tmp_path), "kernel_trace.csv"), sizes, configs, cold, reps)
+    assert set(got) == set(want)
+    for k in want:
+        assert abs(got[k][0] - want[k][0]) < 1e-9 and abs(got[k][1] - want[k][1]) < 1e-9, k
