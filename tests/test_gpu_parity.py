@@ -407,9 +407,10 @@ def test_fused_quant_linear_equals_two_calls(M, N, K, act_group, target):
 @pytest.mark.parametrize("M,target", [(1, False), (1, True), (4, True), (4, False), (2, True)])
 def test_fused_single_token_full_layer(llama_layer, M, target):
     # The launches a round times: quantisation and the linear in one launch
-    # (one token: a draft pass, all four shapes; four tokens: the verify pass
-    # at K = 4096, qkv, o_proj and gate_up, while down takes two launches) at
-    # the Llama-3-8B shapes, o_proj with per-group activation scales. Codes,
+    # (one token: a draft pass, all four shapes; four tokens: the verify pass's
+    # qkv and o_proj, while gate_up (N above 8192) and down (K = 14336) take
+    # two launches) at the Llama-3-8B shapes, o_proj with per-group activation
+    # scales. Codes,
     # scales and y are bit-identical to the two-call path; every row of y is
     # within the bar of the oracle.
     for li, (name, N, K, g, w, wd) in enumerate(llama_layer):
@@ -432,6 +433,26 @@ def test_fused_single_token_full_layer(llama_layer, M, target):
         hi, lo, sc = w.numpy()
         _check_y(y, oracle.linear(q, s, hi, sc, lo if target else None, g), "%s fused t=%s" % (name, target))
 
+
+
+@pytest.mark.parametrize("target", [True, False])
+def test_verify_rows_equal_one_token_calls_full_layer(llama_layer, target):
+    # The verify pass's call (four tokens, quantised in the call: one launch
+    # for qkv and o_proj, two for gate_up and down) at the Llama-3-8B shapes:
+    # each token's codes, scale and y are bit for bit those of a one-token call
+    # on that token, so the verify rows are exactly what one-token target
+    # steps compute.
+    for li, (name, N, K, g, w, wd) in enumerate(llama_layer):
+        xd = _dev(synth.make_activations(4, K, seed=3, layer=2, linear=li))
+        f = bn.bitnest_quant_linear_target if target else bn.bitnest_quant_linear_draft
+        planes = (wd.hi, wd.lo, wd.scale) if target else (wd.hi, wd.scale)
+        y4, q4, s4 = f(xd, *planes, g)
+        for m in range(4):
+            y1, q1, s1 = f(xd[m:m + 1].contiguous(), *planes, g)
+            torch.cuda.synchronize()
+            assert torch.equal(q1[0], q4[m]), (name, m)
+            assert torch.equal(s1[0].view(torch.int32), s4[m].view(torch.int32)), (name, m)
+            assert torch.equal(y1[0].view(torch.int32), y4[m].view(torch.int32)), (name, m)
 
 def test_fused_quant_linear_with_no_rows_still_quantises():
     x = synth.make_activations(3, 512, seed=10)
