@@ -132,6 +132,13 @@ bitnest_status bitnest_linear_draft(const int8_t *xq, const float *xs, int act_g
  *           group;
  *   M >= 8  separate int8 matrix-core contractions of the hi and the lo
  *           plane, combined as 16 P_hi + P_lo in int32.
+ * Rows and batches (draft and target alike): for M <= 7 every row of y is bit
+ * for bit the y of a one-token call on that row's codes, so a verify batch
+ * computes exactly what one-token steps would (the model card's introduction:
+ * speculative decoding returns the target's own greedy output). For M >= 8 a
+ * row does not depend on the other rows either (bit for bit across M = 8 to
+ * 32), but the fp32 sums run in another order than for M <= 7, so those rows
+ * agree with one-token calls to fp32 rounding, not bit for bit.
  */
 bitnest_status bitnest_linear_target(const int8_t *xq, const float *xs, int act_group,
                                      const uint8_t *hi, const uint8_t *lo,
