@@ -295,3 +295,22 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros((1, 128), dtype=torch.float32)
     with pytest.raises(ValueError):
         bn.bitnest_quant_act(x)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # no fallback: without the built HIP library every call path raises
+    monkeypatch.setattr(bn, "_lib", None)
+    monkeypatch.setattr(bn, "library_path", str(tmp_path / "libbitnest.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bn.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        bn.bitnest_abi_version()
+
+
+def test_smoke_refuses_to_run_without_a_gpu():
+    import torch
+    import __graft_entry__
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(RuntimeError, match="needs a GPU"):
+        __graft_entry__.smoke()
