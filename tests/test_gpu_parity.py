@@ -230,17 +230,18 @@ def test_verify_batch_rows_equal_single_token_calls(act_group, target):
             assert torch.equal(a[0], b[m])
 
 
+@pytest.mark.parametrize("act_group", [0, 128])
 @pytest.mark.parametrize("target", [False, True])
-def test_batched_verify_rows_do_not_depend_on_batch(target):
-    # The matrix-core kernel: rows of an M = 32 call equal an M = 8 and an
-    # M = 16 call on the same tokens, bit for bit.
+def test_batched_verify_rows_do_not_depend_on_batch(target, act_group):
+    # The matrix-core kernel: rows of an M = 32 call equal those of M = 8, 9,
+    # 16, 17 and 23 calls on the same tokens (one and two token tiles, full
+    # and ragged), bit for bit.
     N, K = 160, 4096
     w, x = _problem(32, N, K, seed=5)
-    _, _, y32 = _run(w, x, 0, target)
-    _, _, y8 = _run(w, x[:8], 0, target)
-    _, _, y16 = _run(w, x[8:24], 0, target)
-    assert torch.equal(y8.view(torch.int32), y32[:8].view(torch.int32))
-    assert torch.equal(y16.view(torch.int32), y32[8:24].view(torch.int32))
+    _, _, y32 = _run(w, x, act_group, target)
+    for a, b in ((0, 8), (8, 24), (3, 12), (15, 32), (0, 17), (9, 32)):
+        _, _, y = _run(w, x[a:b], act_group, target)
+        assert torch.equal(y.view(torch.int32), y32[a:b].view(torch.int32)), (a, b)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
