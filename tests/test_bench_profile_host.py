@@ -130,3 +130,42 @@ def test_ceiling_sweep_labels_and_spans(tmp_path):
     assert set(got) == set(want)
     for k in want:
         assert abs(got[k][0] - want[k][0]) < 1e-9 and abs(got[k][1] - want[k][1]) < 1e-9, k
+
+
+def _counter_run(d, counter, seq, values, copy_value):
+    os.makedirs(d, exist_ok=True)
+    rows = [{"Dispatch_Id": 1, "Kernel_Name": "void at::native::elementwise_copy_kernel<float>(...)",
+             "Counter_Name": counter, "Counter_Value": copy_value}]
+    for i, (name, label, _) in enumerate(seq):
+        rows.append({"Dispatch_Id": i + 2, "Kernel_Name": name, "Counter_Name": counter,
+                     "Counter_Value": values[label]})
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_traffic_scaling_and_launch_weighting(tmp_path):
+    # FETCH_SIZE and WRITE_SIZE per dispatch (KiB) scaled by what a copy of
+    # known size reads (here: half its bytes) and writes (all of them), then
+    # weighted 3 : 1 over the draft and verify launches of each shape
+    import json
+    seq = launches(2, 2)[:-2]                        # the rounds only
+    labels = [l for _, l, _ in DRAFT + VERIFY]
+    fetch = {l: 1000.0 + 37 * i for i, l in enumerate(labels)}
+    write = {l: 10.0 + 3 * i for i, l in enumerate(labels)}
+    copy_mib = 16
+    _counter_run(str(tmp_path / "f"), "FETCH_SIZE", seq, fetch, copy_mib * 1024 / 2)
+    _counter_run(str(tmp_path / "w"), "WRITE_SIZE", seq, write, copy_mib * 1024)
+    out_json = str(tmp_path / "t.json")
+    buf = io.StringIO()
+    with redirect_stdout(buf):
+        bp.cmd_traffic(str(tmp_path / "f"), str(tmp_path / "w"), out_json, copy_mib)
+    got = json.load(open(out_json))
+    assert abs(got["fetch_factor"] - 2.0) < 1e-12 and abs(got["write_factor"] - 1.0) < 1e-12
+    per_shape = {s: fetch[s] * 1024 * 2 + write[s] * 1024 for s in bp.ROUND_SHAPES}
+    for s in bp.ROUND_SHAPES:
+        assert got["per_shape_bytes"][s] == round(per_shape[s])
+    want = sum((3 if s.startswith("draft") else 1) * per_shape[s] for s in bp.ROUND_SHAPES) / 16
+    assert got["traffic_bytes_per_launch"] == round(want)
+    assert got["sources"] == bp.KERNEL_SOURCES and len(got["sources_sha256"]) == 64
