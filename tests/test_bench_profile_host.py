@@ -169,3 +169,57 @@ def test_traffic_scaling_and_launch_weighting(tmp_path):
     want = sum((3 if s.startswith("draft") else 1) * per_shape[s] for s in bp.ROUND_SHAPES) / 16
     assert got["traffic_bytes_per_launch"] == round(want)
     assert got["sources"] == bp.KERNEL_SOURCES and len(got["sources_sha256"]) == 64
+
+
+def _pmc_rows(d, entries):
+    # entries: (dispatch id, kernel name, duration ns, grid, {counter: value})
+    os.makedirs(d, exist_ok=True)
+    rows = []
+    for did, name, dur, grid, counters in entries:
+        for c, v in counters.items():
+            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Start_Timestamp": 1000 * did,
+                         "End_Timestamp": 1000 * did + dur, "Grid_Size": grid * 512, "Workgroup_Size": 512,
+                         "Counter_Name": c, "Counter_Value": v})
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _table(text):
+    return [[c.strip() for c in line.strip().strip("|").split("|")] for line in text.splitlines()
+            if line.startswith("| ") and not line.startswith("| kernel")]
+
+
+def test_mfma_busy_share(tmp_path):
+    name = NS + "verify_mfma_kernel<2, 1, false, false, 1>(bitnest::LinearArgs, int)"
+    # 448 MFMAs per workgroup x 256 workgroups, 32768 int8 ops each; busy
+    # cycles summed over the 1024 SIMDs: 1792 per SIMD in a 16 us dispatch
+    c = {"SQ_INSTS_VALU_MFMA_MOPS_I8": 114688 * 32768 / 512, "SQ_INSTS_VALU_MFMA_I8": 114688,
+         "SQ_VALU_MFMA_BUSY_CYCLES": 1792 * 1024, "GRBM_GUI_ACTIVE": 1.0}
+    _pmc_rows(str(tmp_path), [(1, name, 16000, 256, c), (2, name, 16000, 256, c)])
+    out = io.StringIO()
+    with redirect_stdout(out):
+        bp.cmd_mfma(str(tmp_path))
+    (row,) = _table(out.getvalue())
+    assert row[0] == "verify_mfma_kernel<2, 1, false, false, 1>" and row[1] == "2" and row[2] == "256"
+    assert row[3] == "16.00" and float(row[4]) == float("%.4g" % (114688 * 32768)) and row[5] == "114688"
+    assert row[6] == "1792"
+    assert row[7] == "%.2f %%" % (100.0 * 1792 / (16000 * 2.4))
+
+
+def test_counters_derived_rates(tmp_path):
+    qkv = NS + "gemv_planes_kernel<1, 1, false, false, 4, 8, 1, 0>(bitnest::LinearArgs)"
+    c1 = {"TCC_HIT_sum": 300.0, "TCC_MISS_sum": 100.0, "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 60.0}
+    c2 = {"TCC_HIT_sum": 100.0, "TCC_MISS_sum": 300.0, "SQ_LDS_BANK_CONFLICT": 30.0, "SQ_LDS_IDX_ACTIVE": 100.0}
+    # launch order qkv, gate_up, qkv, gate_up for this instantiation
+    _pmc_rows(str(tmp_path), [(1, qkv, 5000, 256, c1), (2, qkv, 12000, 256, c2),
+                              (3, qkv, 5000, 256, c1), (4, qkv, 12000, 256, c2)])
+    out = io.StringIO()
+    with redirect_stdout(out):
+        bp.cmd_counters(str(tmp_path))
+    rows = {r[0]: r for r in _table(out.getvalue())}
+    assert set(rows) == {"draft qkv", "draft gate_up"}
+    assert rows["draft qkv"][1] == "2" and rows["draft qkv"][2] == "5.00"
+    assert rows["draft qkv"][-2] == "75.0" and rows["draft gate_up"][-2] == "25.0"       # L2 hit %
+    assert rows["draft qkv"][-1] == "0.2000" and rows["draft gate_up"][-1] == "0.4286"   # c / (a - c)
