@@ -108,7 +108,8 @@ bitnest_status bitnest_quant_act(const float *x, int M, int K, int act_group,
  * This equals sum_k (xq[m,k] * s_a) * W4[n,k] up to fp32 rounding.
  *
  *   xq     int8 [M, K] codes;  xs  fp32 [M] or [M, K/128]
- *   hi     uint8 [N, K/2]      scale  fp16 bit patterns [N, K/128]
+ *   hi     uint8 [N, K/2]      scale  fp16 bit patterns [N, K/128], any finite
+ *                              value (negative, zero and subnormal included)
  *   y      fp32 [M, N], every element overwritten.
  * Only `hi` and `scale` are read from the weights.
  */

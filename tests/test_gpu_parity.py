@@ -230,6 +230,61 @@ def test_verify_batch_rows_equal_single_token_calls(act_group, target):
             assert torch.equal(a[0], b[m])
 
 
+
+def _special_scales(N, G, seed):
+    # fp16 bit patterns, 16 rows per class: negative normals; subnormals of
+    # both signs; zeros of both signs between normals; the extremes (largest
+    # finite 65504, smallest normal 2^-14) of both signs
+    rng = np.random.default_rng(seed)
+    sc = np.empty((N, G), np.uint16)
+    normal = lambda n: (np.exp(np.log(0.01) + 0.3 * rng.standard_normal(n))).astype(np.float16).view(np.uint16)
+    for r in range(N):
+        kind = (r // 16) % 4
+        if kind == 0:
+            sc[r] = normal(G) | 0x8000
+        elif kind == 1:
+            sc[r] = rng.integers(1, 0x400, G).astype(np.uint16) | (rng.integers(0, 2, G) << 15).astype(np.uint16)
+        elif kind == 2:
+            sc[r] = np.where(rng.integers(0, 2, G) == 1, normal(G), np.where(rng.integers(0, 2, G) == 1, 0x8000, 0))
+        else:
+            sc[r] = rng.choice(np.array([0x7BFF, 0xFBFF, 0x0400, 0x8400], np.uint16), G)
+    return sc
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("act_group", [0, 128])
+@pytest.mark.parametrize("target", [False, True])
+def test_special_weight_scales(M, act_group, target):
+    # Any finite fp16 scale: each output within 1e-5 of the sum of the
+    # magnitudes of its group terms |P * scale * f * s_a| (the fp32 sum of at
+    # most 128 terms stays within 130 * 2^-24 of that; rows whose terms
+    # cancel are not held to a bound relative to their own small value)
+    N, K = 64, 4096
+    G = K // 128
+    w, x = _problem(M, N, K, seed=31)
+    sc = _special_scales(N, G, seed=31)
+    xd = _dev(x)
+    xq, xs = bn.bitnest_quant_act(xd, act_group)
+    hi, lo, scd = _dev(w.hi), _dev(w.lo), torch.from_numpy(sc.view(np.int16)).cuda()
+    if target:
+        y = bn.bitnest_linear_target(xq, xs, hi, lo, scd, act_group)
+    else:
+        y = bn.bitnest_linear_draft(xq, xs, hi, scd, act_group)
+    torch.cuda.synchronize()
+    q, s = oracle.quant_act(x.numpy(), act_group)
+    hn, ln, _ = w.numpy()
+    y64 = oracle.linear(q, s, hn, sc, ln if target else None, act_group)
+    P = oracle.partials(q, hn, ln)[2] if target else oracle.partials(q, hn)
+    f = 1.0 / 16 if target else 1.0
+    sa = s[:, None, None] if act_group == 0 else s[:, None, :]
+    terms = np.abs(P.astype(np.float64) * sc.view(np.float16).astype(np.float64)[None] * f * sa)
+    bound = 1e-5 * terms.sum(axis=2) + 1e-38
+    got = y.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    err = np.abs(got - y64)
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert (err <= bound).all(), ("token, row", worst, err[worst], bound[worst])
+
 @pytest.mark.parametrize("act_group", [0, 128])
 @pytest.mark.parametrize("target", [False, True])
 def test_batched_verify_rows_do_not_depend_on_batch(target, act_group):
