@@ -42,6 +42,10 @@
  *     A fault inside a kernel surfaces at the caller's next synchronisation
  *     of the stream, as for any HIP kernel.
  *   - Outputs must not overlap inputs.
+ *   - Inputs are finite. Results are the definitions below computed in fp32
+ *     (the integer parts exactly) as long as they stay within fp32's range;
+ *     a result that overflows it is undefined (+-inf or NaN). Subnormal
+ *     inputs and scales are handled as IEEE values, not flushed.
  *   - Calls are reentrant; calls on different streams may run concurrently,
  *     except two bitnest_greedy_accept_noalloc calls on one device, which
  *     share that device's scratch, and two calls that share a workspace.

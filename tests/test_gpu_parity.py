@@ -522,6 +522,75 @@ def test_fused_quant_linear_with_no_rows_still_quantises():
     assert np.array_equal(fq.cpu().numpy(), q) and np.array_equal(fs.cpu().numpy(), s)
 
 
+
+def _extreme_tokens(K, seed):
+    # fp32 tokens whose maxima span the range: ordinary, 1e34 and 1e30 times
+    # larger, 1e-30 and 1e-37 times smaller (s = amax / 127 subnormal), 1e-44
+    # (the values themselves subnormal; s underflows to 0, so every code is
+    # 0), a single nonzero value, and all zeros
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((8, K)).astype(np.float32)
+    x = np.empty((8, K), np.float32)
+    for i, f in enumerate([1.0, 1e34, 1e30, 1e-30, 1e-37, 1e-44]):
+        x[i] = (base[i].astype(np.float64) * f).astype(np.float32)
+    x[6] = 0.0
+    x[6, K // 3] = -1.0
+    x[7] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("act_group", [0, 128])
+def test_extreme_activation_magnitudes(act_group):
+    # Codes and scales bit for bit against the oracle on every quantising
+    # path (the quantisation kernel, the fused one-token launch, the fused
+    # four-token launch), and y of the linears (GEMV at four tokens and in the
+    # fused calls, matrix cores at eight) within 1e-5 of the sum of its group
+    # terms' magnitudes
+    N, K = 96, 4096
+    x = _extreme_tokens(K, seed=21)
+    w = synth.make_weights(N, K, seed=21)
+    hn, ln, sc = w.numpy()
+    q, s = oracle.quant_act(x, act_group)
+    assert (q[5] == 0).all() and (s[5] == 0).all()          # the scale underflows: codes 0
+    xd = torch.from_numpy(x).cuda()
+    hi, lo, scd = _dev(w.hi), _dev(w.lo), _dev(w.scale)
+    xq, xs = bn.bitnest_quant_act(xd, act_group)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), q)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+    def bound(P, f, qi, si):
+        sa = si[:, None, None] if act_group == 0 else si[:, None, :]
+        t = np.abs(P.astype(np.float64) * sc.view(np.float16).astype(np.float64)[None] * f * sa)
+        return 1e-5 * t.sum(axis=2) + 1e-38
+
+    def check(y, rows, target):
+        qi, si = q[rows], s[rows]
+        y64 = oracle.linear(qi, si, hn, sc, ln if target else None, act_group)
+        P = oracle.partials(qi, hn, ln)[2] if target else oracle.partials(qi, hn)
+        got = y.double().cpu().numpy()
+        assert np.isfinite(got).all()
+        assert (np.abs(got - y64) <= bound(P, 1 / 16 if target else 1.0, qi, si)).all(), (rows, target)
+
+    for target in (False, True):
+        planes = (hi, lo, scd) if target else (hi, scd)
+        lin = bn.bitnest_linear_target if target else bn.bitnest_linear_draft
+        fused = bn.bitnest_quant_linear_target if target else bn.bitnest_quant_linear_draft
+        check(lin(xq, xs, *planes, act_group), list(range(8)), target)            # matrix cores
+        check(lin(xq[:4].contiguous(), xs[:4].contiguous(), *planes, act_group), [0, 1, 2, 3], target)
+        for m in range(8):                                                       # fused, one token
+            y, fq, fs = fused(xd[m:m + 1].contiguous(), *planes, act_group)
+            torch.cuda.synchronize()
+            assert np.array_equal(fq.cpu().numpy(), q[m:m + 1]), m
+            assert np.array_equal(fs.cpu().numpy().view(np.uint32), s[m:m + 1].view(np.uint32)), m
+            check(y, [m], target)
+        y, fq, fs = fused(xd[4:8].contiguous(), *planes, act_group)             # fused, four tokens
+        torch.cuda.synchronize()
+        assert bn.fused_in_one_launch(4, N, K)
+        assert np.array_equal(fq.cpu().numpy(), q[4:8])
+        assert np.array_equal(fs.cpu().numpy().view(np.uint32), s[4:8].view(np.uint32))
+        check(y, [4, 5, 6, 7], target)
+
 def _near_tie_rows(K=512):
     """Rows whose elements sit within a few ulps of (k + 1/2) * s, s = amax/127:
     the places where a reciprocal-multiply rounds differently from x / s."""
