@@ -49,6 +49,34 @@ def test_rotation_and_codes_bit_exact(M, K, block):
     assert np.array_equal(_bits(xs.cpu().numpy()), _bits(s_ref))
 
 
+
+@pytest.mark.parametrize("block", [512, 64])
+def test_rotation_of_extreme_magnitudes_bit_exact(block):
+    # tokens whose maxima span the fp32 range (1e34 down to subnormal values
+    # whose scale underflows to 0), a single nonzero value and a zero token:
+    # the rotated values, codes and scales bit for bit on the rotation
+    # kernel and on the rotating one-token fused launch
+    K = 14336
+    rng = np.random.default_rng(block)
+    base = rng.standard_normal((8, K))
+    x = np.zeros((8, K), np.float32)
+    for i, f in enumerate([1.0, 1e34, 1e30, 1e-30, 1e-37, 1e-44]):
+        x[i] = (base[i] * f).astype(np.float32)
+    x[6, 5] = 3.0
+    q_ref, s_ref, r_ref = oracle.hadamard_quant_act(x, block)
+    xq, xs, xr = bn.bitnest_hadamard_quant_act(torch.from_numpy(x).cuda(), block, rotated=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(xr.cpu().numpy()), _bits(r_ref))
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(_bits(xs.cpu().numpy()), _bits(s_ref))
+    w = synth.make_weights(64, K, seed=24)
+    for m in range(8):
+        xd = torch.from_numpy(x[m:m + 1].copy()).cuda()
+        _, fq, fs = bn.bitnest_hadamard_quant_linear_draft(xd, block, w.hi.cuda(), w.scale.cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(fq.cpu().numpy(), q_ref[m:m + 1]), m
+        assert np.array_equal(_bits(fs.cpu().numpy()), _bits(s_ref[m:m + 1])), m
+
 def test_rotation_without_rotated_output_gives_same_codes():
     x = synth.make_activations(4, 14336, seed=22)
     xq1, xs1 = bn.bitnest_hadamard_quant_act(x.cuda(), 512)
