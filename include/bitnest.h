@@ -362,10 +362,11 @@ bitnest_status bitnest_greedy_accept(const float *logits, int R, int V, const in
  * harnesses that forbid allocation). The per-slice partials go to a scratch
  * array the library holds in each device's memory for the life of the
  * process (BITNEST_ACCEPT_NOALLOC_SCRATCH_BYTES, enough for every R <=
- * BITNEST_MAX_M and any V). The call allocates and frees nothing. Results are
- * those of bitnest_greedy_accept, bit for bit. All calls on one device share
- * that device's scratch: calls that may overlap on one device (different
- * streams without ordering between them) race and must not be made; calls
+ * BITNEST_MAX_M and every V <= BITNEST_ACCEPT_MAX_V). The call allocates and
+ * frees nothing. Results are those of bitnest_greedy_accept, bit for bit.
+ * All calls on one device share that device's scratch: calls that may
+ * overlap on one device (different streams without ordering between them)
+ * race and must not be made; calls
  * in one stream's order are safe. Arguments and errors as for
  * bitnest_greedy_accept, without `work` / `work_bytes`; a size beyond the
  * scratch (R > BITNEST_MAX_M) gives BITNEST_EUNSUPPORTED.
