@@ -24,10 +24,11 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       DIR holds the output of one rocprofv3 --pmc pass (any counters) of
       bench.py. Prints, per round shape and per batched-verify
       instantiation, the mean of each counter per dispatch, and the derived
-      L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)) and LDS bank conflicts
-      per access (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE -
-      SQ_LDS_BANK_CONFLICT), rocprofv3's LdsBankConflict) where the counters
-      are present.
+      L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS)), LDS bank conflicts per
+      access (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE -
+      SQ_LDS_BANK_CONFLICT), rocprofv3's LdsBankConflict) and the VALU issue
+      share (SQ_INSTS_VALU x 4 cycles over all SIMDs' cycles of the
+      dispatch at the peak clock) where the counters are present.
 
   python bench_profile.py ceiling DIR
       DIR holds the output of
@@ -353,6 +354,8 @@ def cmd_counters(directory: str):
         derived.append("L2 hit %")
     if "SQ_LDS_BANK_CONFLICT" in names and "SQ_LDS_IDX_ACTIVE" in names:
         derived.append("LDS conflicts per access")
+    if "SQ_INSTS_VALU" in names:
+        derived.append("VALU issue share %")
     print("| kernel / shape | dispatches | mean us | " + " | ".join(names + derived) + " |")
     print("|---|---:|---:|" + "---:|" * (len(names) + len(derived)))
     hit = next((n for n in names if n.startswith("TCC_HIT")), None)
@@ -368,6 +371,11 @@ def cmd_counters(directory: str):
         if "LDS conflicts per access" in derived:
             c, a = mean("SQ_LDS_BANK_CONFLICT"), mean("SQ_LDS_IDX_ACTIVE")
             cells.append("%.4f" % (c / (a - c)) if a > c else "-")
+        if "VALU issue share %" in derived:
+            # wave64 VALU instructions take 4 cycles of a 16-lane SIMD; against
+            # every SIMD over the dispatch at the peak clock (an understatement
+            # where the clock runs lower)
+            cells.append("%.1f" % (100.0 * mean("SQ_INSTS_VALU") * 4 / (SIMDS * mean("dur_ns") * CLOCK_GHZ)))
         print("| %s | %d | %.2f | %s |" % (k, n, mean("dur_ns") / 1e3, " | ".join(cells)))
 
 

@@ -210,8 +210,12 @@ def test_mfma_busy_share(tmp_path):
 
 def test_counters_derived_rates(tmp_path):
     qkv = NS + "gemv_planes_kernel<1, 1, false, false, 4, 8, 1, 0>(bitnest::LinearArgs)"
-    c1 = {"TCC_HIT_sum": 300.0, "TCC_MISS_sum": 100.0, "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 60.0}
-    c2 = {"TCC_HIT_sum": 100.0, "TCC_MISS_sum": 300.0, "SQ_LDS_BANK_CONFLICT": 30.0, "SQ_LDS_IDX_ACTIVE": 100.0}
+    # SQ_INSTS_VALU: 1200 (2400) cycles' worth per SIMD at 4 cycles each over
+    # 5 us (12 us) at 2.4 GHz = 10 % (8.33 %)
+    c1 = {"TCC_HIT_sum": 300.0, "TCC_MISS_sum": 100.0, "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 60.0,
+          "SQ_INSTS_VALU": 1200 / 4 * 1024}
+    c2 = {"TCC_HIT_sum": 100.0, "TCC_MISS_sum": 300.0, "SQ_LDS_BANK_CONFLICT": 30.0, "SQ_LDS_IDX_ACTIVE": 100.0,
+          "SQ_INSTS_VALU": 2400 / 4 * 1024}
     # launch order qkv, gate_up, qkv, gate_up for this instantiation
     _pmc_rows(str(tmp_path), [(1, qkv, 5000, 256, c1), (2, qkv, 12000, 256, c2),
                               (3, qkv, 5000, 256, c1), (4, qkv, 12000, 256, c2)])
@@ -221,5 +225,6 @@ def test_counters_derived_rates(tmp_path):
     rows = {r[0]: r for r in _table(out.getvalue())}
     assert set(rows) == {"draft qkv", "draft gate_up"}
     assert rows["draft qkv"][1] == "2" and rows["draft qkv"][2] == "5.00"
-    assert rows["draft qkv"][-2] == "75.0" and rows["draft gate_up"][-2] == "25.0"       # L2 hit %
-    assert rows["draft qkv"][-1] == "0.2000" and rows["draft gate_up"][-1] == "0.4286"   # c / (a - c)
+    assert rows["draft qkv"][-3] == "75.0" and rows["draft gate_up"][-3] == "25.0"       # L2 hit %
+    assert rows["draft qkv"][-2] == "0.2000" and rows["draft gate_up"][-2] == "0.4286"   # c / (a - c)
+    assert rows["draft qkv"][-1] == "10.0" and rows["draft gate_up"][-1] == "8.3"        # VALU issue share
