@@ -136,6 +136,20 @@ class Stack:
                 tot += passes * self.layers * b
         return tot
 
+    def algorithmic_bytes_per_round(self):
+        """All bytes the round must move at least: the linear launches'
+        (gemv_algorithmic_bytes_per_round) plus those of the separate
+        quantisation launches of the calls that take two launches (fp32 rows
+        read, codes and activation scales written)."""
+        import w8_quantized_linear_amd as bn
+        tot = self.gemv_algorithmic_bytes_per_round()
+        for M, passes in ((1, GAMMA), (GAMMA + 1, 1)):
+            for (_, N, K, g) in self.linears:
+                if not bn.fused_in_one_launch(M, N, K):
+                    S = 1 if g == 0 else K // 128
+                    tot += passes * self.layers * (4 * M * K + M * K + 4 * M * S)
+        return tot
+
     def gemv_launches_per_round(self):
         return (GAMMA + 1) * self.layers * len(self.linears)
 
@@ -710,6 +724,7 @@ def main(argv=None):
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = e0.elapsed_time(e1) / args.steps
     plane_bytes = stack.plane_bytes_per_round()
+    alg_bytes = stack.algorithmic_bytes_per_round()
     value = plane_bytes / (ms_per_step * 1e-3) / 1e9
     log("timed %d rounds: %.3f ms/round wall, %.3f ms/round events" % (args.steps, ms_per_step, ev_ms))
 
@@ -764,9 +779,11 @@ def main(argv=None):
                                "round: %d draft passes M=1 (hi plane) + 1 verify pass M=%d (hi+lo planes), "
                                "act quant + nested linear per linear" % (args.layers, GAMMA, GAMMA + 1),
                    "layers": args.layers, "gamma": GAMMA, "plane_bytes_per_round": plane_bytes,
+                   "algorithmic_bytes_per_round": alg_bytes,
                    "quant": "fused into the linear launch" if fused else "separate launch",
                    "replay": "hip_graph"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "algorithmic_GBps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": roofline,
         "read_ceiling": ceiling,
         "per_linear": linears,

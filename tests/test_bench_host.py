@@ -57,6 +57,12 @@ def test_algorithmic_bytes_per_launch():
     assert s.gemv_launches_per_round() == 32 * launches
     assert s.gemv_algorithmic_bytes_per_round() == 32 * total
     assert int(s.gemv_algorithmic_bytes_per_round() / s.gemv_launches_per_round()) == 35045821
+    # the whole round adds the quantisation launches of the verify calls that
+    # take two launches (gate_up, down): 4 fp32 rows read, codes and scales
+    # written
+    quant = sum(4 * 4 * K + 4 * K + 4 * 4 * (K // 128 if g else 1)
+                for (_, N, K, g) in SHAPES if not (K <= 4096 and N <= 8192))
+    assert s.algorithmic_bytes_per_round() == 32 * (total + quant)
     # plane bytes of the round: three hi-only passes and one hi+lo pass
     assert s.plane_bytes_per_round() == 32 * 5 * sum(N * K // 2 for (_, N, K, _) in SHAPES)
 

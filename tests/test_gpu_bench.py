@@ -38,6 +38,8 @@ def test_bench_prints_the_contract_line():
     assert out["n_gpus"] == 1 and out["steps"] == 2 and out["warmup"] == 1
     assert out["value"] > 0 and out["ms_per_step"] > 0 and out["vs_baseline"] is None
     assert "workload" in out["config"] and out["config"]["layers"] == 2
+    assert out["config"]["algorithmic_bytes_per_round"] > out["config"]["plane_bytes_per_round"]
+    assert out["algorithmic_GBps"] > out["value"]
     roof = out["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert 0 < roof["frac"] < 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
