@@ -1,5 +1,6 @@
-"""The oracle's pins, run once more against a copy of the C oracle built
-with AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
+"""The oracle's pins and property tests, run once more against a copy of
+the C oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+(CPU only).
 
 An out-of-bounds access, a use of freed memory, a signed overflow or an
 invalid shift anywhere in bitnest_oracle.c that the pins reach aborts the
@@ -44,7 +45,7 @@ def test_oracle_pins_pass_under_address_and_undefined_behaviour_sanitizers(tmp_p
     env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1:log_path=%s" % logs
     env["OMP_NUM_THREADS"] = "4"
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", "-x",
-                        os.path.join(HERE, "test_oracle.py")],
+                        os.path.join(HERE, "test_oracle.py"), os.path.join(HERE, "test_oracle_properties.py")],
                        env=env, capture_output=True, text=True, cwd=os.path.dirname(HERE), timeout=900)
     reports = "".join(open(f).read() for f in sorted(tmp_path.glob("san*")))
     tail = (r.stdout + r.stderr)[-2000:] + reports[:4000]
