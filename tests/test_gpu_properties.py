@@ -1,7 +1,9 @@
 """GPU parity over drawn problems: derandomized Hypothesis draws of the
 token count (1 to 32: the GEMV and the matrix-core kernel), ragged N, K (one
 to forty 128-column groups), per-token or per-group activation scales, draft
-or target, and activation magnitudes over many orders, through the C ABI.
+or target, and activation magnitudes over many orders, through the C ABI;
+then drawn problems for the packer, greedy verification and the KV
+attention, each against the oracle to its own bar.
 
 Bars (BitNest-Llama-3-8B model card, "Files", planes.safetensors: the W4 and
 W8 dequantisation; recipe table row "Activations"): codes and scales bit for
@@ -71,3 +73,83 @@ def test_drawn_problems_match_the_oracle(p):
     err = np.abs(y.double().cpu().numpy() - y64)
     worst = np.unravel_index(np.argmax(err / bound), err.shape)
     assert (err <= bound).all(), (p, worst, err[worst], bound[worst])
+
+
+# --------------------------------------------------------------------------- the rows ranked next
+
+@st.composite
+def pack_problems(draw):
+    N = draw(st.integers(1, 300))
+    K = 128 * draw(st.integers(1, 24))
+    mag = draw(st.sampled_from([1.0, 1e-3, 1e4, 1e-7, 3e-8]))     # the last: subnormal fp16 scales
+    seed = draw(st.integers(0, 2**16))
+    return N, K, mag, seed
+
+
+@settings(max_examples=120, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(p=pack_problems())
+def test_drawn_packs_match_the_oracle(p):
+    # the offline packer (model card introduction: the hi nibble the W4 fit,
+    # the lo nibble the closed-form residual): planes and scale bits exact
+    N, K, mag, seed = p
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * mag * rng.uniform(0.1, 3.0, size=(N, 1))).astype(np.float32)
+    W[rng.random((N, K)) < 0.01] = 0.0
+    hi, lo, sc = bn.bitnest_pack_nested(torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    h_ref, l_ref, s_ref = oracle.pack_nested(W)
+    assert np.array_equal(hi.cpu().numpy(), h_ref)
+    assert np.array_equal(lo.cpu().numpy(), l_ref)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), s_ref)
+
+
+@st.composite
+def accept_problems(draw):
+    R = draw(st.integers(1, 32))
+    V = draw(st.one_of(st.integers(1, 5000), st.integers(5000, 300000)))
+    ties = draw(st.sampled_from(["none", "top", "flat", "negative"]))
+    seed = draw(st.integers(0, 2**16))
+    return R, V, ties, seed
+
+
+@settings(max_examples=120, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(p=accept_problems())
+def test_drawn_greedy_rounds_match_the_oracle(p):
+    # greedy verification (model card introduction: every draft token is
+    # checked against the target): argmax with ties to the smallest index,
+    # accepted count and next token exact
+    from test_gpu_accept import _case
+    R, V, ties, seed = p
+    logits, draft = _case(R, V, seed=seed, ties=ties)
+    targ, res = bn.bitnest_greedy_accept(torch.from_numpy(logits).cuda(), torch.from_numpy(draft).cuda())
+    torch.cuda.synchronize()
+    t_ref, n_ref, next_ref = oracle.greedy_accept(logits, draft)
+    assert np.array_equal(targ.cpu().numpy(), t_ref)
+    assert res.cpu().numpy().tolist() == [n_ref, next_ref]
+
+
+@st.composite
+def kv_problems(draw):
+    Hkv = draw(st.sampled_from([1, 2, 4, 8]))
+    G = draw(st.sampled_from([1, 2, 4, 8]))
+    M = draw(st.integers(1, max(1, min(4, 16 // G))))
+    T = draw(st.integers(M, 3000))
+    t_cap = T + draw(st.integers(0, 200))
+    kv8 = draw(st.booleans())
+    seed = draw(st.integers(0, 2**16))
+    return M, G * Hkv, Hkv, T, t_cap, kv8, seed
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(p=kv_problems())
+def test_drawn_kv_attention_matches_the_oracle(p):
+    # nested KV decode attention (model card recipe table row "KV cache"):
+    # each (token, query head) output within 1e-5 of its own largest
+    # magnitude, plus 1e-8 of max|V|
+    from test_gpu_kv import _cache, _check, _ref, _run, _vmax
+    M, Hq, Hkv, T, t_cap, kv8, seed = p
+    assert M * Hq // Hkv <= 16
+    kc, vc = _cache(T, Hkv, seed=seed, spread=0.5)
+    q = np.random.default_rng(seed).standard_normal((M, Hq, 128)).astype(np.float32)
+    got = _run(q, kc, vc, kv8, t_cap=t_cap)
+    _check(got, _ref(q, kc, vc, kv8), _vmax(vc, kv8))
