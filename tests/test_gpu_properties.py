@@ -2,8 +2,8 @@
 token count (1 to 32: the GEMV and the matrix-core kernel), ragged N, K (one
 to forty 128-column groups), per-token or per-group activation scales, draft
 or target, and activation magnitudes over many orders, through the C ABI;
-then drawn problems for the packer, greedy verification and the KV
-attention, each against the oracle to its own bar.
+then drawn problems for the packer, greedy verification, the KV attention
+and the R4 rotation, each against the oracle to its own bar.
 
 Bars (BitNest-Llama-3-8B model card, "Files", planes.safetensors: the W4 and
 W8 dequantisation; recipe table row "Activations"): codes and scales bit for
@@ -153,3 +153,45 @@ def test_drawn_kv_attention_matches_the_oracle(p):
     q = np.random.default_rng(seed).standard_normal((M, Hq, 128)).astype(np.float32)
     got = _run(q, kc, vc, kv8, t_cap=t_cap)
     _check(got, _ref(q, kc, vc, kv8), _vmax(vc, kv8))
+
+
+@st.composite
+def rotation_problems(draw):
+    block = 2 ** draw(st.integers(1, 9))                 # 2 .. 512
+    K = 128 * draw(st.integers(1, 112))
+    if K % block:
+        K = block * (K // block + 1)
+    M = draw(st.integers(1, 8))
+    N = draw(st.integers(1, 200))
+    mag = draw(st.sampled_from([1.0, 1e-30, 1e30]))
+    target = draw(st.booleans())
+    seed = draw(st.integers(0, 2**16))
+    return M, N, K, block, mag, target, seed
+
+
+@settings(max_examples=80, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(p=rotation_problems())
+def test_drawn_rotations_match_the_oracle(p):
+    # the R4 rotation of the down_proj input (model card recipe table row
+    # "Rotation"): rotated values, codes and scales bit for bit; the rotating
+    # quantise + linear call bit for bit equal to the rotation call followed
+    # by the linear
+    M, N, K, block, mag, target, seed = p
+    x = (synth.make_activations(M, K, seed=seed, layer=block).double() * mag).float()
+    xd = x.cuda()
+    xq, xs, xr = bn.bitnest_hadamard_quant_act(xd, block, rotated=True)
+    w = synth.make_weights(N, K, seed=seed, layer=block)
+    hi, lo, sc = w.hi.cuda(), w.lo.cuda(), w.scale.cuda()
+    if target:
+        y_ref = bn.bitnest_linear_target(xq, xs, hi, lo, sc)
+        y, fq, fs = bn.bitnest_hadamard_quant_linear_target(xd, block, hi, lo, sc)
+    else:
+        y_ref = bn.bitnest_linear_draft(xq, xs, hi, sc)
+        y, fq, fs = bn.bitnest_hadamard_quant_linear_draft(xd, block, hi, sc)
+    torch.cuda.synchronize()
+    q_ref, s_ref, r_ref = oracle.hadamard_quant_act(x.numpy(), block)
+    assert np.array_equal(xr.cpu().numpy().view(np.uint32), r_ref.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert torch.equal(fq, xq) and torch.equal(fs.view(torch.int32), xs.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
