@@ -3,7 +3,8 @@ token count (1 to 32: the GEMV and the matrix-core kernel), ragged N, K (one
 to forty 128-column groups), per-token or per-group activation scales, draft
 or target, and activation magnitudes over many orders, through the C ABI;
 then drawn problems for the packer, greedy verification, the KV attention
-and the R4 rotation, each against the oracle to its own bar.
+and the R4 rotation, each against the oracle to its own bar, and drawn
+chains of linears against the single calls.
 
 Bars (BitNest-Llama-3-8B model card, "Files", planes.safetensors: the W4 and
 W8 dequantisation; recipe table row "Activations"): codes and scales bit for
@@ -195,3 +196,53 @@ def test_drawn_rotations_match_the_oracle(p):
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     assert torch.equal(fq, xq) and torch.equal(fs.view(torch.int32), xs.view(torch.int32))
     assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
+
+
+@st.composite
+def chain_problems(draw):
+    M = draw(st.integers(1, 4))
+    target = draw(st.booleans())
+    links = []
+    for j in range(draw(st.integers(1, 8))):
+        prev_n = links[-1][0] if links else 0
+        chained = bool(links) and prev_n >= 128 and prev_n % 128 == 0 and draw(st.booleans())
+        N = draw(st.one_of(st.just(0), st.integers(1, 3000), st.sampled_from([128, 256, 1024, 4096])))
+        K = prev_n if chained else 128 * draw(st.integers(1, 32))
+        links.append((N, K, draw(st.sampled_from([0, 128])), chained))
+    return M, target, links, draw(st.integers(0, 2**16))
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(p=chain_problems())
+def test_drawn_chains_equal_single_calls(p):
+    # a chain of quantise + linear steps in one launch, some links reading the
+    # previous link's output: every y, code and scale bit for bit that of the
+    # single calls made one after another
+    M, target, spec, seed = p
+    links = []
+    for i, (N, K, g, chained) in enumerate(spec):
+        w = synth.make_weights(N, K, seed=seed, layer=i, with_lo=target, device="cuda")
+        x = links[-1]["y"] if chained else synth.make_activations(M, K, seed=seed, layer=i, device="cuda")
+        d = dict(x=x, hi=w.hi, scale=w.scale, y=torch.empty((M, N), device="cuda"), act_group=g,
+                 xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                 xs=torch.empty((M,) if g == 0 else (M, K // 128), device="cuda"))
+        if target:
+            d["lo"] = w.lo
+        links.append(d)
+    chain = bn.LinearChain(links)
+    chain.run()
+    torch.cuda.synchronize()
+    got = [(d["y"].clone(), d["xq"].clone(), d["xs"].clone()) for d in links]
+    prev = None
+    for j, (d, (N, K, g, chained)) in enumerate(zip(links, spec)):
+        x = prev if chained else d["x"]
+        if target:
+            y, q, s = bn.bitnest_quant_linear_target(x, d["hi"], d["lo"], d["scale"], g)
+        else:
+            y, q, s = bn.bitnest_quant_linear_draft(x, d["hi"], d["scale"], g)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), got[j][0].view(torch.int32)), ("y", j)
+        assert torch.equal(q, got[j][1]), ("codes", j)
+        assert torch.equal(s.view(torch.int32), got[j][2].view(torch.int32)), ("scales", j)
+        prev = y
+    assert chain.work[:8].view(torch.int32).cpu().tolist() == [0, 0]
