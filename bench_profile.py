@@ -28,7 +28,9 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       access (SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE -
       SQ_LDS_BANK_CONFLICT), rocprofv3's LdsBankConflict) and the VALU issue
       share (SQ_INSTS_VALU x 4 cycles over all SIMDs' cycles of the
-      dispatch at the peak clock) where the counters are present.
+      dispatch at the peak clock) where the counters are present; with
+      --copy-mib MIB (the run's --copy-calibration), FETCH_SIZE and
+      WRITE_SIZE scaled to bytes by what that copy reads and writes.
 
   python bench_profile.py ceiling DIR
       DIR holds the output of
@@ -338,9 +340,19 @@ def cmd_mfma(directory: str):
             mean("SQ_INSTS_VALU_MFMA_I8"), busy, 100.0 * busy / (dur * CLOCK_GHZ)))
 
 
-def cmd_counters(directory: str):
+def cmd_counters(directory: str, copy_mib: int = 0):
     rows = read_csv(directory, "counter_collection.csv")
     names = sorted({r["Counter_Name"] for r in rows})
+    scaled = {}
+    if copy_mib:
+        # bytes per counter KiB from the run's known-size device copy, as for
+        # the traffic summary
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in names:
+                f, raw = copy_factor(per_dispatch(rows, c), c, copy_mib * 1048576.0)
+                scaled[c] = f
+                print("Calibration: the %d MiB copy reads %s = %.1f KiB: bytes = %.4f x %s KiB x 1024.\n"
+                      % (copy_mib, c, raw, f, c))
     per = {}
     for r in rows:
         if "bitnest" not in r["Kernel_Name"]:
@@ -356,6 +368,8 @@ def cmd_counters(directory: str):
         derived.append("LDS conflicts per access")
     if "SQ_INSTS_VALU" in names:
         derived.append("VALU issue share %")
+    for c in sorted(scaled):
+        derived.append("%s MB (scaled)" % c)
     print("| kernel / shape | dispatches | mean us | " + " | ".join(names + derived) + " |")
     print("|---|---:|---:|" + "---:|" * (len(names) + len(derived)))
     hit = next((n for n in names if n.startswith("TCC_HIT")), None)
@@ -376,6 +390,8 @@ def cmd_counters(directory: str):
             # every SIMD over the dispatch at the peak clock (an understatement
             # where the clock runs lower)
             cells.append("%.1f" % (100.0 * mean("SQ_INSTS_VALU") * 4 / (SIMDS * mean("dur_ns") * CLOCK_GHZ)))
+        for c in sorted(scaled):
+            cells.append("%.3f" % (mean(c) * 1024 * scaled[c] / 1e6))
         print("| %s | %d | %.2f | %s |" % (k, n, mean("dur_ns") / 1e3, " | ".join(cells)))
 
 
@@ -394,6 +410,8 @@ def main(argv=None):
     m.add_argument("dir")
     k = sub.add_parser("counters")
     k.add_argument("dir")
+    k.add_argument("--copy-mib", type=int, default=0,
+                   help="the run's --copy-calibration size: scale FETCH_SIZE / WRITE_SIZE to bytes")
     r = sub.add_parser("ceiling")
     r.add_argument("dir")
     a = ap.parse_args(argv)
@@ -402,7 +420,7 @@ def main(argv=None):
     elif a.cmd == "mfma":
         cmd_mfma(a.dir)
     elif a.cmd == "counters":
-        cmd_counters(a.dir)
+        cmd_counters(a.dir, a.copy_mib)
     elif a.cmd == "ceiling":
         cmd_ceiling(a.dir)
     else:

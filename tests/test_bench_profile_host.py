@@ -228,3 +228,20 @@ def test_counters_derived_rates(tmp_path):
     assert rows["draft qkv"][-3] == "75.0" and rows["draft gate_up"][-3] == "25.0"       # L2 hit %
     assert rows["draft qkv"][-2] == "0.2000" and rows["draft gate_up"][-2] == "0.4286"   # c / (a - c)
     assert rows["draft qkv"][-1] == "10.0" and rows["draft gate_up"][-1] == "8.3"        # VALU issue share
+
+
+def test_counters_scale_fetch_by_the_copy(tmp_path):
+    # a 16 MiB copy that FETCH_SIZE counts as 8192 KiB: 2 bytes per KiB x 1024
+    name = NS + "verify_mfma_kernel<2, 1, false, false, 1>(bitnest::LinearArgs, int)"
+    copy = "void at::native::elementwise_copy_kernel<float>(...)"
+    entries = [(1, copy, 1000, 256, {"FETCH_SIZE": 8192.0}),
+               (2, name, 16000, 256, {"FETCH_SIZE": 30000.0}), (3, name, 16000, 256, {"FETCH_SIZE": 32000.0})]
+    _pmc_rows(str(tmp_path), entries)
+    out = io.StringIO()
+    with redirect_stdout(out):
+        bp.cmd_counters(str(tmp_path), copy_mib=16)
+    text = out.getvalue()
+    assert "bytes = 2.0000 x FETCH_SIZE KiB x 1024" in text
+    (row,) = _table(text)
+    assert row[0] == "verify_mfma_kernel<2, 1, false, false, 1>"
+    assert row[-1] == "%.3f" % (31000.0 * 1024 * 2 / 1e6)
