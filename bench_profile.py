@@ -40,6 +40,12 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       the median dispatch duration of the timed graph replays with its GB/s
       (the fastest configuration of each size marked).
 
+  python bench_profile.py kv FETCH_DIR WRITE_DIR [--copy-mib 256]
+      The two directories hold --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of
+      bench.py's nested-KV attention section (with --copy-calibration).
+      Prints, per context length and mode, the split kernel's scaled HBM
+      reads and writes per dispatch against the cache bytes it must read.
+
   python bench_profile.py mfma DIR
       DIR holds the output of
         rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_VALU_MFMA_BUSY_CYCLES
@@ -395,6 +401,37 @@ def cmd_counters(directory: str, copy_mib: int = 0):
         print("| %s | %d | %.2f | %s |" % (k, n, mean("dur_ns") / 1e3, " | ".join(cells)))
 
 
+
+def kv_blocks(rows, counter, contexts, layers, reps):
+    """[(T, mode, mean counter value per split dispatch)] from bench.py's KV
+    section: the split-kernel dispatches in start order, one block of
+    layers x (2 + reps) per (context, mode), draft KV4 then verify KV8; the
+    eager pass and the warm replay of each block are left out."""
+    split = sorted((r for r in per_dispatch(rows, counter) if "kv_attn_split_kernel" in r["Kernel_Name"]),
+                   key=lambda r: int(r["Dispatch_Id"]))
+    n = layers * (2 + reps)
+    if len(split) != n * 2 * len(contexts):
+        sys.exit("expected %d split dispatches, found %d" % (n * 2 * len(contexts), len(split)))
+    out = []
+    for i, (T, mode) in enumerate((T, m) for T in contexts for m in ("draft KV4", "verify KV8")):
+        timed = split[i * n + 2 * layers:(i + 1) * n]
+        out.append((T, mode, sum(float(r["Counter_Value"]) for r in timed) / len(timed)))
+    return out
+
+
+def cmd_kv(fetch_dir: str, write_dir: str, copy_mib: int, contexts, layers: int, reps: int, hkv: int):
+    print("| T | mode | cache bytes read (algorithmic) MB | FETCH (scaled) MB | ratio | WRITE (scaled) MB |")
+    print("|---:|---|---:|---:|---:|---:|")
+    res = {}
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read_csv(d, "counter_collection.csv")
+        f, _ = copy_factor(per_dispatch(rows, c), c, copy_mib * 1048576.0)
+        res[c] = [(T, m, v * 1024 * f) for T, m, v in kv_blocks(rows, c, contexts, layers, reps)]
+    for (T, mode, fb), (_, _, wb) in zip(res["FETCH_SIZE"], res["WRITE_SIZE"]):
+        planes = 2 if mode.startswith("verify") else 1
+        alg = 2 * T * hkv * (64 * planes + 2)
+        print("| %d | %s | %.3f | %.3f | %.3f | %.3f |" % (T, mode, alg / 1e6, fb / 1e6, fb / alg, wb / 1e6))
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -414,6 +451,14 @@ def main(argv=None):
                    help="the run's --copy-calibration size: scale FETCH_SIZE / WRITE_SIZE to bytes")
     r = sub.add_parser("ceiling")
     r.add_argument("dir")
+    v = sub.add_parser("kv")
+    v.add_argument("fetch_dir")
+    v.add_argument("write_dir")
+    v.add_argument("--copy-mib", type=int, default=256)
+    v.add_argument("--contexts", default="2048,8192,32768")
+    v.add_argument("--layers", type=int, default=32)
+    v.add_argument("--reps", type=int, default=5)
+    v.add_argument("--hkv", type=int, default=8)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         cmd_trace(a.dir, a.layers)
@@ -423,6 +468,9 @@ def main(argv=None):
         cmd_counters(a.dir, a.copy_mib)
     elif a.cmd == "ceiling":
         cmd_ceiling(a.dir)
+    elif a.cmd == "kv":
+        cmd_kv(a.fetch_dir, a.write_dir, a.copy_mib, [int(t) for t in a.contexts.split(",")], a.layers, a.reps,
+               a.hkv)
     else:
         cmd_traffic(a.fetch_dir, a.write_dir, a.json, a.copy_mib)
 

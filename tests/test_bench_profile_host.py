@@ -245,3 +245,25 @@ def test_counters_scale_fetch_by_the_copy(tmp_path):
     (row,) = _table(text)
     assert row[0] == "verify_mfma_kernel<2, 1, false, false, 1>"
     assert row[-1] == "%.3f" % (31000.0 * 1024 * 2 / 1e6)
+
+
+def test_kv_blocks_follow_the_section_order(tmp_path):
+    # two contexts x (draft, verify), 2 layers, 1 timed replay: blocks of
+    # 2 x (2 + 1) split dispatches; combine dispatches interleaved and ignored
+    contexts, layers, reps = [64, 128], 2, 1
+    entries, did = [], 1
+    want = []
+    for T in contexts:
+        for m, base in (("draft KV4", 10.0), ("verify KV8", 20.0)):
+            for p in range(2 + reps):
+                for l in range(layers):
+                    v = base * T + (100.0 if p < 2 else 0.0) + l      # eager and warm passes differ
+                    entries.append((did, NS + "kv_attn_split_kernel<false, 4>(bitnest::KvArgs, int)", 1000, 8,
+                                    {"FETCH_SIZE": v}))
+                    entries.append((did + 1, NS + "kv_attn_combine_kernel(bitnest::KvArgs, int)", 500, 8,
+                                    {"FETCH_SIZE": 1.0}))
+                    did += 2
+            want.append((T, m, base * T + 0.5))
+    _pmc_rows(str(tmp_path), entries)
+    got = bp.kv_blocks(bp.read_csv(str(tmp_path), "counter_collection.csv"), "FETCH_SIZE", contexts, layers, reps)
+    assert got == want
