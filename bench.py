@@ -492,6 +492,12 @@ def r4_timing(stack, bn, block=512, steps=10, reps=5):
     return out
 
 
+def pack_buffers(N, K):
+    """Distinct fp32 weight buffers the packer timing rotates through for an
+    [N, K] shape: more than 512 MiB of inputs, at least two."""
+    return max(2, -(-(512 << 20) // (4 * N * K)))
+
+
 def pack_timing(stack, bn, reps=5):
     """The offline nested packer on each Llama-3-8B linear shape: fp32
     weights (cold: buffers rotate through more memory than the caches hold)
@@ -502,7 +508,7 @@ def pack_timing(stack, bn, reps=5):
     out = {}
     g = torch.Generator(device="cuda").manual_seed(1234)
     for (name, N, K, _) in stack.linears:
-        nbuf = max(2, -(-(512 << 20) // (4 * N * K)))          # > 512 MiB of inputs in rotation
+        nbuf = pack_buffers(N, K)
         Ws = [torch.randn((N, K), generator=g, device="cuda") * 0.02 for _ in range(nbuf)]
         hi = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
         lo = torch.empty_like(hi)

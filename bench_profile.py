@@ -40,6 +40,11 @@ Runs on the host and reads rocprofv3 CSV output only (plain or gzipped):
       the median dispatch duration of the timed graph replays with its GB/s
       (the fastest configuration of each size marked).
 
+  python bench_profile.py pack FETCH_DIR WRITE_DIR [--copy-mib 256]
+      The same for bench.py's packer section: per Llama-3-8B shape, the
+      scaled reads and writes per dispatch against the fp32 weights read and
+      the planes and scales written.
+
   python bench_profile.py kv FETCH_DIR WRITE_DIR [--copy-mib 256]
       The two directories hold --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of
       bench.py's nested-KV attention section (with --copy-calibration).
@@ -432,6 +437,43 @@ def cmd_kv(fetch_dir: str, write_dir: str, copy_mib: int, contexts, layers: int,
         alg = 2 * T * hkv * (64 * planes + 2)
         print("| %d | %s | %.3f | %.3f | %.3f | %.3f |" % (T, mode, alg / 1e6, fb / 1e6, fb / alg, wb / 1e6))
 
+
+def pack_blocks(rows, counter, shapes, reps):
+    """[(name, mean counter value per dispatch)] from bench.py's packer
+    section: pack_nested_kernel dispatches in start order, per shape
+    pack_buffers(N, K) x (2 + reps) of them (eager pass, warm replay, timed
+    replays); the timed ones are averaged."""
+    sys.path.insert(0, ROOT)
+    import bench
+    pk = sorted((r for r in per_dispatch(rows, counter) if "pack_nested_kernel" in r["Kernel_Name"]),
+                key=lambda r: int(r["Dispatch_Id"]))
+    sizes = [bench.pack_buffers(N, K) for (_, N, K) in shapes]
+    if len(pk) != sum(n * (2 + reps) for n in sizes):
+        sys.exit("expected %d pack dispatches, found %d" % (sum(n * (2 + reps) for n in sizes), len(pk)))
+    out, i = [], 0
+    for (name, _, _), n in zip(shapes, sizes):
+        timed = pk[i + 2 * n:i + n * (2 + reps)]
+        out.append((name, sum(float(r["Counter_Value"]) for r in timed) / len(timed)))
+        i += n * (2 + reps)
+    return out
+
+
+def cmd_pack(fetch_dir: str, write_dir: str, copy_mib: int, reps: int):
+    from w8_quantized_linear_amd import synth
+    shapes = [(name, N, K) for (name, N, K, _) in synth.LLAMA3_8B_LINEARS]
+    res = {}
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read_csv(d, "counter_collection.csv")
+        f, _ = copy_factor(per_dispatch(rows, c), c, copy_mib * 1048576.0)
+        res[c] = {name: v * 1024 * f for name, v in pack_blocks(rows, c, shapes, reps)}
+    print("| shape | fp32 read MB | FETCH (scaled) MB | ratio | planes + scales written MB | WRITE (scaled) MB | ratio |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for name, N, K in shapes:
+        rd, wr = 4 * N * K, N * K + 2 * N * (K // 128)
+        fb, wb = res["FETCH_SIZE"][name], res["WRITE_SIZE"][name]
+        print("| %s | %.2f | %.2f | %.3f | %.2f | %.2f | %.3f |" % (name, rd / 1e6, fb / 1e6, fb / rd, wr / 1e6,
+                                                                  wb / 1e6, wb / wr))
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -451,6 +493,11 @@ def main(argv=None):
                    help="the run's --copy-calibration size: scale FETCH_SIZE / WRITE_SIZE to bytes")
     r = sub.add_parser("ceiling")
     r.add_argument("dir")
+    pk = sub.add_parser("pack")
+    pk.add_argument("fetch_dir")
+    pk.add_argument("write_dir")
+    pk.add_argument("--copy-mib", type=int, default=256)
+    pk.add_argument("--reps", type=int, default=5)
     v = sub.add_parser("kv")
     v.add_argument("fetch_dir")
     v.add_argument("write_dir")
@@ -468,6 +515,8 @@ def main(argv=None):
         cmd_counters(a.dir, a.copy_mib)
     elif a.cmd == "ceiling":
         cmd_ceiling(a.dir)
+    elif a.cmd == "pack":
+        cmd_pack(a.fetch_dir, a.write_dir, a.copy_mib, a.reps)
     elif a.cmd == "kv":
         cmd_kv(a.fetch_dir, a.write_dir, a.copy_mib, [int(t) for t in a.contexts.split(",")], a.layers, a.reps,
                a.hkv)

@@ -267,3 +267,23 @@ def test_kv_blocks_follow_the_section_order(tmp_path):
     _pmc_rows(str(tmp_path), entries)
     got = bp.kv_blocks(bp.read_csv(str(tmp_path), "counter_collection.csv"), "FETCH_SIZE", contexts, layers, reps)
     assert got == want
+
+
+def test_pack_blocks_follow_the_section_order(tmp_path):
+    # two shapes with 3 and 2 rotating buffers, 1 timed replay: blocks of
+    # nbuf x (2 + 1) dispatches, the timed replay averaged
+    import bench
+    shapes = [("a", 8192, 16384), ("b", 16384, 16384)]
+    nb = [bench.pack_buffers(N, K) for _, N, K in shapes]
+    assert nb == [2, 2]
+    entries, did, want = [], 1, []
+    for (name, N, K), n in zip(shapes, nb):
+        for p in range(3):
+            for j in range(n):
+                entries.append((did, NS + "pack_nested_kernel(float const*, long long, ...)", 1000, 8,
+                                {"FETCH_SIZE": float(N + (7 if p < 2 else j))}))
+                did += 1
+        want.append((name, N + (n - 1) / 2))
+    _pmc_rows(str(tmp_path), entries)
+    got = bp.pack_blocks(bp.read_csv(str(tmp_path), "counter_collection.csv"), "FETCH_SIZE", shapes, 1)
+    assert got == want
