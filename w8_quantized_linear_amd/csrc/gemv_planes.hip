@@ -456,7 +456,8 @@ typedef void (*GemvKernel)(const LinearArgs);
 
 // Launch shape: waves per workgroup and items (1 KiB chunks per plane) in
 // flight per wave. (Measured on MI355X over the Llama-3-8B shapes: 2-4 items
-// per wave with 8-wave workgroups beat deeper rings, which cost occupancy.)
+// per wave with 8-wave workgroups beat deeper rings, whose code has no spills
+// and the same waits: the bigger first burst of requests is itself slower.)
 constexpr int kGemvWaves = 8;
 // The fused single-token kernel quantises the whole row in every workgroup,
 // so it runs one workgroup per compute unit. (Measured on MI355X: 8 waves
