@@ -362,6 +362,42 @@ def test_runs_on_a_side_stream():
     _check_y(y, oracle.linear(q, sa, hi, sc, lo), "side stream")
 
 
+
+def test_calls_on_two_streams_run_concurrently():
+    # Calls keep no state between them (outside the no-allocation scratch
+    # and caller workspaces), so work enqueued on two streams with no order
+    # between them gives what the same calls give one after another: the
+    # fused one-token path, the two-launch four-token path and the matrix
+    # cores, alternately enqueued on both streams
+    cases = [(1, 1536, 4096, 0, False), (4, 9216, 4096, 0, True), (1, 1024, 14336, 0, True),
+             (8, 512, 4096, 128, True), (4, 1024, 4096, 128, False), (1, 2048, 4096, 128, True)]
+    probs = []
+    for i, (M, N, K, g, target) in enumerate(cases):
+        w = synth.make_weights(N, K, seed=40 + i, device="cuda")
+        x = synth.make_activations(M, K, seed=40 + i, device="cuda")
+        probs.append((x, w, g, target))
+
+    def call(x, w, g, target):
+        if target:
+            return bn.bitnest_quant_linear_target(x, w.hi, w.lo, w.scale, g)
+        return bn.bitnest_quant_linear_draft(x, w.hi, w.scale, g)
+
+    serial = [call(*p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    out = []
+    for rep in range(3):
+        for i, p in enumerate(probs):
+            with torch.cuda.stream(streams[(i + rep) % 2]):
+                out.append((i, call(*p)))
+    torch.cuda.synchronize()
+    for i, (y, q, s) in out:
+        y0, q0, s0 = serial[i]
+        assert torch.equal(q, q0) and torch.equal(s.view(torch.int32), s0.view(torch.int32)), i
+        assert torch.equal(y.view(torch.int32), y0.view(torch.int32)), i
+
 # --------------------------------------------------------------------------- full-size layers
 
 @pytest.fixture(scope="module")
