@@ -10,7 +10,6 @@
 #include <map>
 #include <mutex>
 #include <tuple>
-#include <vector>
 
 namespace bitnest {
 
@@ -26,7 +25,10 @@ std::map<std::pair<const void *, int>, bool> g_lds_raised;
 std::map<std::tuple<const void *, int, int, size_t>, int> g_occupancy;
 }  // namespace
 
-hipError_t set_max_dynamic_lds(const void *kernel, size_t bytes) {
+// The two lookups below are the library's only code that can throw (a map
+// insertion, a mutex); they answer with an error code instead, so nothing
+// throws across the C boundary.
+hipError_t set_max_dynamic_lds(const void *kernel, size_t bytes) try {
     if (bytes <= 65536) return hipSuccess;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -43,9 +45,11 @@ hipError_t set_max_dynamic_lds(const void *kernel, size_t bytes) {
     if (e != hipSuccess) return e;
     g_lds_raised[key] = true;
     return hipSuccess;
+} catch (...) {
+    return hipErrorUnknown;
 }
 
-hipError_t occupancy(const void *kernel, int threads, size_t lds, int *out) {
+hipError_t occupancy(const void *kernel, int threads, size_t lds, int *out) try {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -65,6 +69,8 @@ hipError_t occupancy(const void *kernel, int threads, size_t lds, int *out) {
     g_occupancy[key] = occ;
     *out = occ;
     return hipSuccess;
+} catch (...) {
+    return hipErrorUnknown;
 }
 
 hipError_t device_info(DeviceInfo *out) {
