@@ -211,3 +211,19 @@ def test_chain_with_one_poll_per_wait_still_ends():
     torch.cuda.synchronize()
     _check_same(links, ref)
     assert _counter_words(ok) == (0, 0)
+
+
+def test_chain_built_on_one_stream_runs_on_another():
+    # the constructor's table copy and workspace fill are complete before it
+    # returns, so a first run() on an unrelated stream, with no ordering
+    # between the two streams, sees them
+    links = _links(LAYER, 1, True, seed=17)
+    ref = _single_calls(links, True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    chain = bn.LinearChain(links)
+    with torch.cuda.stream(s):
+        chain.run()
+    s.synchronize()
+    _check_same(links, ref)
+    assert _counter_words(chain) == (0, 0)

@@ -502,9 +502,11 @@ class LinearChain:
     lo (target chains; None or absent for draft chains), scale [N, K/128],
     y fp32 [M, N], optional xq int8 [M, K] and xs fp32 [M] or [M, K/128]
     (both or neither), act_group 0 or 128. The link table is built and copied
-    to the device once here (so run() can be captured in a HIP graph); the
-    tensors must stay alive and in place, which this object ensures by holding
-    them. A link's x may be an earlier link's y."""
+    to the device once here (so run() can be captured in a HIP graph), and the
+    constructor waits until that copy and the workspace's zero fill are done,
+    so run() may be called on any stream of the device; the tensors must stay
+    alive and in place, which this object ensures by holding them. A link's x
+    may be an earlier link's y."""
 
     def __init__(self, links, max_polls: int = 0, work: torch.Tensor | None = None):
         if not links:
@@ -559,6 +561,10 @@ class LinearChain:
             raise ValueError("work must hold %d bytes" % nbytes)
         self.work = work
         self.max_polls = int(max_polls)
+        # the link table's copy and the workspace's zero fill were enqueued on
+        # the current stream; run() may be called on another one (a capture
+        # stream, a worker stream), so they must be complete before it
+        torch.cuda.current_stream(self.device).synchronize()
 
     def run(self):
         """Enqueue the chain on torch's current stream (one launch)."""
